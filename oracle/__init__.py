@@ -1,0 +1,129 @@
+"""Python access to the CPU oracle (plain C, see ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg. The library never imports it.
+
+Arrays are numpy: bfloat16 operands are ``uint16`` bit patterns, binary32 is
+``float32``. ``threads > 1`` splits the rows of A over threads; each call of
+the C routine covers whole rows, and rows are independent, so the result is
+the same bytes as one single-threaded call.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load (building if needed) the oracle library; a path loads a specific build."""
+    global _lib
+    if path is not None:
+        return _bind(ct.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_build.LIB) or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
+            _build.build()
+        _lib = _bind(ct.CDLL(_build.LIB))
+    return _lib
+
+
+def _bind(lib):
+    P, I64, I = ct.c_void_p, ct.c_int64, ct.c_int
+    lib.oracle_source_sha256.restype = ct.c_char_p
+    lib.oracle_gemm_ordered.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
+    lib.oracle_gemm_f64.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
+    lib.oracle_gemm_absdot_f64.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
+    lib.oracle_freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
+    lib.oracle_freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
+    lib.oracle_freivalds_check.restype = I
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _a_dtype(A: np.ndarray) -> int:
+    if A.dtype == np.uint16:
+        return 0
+    if A.dtype == np.float32:
+        return 1
+    raise TypeError(f"A must be bf16 bits (uint16) or float32, got {A.dtype}")
+
+
+def _rows(fn, A, W, out, threads):
+    M, K = A.shape
+    N = W.shape[1]
+    ad = _a_dtype(A)
+
+    def run(r0, r1):
+        if r1 > r0:
+            fn(_ptr(A[r0:]), ad, max(A.strides[0] // A.itemsize, K), _ptr(W), max(W.strides[0] // W.itemsize, N),
+               _ptr(out[r0:]), out.strides[0] // out.itemsize, r1 - r0, N, K)
+
+    if threads <= 1 or M < 2:
+        run(0, M)
+    else:
+        step = (M + threads - 1) // threads
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda r0: run(r0, min(M, r0 + step)), range(0, M, step)))
+    return out
+
+
+def _check(A, W):
+    assert A.ndim == 2 and W.ndim == 2 and A.shape[1] == W.shape[0], (A.shape, W.shape)
+    assert W.dtype == np.uint16, W.dtype
+    # rows may be strided; the inner (k or n) axis must be unit stride
+    if A.shape[1] > 1 and A.strides[1] != A.itemsize or A.strides[0] < 0:
+        A = np.ascontiguousarray(A)
+    if W.shape[1] > 1 and W.strides[1] != W.itemsize or W.strides[0] < 0 or W.shape[1] == 1:
+        W = np.ascontiguousarray(W)
+    return A, W
+
+
+def gemm_ordered(A: np.ndarray, W: np.ndarray, threads: int = 1, lib=None) -> np.ndarray:
+    """The order-contract product: float32 [M, N]."""
+    A, W = _check(A, W)
+    out = np.empty((A.shape[0], W.shape[1]), dtype=np.float32)
+    return _rows((lib or load()).oracle_gemm_ordered, A, W, out, threads)
+
+
+def gemm_f64(A: np.ndarray, W: np.ndarray, threads: int = 1) -> np.ndarray:
+    A, W = _check(A, W)
+    out = np.empty((A.shape[0], W.shape[1]), dtype=np.float64)
+    return _rows(load().oracle_gemm_f64, A, W, out, threads)
+
+
+def gemm_absdot_f64(A: np.ndarray, W: np.ndarray, threads: int = 1) -> np.ndarray:
+    A, W = _check(A, W)
+    out = np.empty((A.shape[0], W.shape[1]), dtype=np.float64)
+    return _rows(load().oracle_gemm_absdot_f64, A, W, out, threads)
+
+
+def freivalds_prepare(W: np.ndarray, r: np.ndarray):
+    """(s, q, a) K-vectors in float64 for matrix W [K, N] and signs r (int8, length N)."""
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    r = np.ascontiguousarray(r, dtype=np.int8)
+    K, N = W.shape
+    assert r.shape == (N,)
+    s, q, a = (np.empty(K, dtype=np.float64) for _ in range(3))
+    load().oracle_freivalds_prepare(_ptr(W), N, K, N, _ptr(r), _ptr(s), _ptr(q), _ptr(a))
+    return s, q, a
+
+
+def freivalds_check(prep, r: np.ndarray, x: np.ndarray, y: np.ndarray, c_f: float = 0.125):
+    """Returns (accept: bool, rho, sigma, tau, bound) for one row x (bf16, K) and y (f32, N)."""
+    s, q, a = prep
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    r = np.ascontiguousarray(r, dtype=np.int8)
+    out = np.empty(4, dtype=np.float64)
+    ok = load().oracle_freivalds_check(_ptr(s), _ptr(q), _ptr(a), _ptr(r), s.shape[0], y.shape[0],
+                                       _ptr(x), _ptr(y), float(c_f), _ptr(out))
+    return bool(ok), float(out[0]), float(out[1]), float(out[2]), float(out[3])
