@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant matmul library on one MI355X.
+
+Headline workload (one "step"): the decode GEMV of x[M, 4096] (bf16) by
+W[4096, 4096] (bf16), binary32 fold, for M = 1, 4 and 8, through gemv_ordered.
+Sixteen copies of W (512 MiB, twice the 256 MB Infinity Cache) are rotated so
+every launch streams its W from HBM. The value is GB/s of algorithmic traffic
+(2KN + 2MK + 4MN bytes per launch) over the timed steps. The timed steps are
+captured once in a HIP graph and replayed, so host launch overhead is not
+timed; HIP events on the launch stream bracket the replay.
+
+Beside it, in the same JSON line:
+  roofline      the GEMV kernel against 8 TB/s HBM
+  cpu_baseline  the CPU oracle on the same step, one core, for ~10 s
+  certificate   Freivalds checks of sampled rows (honest pass, planted fault caught)
+  paths         the other paths at their workloads: ordered GEMM and MFMA GEMM
+                TFLOP/s (MLP up-projection, 7B projections), the value product,
+                and torch.matmul (hipBLASLt, not batch invariant) on the same shapes
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2516.0          # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+VALU_CONTRACT_PEAK_TFS = 39.3        # unpacked v_mul_f32 + v_add_f32 per MAC (2 flop in 2 issues)
+VALU_NOMINAL_PEAK_TFS = 157.3        # packed FMA
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_region(fn, reps: int, warmup: int = 2) -> float:
+    """Mean ms per call of fn(), HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def gemv_bytes(M, K=4096, N=4096):
+    return 2 * K * N + 2 * M * K + 4 * M * N
+
+
+def cpu_baseline(x, W, ms, seconds):
+    import oracle
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for M in ms:
+            oracle.gemm_ordered(x[:M], W, threads=1)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    gbs = steps * sum(gemv_bytes(M) for M in ms) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full decode steps (M={','.join(map(str, ms))}, K=N=4096), plain C oracle "
+                      f"single-threaded, {dt:.1f} s"}
+
+
+def certificate(g, x, W, r, ys, ms):
+    import numpy as np
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    prep = g.freivalds_prepare(W, r)
+    t_prep = time.perf_counter() - t0
+    y8 = ys[ms[-1]]
+    t1 = time.perf_counter()
+    yh = y8.cpu().numpy()
+    t_d2h = (time.perf_counter() - t1) / y8.shape[0]
+    checks, worst, t_check = 0, 0.0, 0.0
+    for m in range(yh.shape[0]):
+        t2 = time.perf_counter()
+        ok, rho, sigma, tau, bound = g.freivalds_check(prep, r, x[m], yh[m])
+        t_check += time.perf_counter() - t2
+        checks += ok
+        worst = max(worst, rho / sigma)
+    j = 1234
+    yb = yh[0].copy()
+    yb[j] += np.float32(0.005)
+    caught = not g.freivalds_check(prep, r, x[0], yb)[0]
+    return {"honest_pass": f"{checks}/{yh.shape[0]}", "max_honest_ratio": round(worst, 5), "c_f": 0.125,
+            "planted_0.005_caught": caught, "us_per_check": round(1e6 * t_check / yh.shape[0], 2),
+            "d2h_us_per_row_pair": round(1e6 * t_d2h, 2), "prepare_ms": round(1e3 * t_prep, 2)}
+
+
+def paths(g, reps):
+    """Throughput of the other paths at their workloads (seeded torch data, timing only)."""
+    import torch
+    torch.manual_seed(0)
+    out = {}
+
+    def randn_bf16(shape, std):
+        return (torch.randn(shape, device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
+
+    def mm_blaslt(A, W):
+        try:
+            return torch.mm(A, W, out_dtype=torch.float32)
+        except TypeError:
+            return torch.mm(A, W)
+
+    # MLP up-projection and 7B projections: ordered VALU, MFMA invariant, hipBLASLt
+    shapes = [("mlp_up", 256, 4096, 1024), ("mlp_up", 2048, 4096, 1024),
+              ("7b_qkvo", 4096, 4096, 4096), ("7b_up", 4096, 11008, 4096)]
+    for name, M, N, K in shapes:
+        A = randn_bf16((M, K), 1.0)
+        W = randn_bf16((K, N), 0.02)
+        C = torch.empty((M, N), device="cuda")
+        flop = 2.0 * M * N * K
+        rec = {}
+        if name == "mlp_up":
+            t = time_region(lambda: g.gemm_ordered(A, W, C=C), max(2, reps // 4), 1)
+            rec["ordered_tflops"] = round(flop / t / 1e9, 2)
+            rec["ordered_frac_contract_peak"] = round(flop / t / 1e9 / VALU_CONTRACT_PEAK_TFS, 4)
+        t = time_region(lambda: g.gemm_mfma_invariant(A, W, C=C), reps)
+        rec["mfma_tflops"] = round(flop / t / 1e9, 1)
+        rec["mfma_frac_peak"] = round(flop / t / 1e9 / MFMA_BF16_PEAK_TFS, 4)
+        tb = time_region(lambda: mm_blaslt(A, W), reps)
+        rec["hipblaslt_tflops"] = round(flop / tb / 1e9, 1)
+        rec["mfma_vs_hipblaslt"] = round(tb / t, 3)
+        out[f"{name}_M{M}_N{N}_K{K}"] = rec
+        del A, W, C
+    # attention value product, 32 heads, head_dim 128
+    for L in (256, 1024):
+        P = torch.softmax(torch.randn((32, L, L), device="cuda"), dim=-1)
+        V = randn_bf16((32, L, 128), 1.0)
+        O = torch.empty((32, L, 128), device="cuda")
+        t = time_region(lambda: g.gemm_ordered_grouped([(P, V, O)]), max(2, reps // 4), 1)
+        flop = 2.0 * 32 * L * L * 128
+        out[f"pv_L{L}_h32"] = {"ordered_tflops": round(flop / t / 1e9, 2), "ms": round(t, 4)}
+        del P, V, O
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-paths", action="store_true", help="skip the other paths' throughput")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches instead of one graph replay")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this library's path has no cross-GPU step, and this "
+              "benchmark reports one GPU's throughput (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemv_gemm_ordered_amd as g
+    import oracle
+    import synth
+
+    K = N = 4096
+    ms = (1, 4, 8)
+    log("generating decode workload")
+    x, W, r = synth.decode_gemv(0, 8)
+    dx = dev_bf16(x)
+    copies = 16
+    dW0 = dev_bf16(W)
+    dWs = [dW0] + [dW0.clone() for _ in range(copies - 1)]
+    ys = {M: torch.empty((M, N), device="cuda") for M in ms}
+    step_bytes = sum(gemv_bytes(M) for M in ms)
+    counter = [0]
+
+    def step():
+        for M in ms:
+            g.gemv_ordered(dx[:M], dWs[counter[0] % copies], y=ys[M])
+            counter[0] += 1
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if args.no_graph:
+        run = None
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        run = graph.replay
+        run()                       # one untimed replay: uploads the graph
+        torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    if run is not None:
+        run()
+    else:
+        for _ in range(args.steps):
+            step()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = s.elapsed_time(e)
+    ms_per_step = ms_total / args.steps
+    value = step_bytes * args.steps / (ms_total / 1e3) / 1e9
+    avg_launch_us = 1e3 * ms_total / (args.steps * len(ms))
+
+    # parity spot check of the timed kernel's last outputs against the oracle
+    ref = oracle.gemm_ordered(x[:8][[0, 7]], W, threads=2).view(np.uint32)
+    got = ys[8].cpu().numpy().view(np.uint32)[[0, 7]]
+    parity = "bit-exact (rows 0 and 7 of M=8 vs CPU oracle)" if np.array_equal(got, ref) else "MISMATCH"
+
+    # per-M kernel time (events around 16 launches each, rotating W)
+    per_m = {}
+    for M in ms:
+        i = [0]
+
+        def one():
+            g.gemv_ordered(dx[:M], dWs[i[0] % copies], y=ys[M])
+            i[0] += 1
+        t = time_region(one, 32)
+        per_m[str(M)] = {"us": round(1e3 * t, 2), "GBps": round(gemv_bytes(M) / t / 1e6, 1),
+                         "frac_hbm": round(gemv_bytes(M) / t / 1e6 / HBM_PEAK_GBS, 4)}
+
+    cert = certificate(g, x, W, r, ys, ms)
+    extra = {} if args.no_paths else paths(g, 10)
+    log("cpu baseline")
+    cpu = cpu_baseline(x, W, ms, args.cpu_seconds)
+
+    achieved = (step_bytes / len(ms)) / (avg_launch_us * 1e-6) / 1e9
+    line = {
+        "metric": "batch-invariant GEMM TFLOP/s & GEMV GB/s vs M, bit-exact; % of roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded splitmix64/Box-Muller; x ~ N(0,1), W ~ N(0,0.02), bf16)",
+        "config": {"workload": "decode GEMV, gemv_ordered: x[M,4096] bf16 x W[4096,4096] bf16 -> y f32, "
+                               "M in {1,4,8} per step, 16 rotated W copies",
+                   "K": K, "N": N, "M_per_step": list(ms), "w_copies": copies,
+                   "graph": run is not None, "parity": parity},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_gemv_ordered", "avg_launch_us": round(avg_launch_us, 3),
+                     "bytes_per_launch": step_bytes / len(ms)},
+        "cpu_baseline": cpu,
+        "per_M": per_m,
+        "certificate": cert,
+        "paths": extra,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

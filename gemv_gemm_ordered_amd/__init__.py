@@ -1,0 +1,218 @@
+"""Batch-invariant matrix multiply for MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over the C-ABI in ``include/ggo.h``: every function
+takes torch tensors (device memory and streams come from torch), checks
+shapes and dtypes, and passes raw pointers, strides and the current HIP
+stream to ``libggo.so``. All arithmetic runs in the library's HIP kernels
+(the Freivalds certificate runs in the library's host code). If the library
+is missing the import fails; there is no fallback.
+
+bfloat16 operands are ``torch.bfloat16`` tensors (or int16/uint16 tensors
+holding the bit patterns); results are ``torch.float32``.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libggo.so")
+
+GGO_BF16, GGO_F32 = 0, 1
+GEMV_MAX_M = 16
+MAX_PROBLEMS = 16
+
+
+class GGOError(RuntimeError):
+    pass
+
+
+class Problem(ct.Structure):
+    """Mirror of ``ggo_problem``."""
+    _fields_ = [("A", ct.c_void_p), ("W", ct.c_void_p), ("C", ct.c_void_p),
+                ("lda", ct.c_int64), ("ldw", ct.c_int64), ("ldc", ct.c_int64),
+                ("batch", ct.c_int64),
+                ("stride_a", ct.c_int64), ("stride_w", ct.c_int64), ("stride_c", ct.c_int64),
+                ("M", ct.c_int64), ("N", ct.c_int64), ("K", ct.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc for gfx950) first")
+    lib = ct.CDLL(LIB_PATH)
+    P, I64, I = ct.c_void_p, ct.c_int64, ct.c_int
+    lib.gemm_ordered.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemm_ordered_grouped.argtypes = [ct.POINTER(Problem), I64, I, P]
+    lib.gemv_ordered.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemm_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
+    lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
+    lib.ggo_build_info.restype = ct.c_char_p
+    lib.ggo_last_error.restype = ct.c_char_p
+    for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
+              "freivalds_prepare", "freivalds_check"):
+        getattr(lib, f).restype = I
+    return lib
+
+
+lib = _load()
+
+EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
+           "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error")
+
+
+def build_info() -> str:
+    return lib.ggo_build_info().decode()
+
+
+def _raise(rc: int, fn: str):
+    if rc < 0:
+        raise GGOError(f"{fn} failed ({rc}): {lib.ggo_last_error().decode()}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _is_bf16(t) -> bool:
+    torch = _torch()
+    return t.dtype in (torch.bfloat16, torch.int16) or str(t.dtype) == "torch.uint16"
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last axis")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return max(t.stride(0), t.shape[1])
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ct.c_void_p(s.cuda_stream)
+
+
+def _out(C, M, N, like):
+    torch = _torch()
+    if C is None:
+        return torch.empty((M, N), dtype=torch.float32, device=like.device)
+    if C.dtype != torch.float32 or tuple(C.shape) != (M, N):
+        raise ValueError(f"C must be float32 [{M}, {N}]")
+    return C
+
+
+def gemm_ordered(A, W, C=None, stream=None):
+    """C = A W under the order contract (A bf16 or float32, W bf16, C float32)."""
+    torch = _torch()
+    lda, ldw = _rowmajor(A, "A"), _rowmajor(W, "W")
+    M, K = A.shape
+    if W.shape[0] != K or not _is_bf16(W):
+        raise ValueError("W must be bf16 [K, N]")
+    N = W.shape[1]
+    if _is_bf16(A):
+        ad = GGO_BF16
+    elif A.dtype == torch.float32:
+        ad = GGO_F32
+    else:
+        raise ValueError(f"A must be bf16 or float32, got {A.dtype}")
+    C = _out(C, M, N, A)
+    ldc = _rowmajor(C, "C") if M and N else N
+    _raise(lib.gemm_ordered(A.data_ptr(), ad, lda, W.data_ptr(), ldw, C.data_ptr(), ldc, M, N, K, _stream(stream)),
+           "gemm_ordered")
+    return C
+
+
+def gemm_ordered_grouped(problems, stream=None):
+    """problems: list of (A, W, C) with A [b, M, K] (bf16 or float32, all the same), W [b, K, N] bf16,
+    C [b, M, N] float32 (3-D, or 2-D for b = 1). One launch; each output has gemm_ordered's bits."""
+    torch = _torch()
+    if not 1 <= len(problems) <= MAX_PROBLEMS:
+        raise ValueError(f"1..{MAX_PROBLEMS} problems per launch")
+    arr = (Problem * len(problems))()
+    ad = None
+    keep = []
+    for i, (A, W, C) in enumerate(problems):
+        A3, W3, C3 = (t if t.dim() == 3 else t.unsqueeze(0) for t in (A, W, C))
+        b, M, K = A3.shape
+        if W3.shape[0] != b or W3.shape[1] != K or C3.shape[0] != b or C3.shape[1] != M or C3.shape[2] != W3.shape[2]:
+            raise ValueError("shape mismatch in grouped problem %d" % i)
+        this = GGO_BF16 if _is_bf16(A3) else GGO_F32 if A3.dtype == torch.float32 else None
+        if this is None or (ad is not None and this != ad) or not _is_bf16(W3) or C3.dtype != torch.float32:
+            raise ValueError("dtype mismatch in grouped problem %d" % i)
+        ad = this
+        for t, nm in ((A3, "A"), (W3, "W"), (C3, "C")):
+            if not t.is_cuda or (t.shape[2] > 1 and t.stride(2) != 1):
+                raise ValueError(f"{nm} of problem {i} must be a device tensor with unit inner stride")
+        arr[i] = Problem(A3.data_ptr(), W3.data_ptr(), C3.data_ptr(),
+                         max(A3.stride(1), K), max(W3.stride(1), W3.shape[2]), max(C3.stride(1), C3.shape[2]),
+                         b, A3.stride(0), W3.stride(0), C3.stride(0), M, W3.shape[2], K)
+        keep.append((A3, W3, C3))
+    _raise(lib.gemm_ordered_grouped(arr, len(problems), ad, _stream(stream)), "gemm_ordered_grouped")
+
+
+def gemv_ordered(x, W, y=None, stream=None):
+    """y = x W for x bf16 [M <= 16, K], W bf16 [K, N]: the same bits as gemm_ordered."""
+    ldx, ldw = _rowmajor(x, "x"), _rowmajor(W, "W")
+    M, K = x.shape
+    if not (_is_bf16(x) and _is_bf16(W)) or W.shape[0] != K:
+        raise ValueError("x and W must be bf16, W [K, N]")
+    N = W.shape[1]
+    y = _out(y, M, N, x)
+    ldy = _rowmajor(y, "y") if M and N else N
+    _raise(lib.gemv_ordered(x.data_ptr(), ldx, W.data_ptr(), ldw, y.data_ptr(), ldy, M, N, K, _stream(stream)),
+           "gemv_ordered")
+    return y
+
+
+def gemm_mfma_invariant(A, W, C=None, stream=None):
+    """C = A W on the matrix cores, bits independent of M (A, W bf16; C float32)."""
+    lda, ldw = _rowmajor(A, "A"), _rowmajor(W, "W")
+    M, K = A.shape
+    if not (_is_bf16(A) and _is_bf16(W)) or W.shape[0] != K:
+        raise ValueError("A and W must be bf16, W [K, N]")
+    N = W.shape[1]
+    C = _out(C, M, N, A)
+    ldc = _rowmajor(C, "C") if M and N else N
+    _raise(lib.gemm_mfma_invariant(A.data_ptr(), lda, W.data_ptr(), ldw, C.data_ptr(), ldc, M, N, K, _stream(stream)),
+           "gemm_mfma_invariant")
+    return C
+
+
+def _np(a, dtype):
+    if hasattr(a, "detach"):
+        a = a.detach().cpu()
+        if str(a.dtype) == "torch.bfloat16":
+            a = a.view(_torch().int16)
+        a = a.numpy()
+    return np.ascontiguousarray(a).view(dtype) if np.asarray(a).dtype.itemsize == np.dtype(dtype).itemsize \
+        else np.ascontiguousarray(a, dtype=dtype)
+
+
+def freivalds_prepare(W, r):
+    """Host precompute (s, q, a) for W [K, N] (bf16 bits, host) and signs r (N, +-1)."""
+    W = _np(W, np.uint16)
+    r = np.ascontiguousarray(r, dtype=np.int8)
+    K, N = W.shape
+    s, q, a = (np.empty(K, dtype=np.float64) for _ in range(3))
+    _raise(lib.freivalds_prepare(W.ctypes.data, N, K, N, r.ctypes.data, s.ctypes.data, q.ctypes.data, a.ctypes.data),
+           "freivalds_prepare")
+    return s, q, a
+
+
+def freivalds_check(prep, r, x, y, c_f: float = 0.125):
+    """(accept, rho, sigma, tau, bound) for one host row x (bf16 bits, K) and y (float32, N)."""
+    s, q, a = prep
+    x = _np(x, np.uint16).reshape(-1)
+    y = _np(y, np.float32).reshape(-1)
+    r = np.ascontiguousarray(r, dtype=np.int8)
+    out = np.empty(4, dtype=np.float64)
+    rc = lib.freivalds_check(s.ctypes.data, q.ctypes.data, a.ctypes.data, r.ctypes.data, s.shape[0], y.shape[0],
+                             x.ctypes.data, y.ctypes.data, float(c_f), out.ctypes.data)
+    _raise(rc, "freivalds_check")
+    return bool(rc), float(out[0]), float(out[1]), float(out[2]), float(out[3])

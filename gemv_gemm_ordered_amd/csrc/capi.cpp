@@ -1,0 +1,228 @@
+// C-ABI shim: argument checks, launch geometry, error reporting.
+// Nothing here depends on M except grid extents; no entry point picks a kernel,
+// tile or split from the problem size.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+
+#ifndef GGO_BUILD_INFO
+#define GGO_BUILD_INFO "unknown build"
+#endif
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return GGO_OK;
+}
+
+constexpr int64_t I32MAX = 0x7fffffff;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return fail(GGO_EINVAL, "%s: negative size (M=%lld N=%lld K=%lld)", fn, (long long)M, (long long)N, (long long)K);
+    if (M > I32MAX || N > I32MAX || K > I32MAX) return fail(GGO_EUNSUPPORTED, "%s: a size exceeds 2^31-1", fn);
+    return GGO_OK;
+}
+
+int launched(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(GGO_ELAUNCH, "%s: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+// Fill an [M, N] binary32 matrix with +0.0 (the value of an empty fold).
+__global__ void k_fill_zero(float* C, int64_t ldc, int M, int N) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(M) * N;
+    if (i < total) {
+        const int64_t m = i / N, n = i - m * N;
+        C[m * ldc + n] = 0.0f;
+    }
+}
+
+hipError_t fill_zero(float* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s) {
+    const int64_t total = M * N;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, C, ldc, (int)M, (int)N);
+    return hipGetLastError();
+}
+
+int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, OrdProblem& p, int64_t& tiles) {
+    int rc = check_mnk(fn, q.M, q.N, q.K);
+    if (rc) return rc;
+    if (q.batch < 0) return fail(GGO_EINVAL, "%s: negative batch", fn);
+    if (q.M && q.N && q.batch) {
+        if (!q.C || (q.K && (!q.A || !q.W))) return fail(GGO_EINVAL, "%s: null pointer", fn);
+        if (q.lda < q.K || q.ldw < q.N || q.ldc < q.N)
+            return fail(GGO_EINVAL, "%s: row stride below extent (lda=%lld K=%lld ldw=%lld ldc=%lld N=%lld)", fn,
+                        (long long)q.lda, (long long)q.K, (long long)q.ldw, (long long)q.ldc, (long long)q.N);
+        if (q.batch > 1 && (q.stride_a < 0 || q.stride_w < 0 || q.stride_c < 0))
+            return fail(GGO_EINVAL, "%s: negative batch stride", fn);
+    }
+    int bm, bn;
+    ordered_tile_shape(&bm, &bn);
+    p.A = q.A;
+    p.W = q.W;
+    p.C = q.C;
+    p.lda = q.lda;
+    p.ldw = q.ldw;
+    p.ldc = q.ldc;
+    p.sa = q.stride_a;
+    p.sw = q.stride_w;
+    p.sc = q.stride_c;
+    p.M = (int32_t)q.M;
+    p.N = (int32_t)q.N;
+    p.K = (int32_t)q.K;
+    p.batch = (int32_t)q.batch;
+    p.tiles_m = (int32_t)((q.M + bm - 1) / bm);
+    p.tiles_n = (int32_t)((q.N + bn - 1) / bn);
+    const size_t esz = a_dtype == GGO_F32 ? 4 : 2;
+    const int64_t avec = a_dtype == GGO_F32 ? 4 : 8;
+    p.vec = 0;
+    if (aligned(q.A, 16) && q.lda % avec == 0 && (q.batch <= 1 || (q.stride_a * (int64_t)esz) % 16 == 0)) p.vec |= VEC_A;
+    if (aligned(q.W, 16) && q.ldw % 8 == 0 && (q.batch <= 1 || q.stride_w % 8 == 0)) p.vec |= VEC_W;
+    if (aligned(q.C, 16) && q.ldc % 4 == 0 && (q.batch <= 1 || q.stride_c % 4 == 0)) p.vec |= VEC_C;
+    tiles = (q.M && q.N) ? q.batch * (int64_t)p.tiles_m * p.tiles_n : 0;
+    if (q.batch > I32MAX) return fail(GGO_EUNSUPPORTED, "%s: batch exceeds 2^31-1", fn);
+    return GGO_OK;
+}
+
+int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype, hipStream_t s) {
+    if (a_dtype != GGO_BF16 && a_dtype != GGO_F32) return fail(GGO_EINVAL, "%s: a_dtype must be GGO_BF16 or GGO_F32", fn);
+    if (!qs) return fail(GGO_EINVAL, "%s: null problem array", fn);
+    if (count < 1 || count > GGO_MAX_PROBLEMS) return fail(GGO_EINVAL, "%s: count must be 1..%d", fn, GGO_MAX_PROBLEMS);
+    OrdGroup g;
+    std::memset(&g, 0, sizeof g);
+    int64_t total = 0;
+    int n = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t tiles = 0;
+        OrdProblem p;
+        int rc = fill_problem(fn, qs[i], a_dtype, p, tiles);
+        if (rc) return rc;
+        if (qs[i].K == 0 && qs[i].M && qs[i].N) {
+            // empty folds: +0.0 for every output of every batch entry
+            for (int64_t b = 0; b < qs[i].batch; ++b) {
+                hipError_t e = fill_zero(qs[i].C + b * qs[i].stride_c, qs[i].ldc, qs[i].M, qs[i].N, s);
+                if (e != hipSuccess) return launched(fn, e);
+            }
+            continue;
+        }
+        if (tiles == 0) continue;
+        g.p[n] = p;
+        g.tile_start[n] = (int32_t)total;
+        total += tiles;
+        if (total > I32MAX) return fail(GGO_EUNSUPPORTED, "%s: more than 2^31-1 tiles", fn);
+        ++n;
+    }
+    if (n == 0) return ok();
+    g.count = n;
+    g.tile_start[n] = (int32_t)total;
+    return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_ordered(const void* A, int a_dtype, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
+                 int64_t M, int64_t N, int64_t K, void* stream) {
+    ggo_problem q;
+    q.A = A;
+    q.W = W;
+    q.C = C;
+    q.lda = lda;
+    q.ldw = ldw;
+    q.ldc = ldc;
+    q.batch = 1;
+    q.stride_a = q.stride_w = q.stride_c = 0;
+    q.M = M;
+    q.N = N;
+    q.K = K;
+    return run_group("gemm_ordered", &q, 1, a_dtype, static_cast<hipStream_t>(stream));
+}
+
+int gemm_ordered_grouped(const ggo_problem* problems, int64_t count, int a_dtype, void* stream) {
+    return run_group("gemm_ordered_grouped", problems, count, a_dtype, static_cast<hipStream_t>(stream));
+}
+
+int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw, float* y, int64_t ldy, int64_t M,
+                 int64_t N, int64_t K, void* stream) {
+    const char* fn = "gemv_ordered";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = check_mnk(fn, M, N, K);
+    if (rc) return rc;
+    if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d (gemm_ordered gives the same bits)", fn, (long long)M, GGO_GEMV_MAX_M);
+    if (M == 0 || N == 0) return ok();
+    if (!y || (K && (!x || !W))) return fail(GGO_EINVAL, "%s: null pointer", fn);
+    if (ldx < K || ldw < N || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
+    if (K == 0) return launched(fn, fill_zero(y, ldy, M, N, s));
+    GemvArgs a;
+    a.x = x;
+    a.W = W;
+    a.y = y;
+    a.ldx = ldx;
+    a.ldw = ldw;
+    a.ldy = ldy;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.vec = 0;
+    if (aligned(W, 16) && ldw % 8 == 0) a.vec |= VEC_W;
+    if (aligned(x, 16) && ldx % 8 == 0) a.vec |= VEC_A;
+    if (aligned(y, 16) && ldy % 4 == 0) a.vec |= VEC_C;
+    return launched(fn, launch_gemv_ordered(a, s));
+}
+
+int gemm_mfma_invariant(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
+                        int64_t M, int64_t N, int64_t K, void* stream) {
+    const char* fn = "gemm_mfma_invariant";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = check_mnk(fn, M, N, K);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return ok();
+    if (!C || (K && (!A || !W))) return fail(GGO_EINVAL, "%s: null pointer", fn);
+    if (lda < K || ldw < N || ldc < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
+    if (K == 0) return launched(fn, fill_zero(C, ldc, M, N, s));
+    int bm, bn;
+    mfma_tile_shape(&bm, &bn);
+    MfmaArgs a;
+    a.A = A;
+    a.W = W;
+    a.C = C;
+    a.lda = lda;
+    a.ldw = ldw;
+    a.ldc = ldc;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+    if (tm * tn > I32MAX) return fail(GGO_EUNSUPPORTED, "%s: too many tiles", fn);
+    a.tiles_m = (int32_t)tm;
+    a.tiles_n = (int32_t)tn;
+    a.vec = 0;
+    if (aligned(A, 16) && lda % 8 == 0) a.vec |= VEC_A;
+    if (aligned(W, 8) && ldw % 4 == 0) a.vec |= VEC_W;
+    return launched(fn, launch_gemm_mfma_invariant(a, s));
+}
+
+const char* ggo_build_info(void) { return GGO_BUILD_INFO; }
+
+const char* ggo_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Launch-side declarations shared by the kernel sources and the C-ABI shim.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ggo.h"
+
+enum : uint32_t { VEC_A = 1u, VEC_W = 2u, VEC_C = 4u };
+
+// One ordered problem as the kernel sees it (passed by value in the kernel arguments).
+struct OrdProblem {
+    const void* A;
+    const uint16_t* W;
+    float* C;
+    int64_t lda, ldw, ldc;
+    int64_t sa, sw, sc;
+    int32_t M, N, K, batch;
+    int32_t tiles_m, tiles_n;
+    uint32_t vec;     // VEC_* bits: 16-byte loads / stores allowed
+};
+
+struct OrdGroup {
+    int32_t count;
+    int32_t tile_start[GGO_MAX_PROBLEMS + 1];   // prefix sums of batch * tiles_m * tiles_n
+    OrdProblem p[GGO_MAX_PROBLEMS];
+};
+
+void ordered_tile_shape(int* bm, int* bn);
+hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, hipStream_t stream);
+
+struct GemvArgs {
+    const uint16_t* x;
+    const uint16_t* W;
+    float* y;
+    int64_t ldx, ldw, ldy;
+    int32_t M, N, K;
+    uint32_t vec;
+};
+hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream);
+
+struct MfmaArgs {
+    const uint16_t* A;
+    const uint16_t* W;
+    float* C;
+    int64_t lda, ldw, ldc;
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n;
+    uint32_t vec;
+};
+void mfma_tile_shape(int* bm, int* bn);
+hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream);

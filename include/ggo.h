@@ -1,0 +1,177 @@
+/*
+ * ggo.h -- C-ABI of the batch-invariant matrix-multiply library for MI355X (gfx950).
+ *
+ * The library computes C[m, n] = sum_k A[m, k] * W[k, n] with bfloat16 (or
+ * binary32) A, bfloat16 W and binary32 results, in a reduction order the
+ * library owns: the bits of every output depend only on row m of A, column n
+ * of W and K -- never on M, on the tile an output falls in, on the number of
+ * compute units or on the launch configuration.
+ *
+ * Conventions shared by every entry point
+ *  - Layouts are row major. A is [M, K] with row stride lda >= K, W is [K, N]
+ *    with row stride ldw >= N, C is [M, N] with row stride ldc >= N. Strides
+ *    and sizes count elements, not bytes.
+ *  - Pointers marked "device" must be device memory of the current HIP device
+ *    (e.g. from torch); pointers marked "host" are host memory. The caller owns
+ *    every buffer; the library allocates no device memory and uses no
+ *    workspace.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Device calls only
+ *    enqueue work on it; they never synchronise.
+ *  - C must not overlap A or W. Inputs need no particular alignment: 16-byte
+ *    aligned operands with strides that are multiples of 8 take vector loads,
+ *    anything else takes element loads, with the same arithmetic and bits.
+ *  - No entry point selects a kernel, tile or split from M.
+ *  - Return value: GGO_OK (0), or a negative error code; the calling thread's
+ *    message is then available from ggo_last_error(). Zero-sized problems
+ *    (M, N or K == 0) are valid: C is filled with +0.0 when K == 0, and nothing
+ *    is touched when M or N is 0.
+ */
+#ifndef GGO_H
+#define GGO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GGO_OK            0
+#define GGO_EINVAL       -1 /* null pointer, negative size, stride below extent, bad dtype */
+#define GGO_EUNSUPPORTED -2 /* valid but outside what this entry point serves (e.g. M too large for gemv) */
+#define GGO_ELAUNCH      -3 /* the HIP runtime reported an error; see ggo_last_error() */
+
+#define GGO_BF16 0 /* A holds bfloat16 bit patterns (uint16_t) */
+#define GGO_F32  1 /* A holds IEEE binary32 values */
+
+/*
+ * gemm_ordered -- the order contract.
+ * Source: "Reproducible GPU inference", section "Three interventions, and what
+ * each was worth" (the kernel package's module docstring): one thread produces
+ * each output as a chain over k in increasing order of acc = acc + x*w, the
+ * product and the sum each rounded on its own, with no contraction and no
+ * fast-math; parallelism only across outputs.
+ * For every (m, n):  acc = +0.0f;  for k = 0 .. K-1:
+ *                        p = fl32(a[m,k] * w[k,n]);  acc = fl32(acc + p);
+ *                    C[m, n] = acc.
+ * Round to nearest even, subnormals kept. The result is bit-identical to a
+ * plain sequential CPU loop doing the same, for every M, tile and launch.
+ *   A      device, [M, K], bfloat16 bits (a_dtype GGO_BF16) or binary32 (GGO_F32)
+ *   W      device, [K, N] bfloat16 bits
+ *   C      device, [M, N] binary32, written (never read)
+ */
+int gemm_ordered(const void *A, int a_dtype, int64_t lda,
+                 const uint16_t *W, int64_t ldw,
+                 float *C, int64_t ldc,
+                 int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * One problem of gemm_ordered_grouped: `batch` independent products
+ * C_b = A_b W_b (b = 0 .. batch-1), A_b = A + b*stride_a (elements), likewise
+ * W_b and C_b. Used for the attention value product O = P V of "Reproducible
+ * GPU inference", section "Three interventions, and what each was worth"
+ * (owning the value product closed the last divergent card): P binary32
+ * [heads, L, L], V bfloat16 [heads, L, d], O binary32 [heads, L, d].
+ */
+typedef struct ggo_problem {
+    const void *A;      /* device */
+    const uint16_t *W;  /* device */
+    float *C;           /* device */
+    int64_t lda, ldw, ldc;
+    int64_t batch;
+    int64_t stride_a, stride_w, stride_c;
+    int64_t M, N, K;
+} ggo_problem;
+
+#define GGO_MAX_PROBLEMS 16
+
+/*
+ * gemm_ordered_grouped -- several ordered products in one launch, each with
+ * exactly the gemm_ordered arithmetic, so every output's bits are the same as
+ * when its problem runs alone, whatever else shares the launch and in
+ * whatever order.
+ *   problems  host array of `count` descriptors (1 <= count <= GGO_MAX_PROBLEMS);
+ *             copied at the call, so it may be reused as soon as the call returns
+ *   a_dtype   applies to every problem
+ */
+int gemm_ordered_grouped(const ggo_problem *problems, int64_t count, int a_dtype, void *stream);
+
+/*
+ * gemv_ordered -- decode shapes (few rows): the same order contract and bits
+ * as gemm_ordered, with W streamed from memory once per call.
+ *   x   device, [M, K] bfloat16 bits, row stride ldx
+ *   W   device, [K, N] bfloat16 bits
+ *   y   device, [M, N] binary32
+ *   1 <= M <= GGO_GEMV_MAX_M, else GGO_EUNSUPPORTED (use gemm_ordered: same bits).
+ */
+#define GGO_GEMV_MAX_M 16
+int gemv_ordered(const uint16_t *x, int64_t ldx,
+                 const uint16_t *W, int64_t ldw,
+                 float *y, int64_t ldy,
+                 int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * gemm_mfma_invariant -- bfloat16 matrix-core product, batch invariant.
+ * Source: "Taming Bitwise Behavior in GPU Kernels with Tensor Core", sections
+ * 3.2.1 and 3.2.2: a matrix instruction folds a fixed group of instruction_k
+ * products into the accumulator; the order of an output is fixed by
+ * instruction_k, by how the accumulator is carried, and by where a short K
+ * step falls; the block sizes only move work between threads.
+ * Descriptor of this kernel: one opcode for every call
+ * (v_mfma_f32_16x16x32_bf16, instruction_k = 32); the binary32 accumulator is
+ * carried through the instruction's accumulator input from k = 0 upwards,
+ * one group of 32 k at a time; a K that is not a multiple of 32 is padded
+ * with zeros in its last group; no split of K, no workspace, no atomics. So
+ * the bits of C[m, n] depend only on row m of A, column n of W and K.
+ * The result is within 2*K*2^-24*sum_k |a*w| + 2^-8*|c| of the exact sum c.
+ *   A  device, [M, K] bfloat16 bits;  W  device, [K, N] bfloat16 bits;
+ *   C  device, [M, N] binary32
+ */
+int gemm_mfma_invariant(const uint16_t *A, int64_t lda,
+                        const uint16_t *W, int64_t ldw,
+                        float *C, int64_t ldc,
+                        int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * Float Freivalds certificate, run on the host.
+ * Source: "Same Bits on the CPU and the GPU", section "The CPU as a checker: a
+ * float Freivalds certificate": for a sampled GEMV y = xW and a random vector
+ * r of +1/-1 over the outputs, the residual |r.y - (W r).x| is compared with a
+ * bound; W r is computed once per matrix in binary64 (8 bytes per input index).
+ *
+ * freivalds_prepare: once per matrix.
+ *   W   host, [K, N] bfloat16 bits, row stride ldw
+ *   r   host, N signs, each +1 or -1 (else GGO_EINVAL)
+ *   s, q, a   host, K doubles each, written:
+ *       s[k] = sum_n w[k,n] r[n],  q[k] = ||w[k,:]||_2,  a[k] = sum_n |w[k,n]|
+ */
+int freivalds_prepare(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
+                      const int8_t *r, double *s, double *q, double *a);
+
+/*
+ * freivalds_check: one sampled row.
+ *   x    host, K bfloat16 bits (the GEMV input row)
+ *   y    host, N binary32 (the GPU output row, copied back by the caller)
+ *   c_f  the calibrated constant (0.125 is the frozen value of the pages)
+ *   out  host, 4 doubles, written: rho, sigma, tau = c_f * sigma, and the
+ *        rigorous bound gamma_{K-1} * sum_k |x_k| a[k] (+ host rounding), where
+ *        rho = |sum_n r[n] y[n] - sum_k x[k] s[k]|,
+ *        sigma = 2^-24 * sqrt(K) * sum_k |x[k]| q[k].
+ * Returns 1 when rho <= tau (accept), 0 when not (reject), <0 on bad arguments.
+ * A single faulty output off by delta moves rho by exactly |delta|; a fault
+ * spread over outputs so that it cancels under r escapes with probability 1/2.
+ */
+int freivalds_check(const double *s, const double *q, const double *a,
+                    const int8_t *r, int64_t K, int64_t N,
+                    const uint16_t *x, const float *y, double c_f, double *out);
+
+/* Target, compiler, flags and the SHA-256 of every source the library was built from. */
+const char *ggo_build_info(void);
+
+/* Message of the calling thread's last failing call ("" when none). */
+const char *ggo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GGO_H */

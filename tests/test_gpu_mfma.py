@@ -1,0 +1,102 @@
+"""GPU tests of the matrix-core path: bitwise batch invariance across M and row
+position, the error bound against the binary64 reference, and the integer case
+where every summation order is exact (so the output must equal the oracle
+bit for bit)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import dev_bf16, f32_bits, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gemv_gemm_ordered_amd as g
+    return g
+
+
+def assert_within_bound(C, A, W, rows=None):
+    """|c - c*| <= 2 K 2^-24 sum|a w| + 2^-8 |c*| for every checked element."""
+    if rows is not None:
+        A = np.ascontiguousarray(A[rows])
+        C = C[rows]
+    D = oracle.gemm_f64(A, W, threads=16)
+    S = oracle.gemm_absdot_f64(A, W, threads=16)
+    K = A.shape[1]
+    bound = 2.0 * K * 2.0 ** -24 * S + 2.0 ** -8 * np.abs(D)
+    err = np.abs(C.astype(np.float64) - D)
+    assert (err <= bound).all(), f"max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def test_integer_data_exact(g):
+    for (M, N, K) in [(200, 300, 1000), (1, 1, 1), (129, 130, 4096), (64, 128, 32), (7, 33, 65)]:
+        A = synth.integer_bf16(M, "mi.A", (M, K))
+        W = synth.integer_bf16(N, "mi.W", (K, N))
+        ref = f32_bits(oracle.gemm_ordered(A, W, threads=16))
+        got = host_bits(g.gemm_mfma_invariant(dev_bf16(A), dev_bf16(W)))
+        assert np.array_equal(got, ref), (M, N, K)
+
+
+def test_gpt2_rows_identical_for_every_M_1_to_512(g):
+    A, W = synth.gpt2_projection(0, 512)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    full = host_bits(g.gemm_mfma_invariant(dA, dW))
+    assert_within_bound(full.view(np.float32), A, W)
+    say("mfma gpt2 M=1..512")
+    for M in range(1, 513):
+        got = host_bits(g.gemm_mfma_invariant(dA[:M], dW))
+        assert np.array_equal(got, full[:M]), M
+
+
+def test_mlp_sweep_invariant_and_bounded(g):
+    A, W = synth.mlp_up(0, 2048)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    full = host_bits(g.gemm_mfma_invariant(dA, dW))
+    for M in (64, 128, 256, 512, 1024):
+        assert np.array_equal(host_bits(g.gemm_mfma_invariant(dA[:M], dW)), full[:M]), M
+    rows = np.arange(0, 2048, 7)
+    r = assert_within_bound(full.view(np.float32), A, W, rows)
+    say(f"mlp max err/bound {r:.3g}")
+
+
+def test_row_position_and_repeat(g):
+    A, W = synth.mlp_up(1, 300)
+    dW = dev_bf16(W)
+    base = host_bits(g.gemm_mfma_invariant(dev_bf16(A), dW))
+    for pos in (0, 127, 128, 255, 299):
+        B = A.copy()
+        B[pos] = A[17]
+        assert np.array_equal(host_bits(g.gemm_mfma_invariant(dev_bf16(B), dW))[pos], base[17])
+    for _ in range(3):
+        assert np.array_equal(host_bits(g.gemm_mfma_invariant(dev_bf16(A), dW)), base)
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 333, 129), (130, 70, 33), (1, 1000, 4095), (256, 129, 31)])
+def test_ragged_bounded_and_invariant(g, M, N, K):
+    A = synth.normal_bf16(M, "mr.A", (M, K))
+    W = synth.normal_bf16(N, "mr.W", (K, N), 0.02)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    C = host_bits(g.gemm_mfma_invariant(dA, dW))
+    assert_within_bound(C.view(np.float32), A, W)
+    # each single row alone gives the same bits
+    for m in (0, M - 1):
+        assert np.array_equal(host_bits(g.gemm_mfma_invariant(dA[m:m + 1], dW))[0], C[m])
+    # misaligned / strided views give the same bits
+    dAp = dev_bf16(np.pad(A, ((0, 0), (1, 0))))
+    assert np.array_equal(host_bits(g.gemm_mfma_invariant(dAp[:, 1:], dW)), C)
+
+
+@pytest.mark.parametrize("n", [4096, 11008])
+def test_7b_projection_sampled(g, n):
+    say(f"mfma 7b n={n}")
+    A, W = synth.proj_7b(0, n)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    full = host_bits(g.gemm_mfma_invariant(dA, dW))
+    rows = np.array([0, 1, 1000, 2047, 4095])
+    assert_within_bound(full.view(np.float32), A, W, rows)
+    sub = host_bits(g.gemm_mfma_invariant(dA[1000:1128], dW))
+    assert np.array_equal(sub, full[1000:1128])

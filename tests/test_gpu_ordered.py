@@ -1,0 +1,187 @@
+"""GPU parity of the ordered path: gemm_ordered, gemv_ordered and the grouped
+value product, bit for bit against the CPU oracle on the same seeded inputs,
+plus row invariance across M and the edge cases (ragged, strided, misaligned,
+empty)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import dev_bf16, dev_f32, f32_bits, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gemv_gemm_ordered_amd as g
+    return g
+
+
+@pytest.fixture(scope="module")
+def gpt2():
+    A, W = synth.gpt2_projection(0, 512)
+    return A, W, f32_bits(oracle.gemm_ordered(A, W, threads=8)), dev_bf16(A), dev_bf16(W)
+
+
+def test_gpt2_projection_every_M_1_to_512(g, gpt2):
+    A, W, ref, dA, dW = gpt2
+    say("gemm_ordered gpt2 M=1..512")
+    for M in range(1, 513):
+        C = g.gemm_ordered(dA[:M], dW)
+        got = host_bits(C)
+        assert np.array_equal(got, ref[:M]), f"M={M}: {np.count_nonzero(got != ref[:M])} outputs differ"
+
+
+def test_row_content_at_any_position(g, gpt2):
+    A, W, ref, dA, dW = gpt2
+    for pos in (0, 1, 63, 64, 100):
+        B = A[:128].copy()
+        B[pos] = A[300]
+        got = host_bits(g.gemm_ordered(dev_bf16(B), dW))
+        assert np.array_equal(got[pos], ref[300])
+
+
+def test_mlp_up_full(g):
+    A, W = synth.mlp_up(0, 2048)
+    say("gemm_ordered mlp M=2048 oracle")
+    ref = f32_bits(oracle.gemm_ordered(A, W, threads=16))
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    for M in (64, 128, 256, 512, 1024, 2048):
+        got = host_bits(g.gemm_ordered(dA[:M], dW))
+        assert np.array_equal(got, ref[:M]), M
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (37, 333, 129), (65, 65, 65), (130, 70, 33), (3, 200, 1000), (64, 64, 32)])
+@pytest.mark.parametrize("a_dtype", ["bf16", "f32"])
+def test_ragged_shapes(g, M, N, K, a_dtype):
+    Af = synth.normal_f32(M + N + K, "rag.A", (M, K))
+    A = synth.f32_to_bf16_bits(Af) if a_dtype == "bf16" else Af
+    W = synth.normal_bf16(M + N + K, "rag.W", (K, N), 0.02)
+    ref = f32_bits(oracle.gemm_ordered(A, W))
+    dA = dev_bf16(A) if a_dtype == "bf16" else dev_f32(A)
+    assert np.array_equal(host_bits(g.gemm_ordered(dA, dev_bf16(W))), ref)
+
+
+def test_strided_and_misaligned_views(g):
+    A, W = synth.mlp_up(4, 96)
+    # row strides not multiples of 8, base pointers off 16-byte alignment
+    Av, Wv = A[1:90, 3:1003], np.ascontiguousarray(W[3:1003, :])[:, 5:400]
+    ref = f32_bits(oracle.gemm_ordered(np.ascontiguousarray(Av), np.ascontiguousarray(Wv)))
+    dA, dW = dev_bf16(A), dev_bf16(np.ascontiguousarray(W[3:1003, :]))
+    got = g.gemm_ordered(dA[1:90, 3:1003], dW[:, 5:400])
+    assert np.array_equal(host_bits(got), ref)
+    # output with a row stride wider than N
+    import torch
+    Cbig = torch.full((89, 512), float("nan"), device="cuda")
+    g.gemm_ordered(dA[1:90, 3:1003], dW[:, 5:400], C=None)
+    out = Cbig[:, 7:402]
+    g.gemm_ordered(dA[1:90, 3:1003], dW[:, 5:400], C=out)
+    assert np.array_equal(host_bits(out.contiguous()), ref)
+    assert torch.isnan(Cbig[:, :7]).all() and torch.isnan(Cbig[:, 402:]).all()
+
+
+def test_empty_and_zero_K(g):
+    import torch
+    A = torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((0, 7), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((5, 7), 3.0, device="cuda")
+    g.gemm_ordered(A, W, C=C)
+    assert (host_bits(C) == 0).all()
+    C2 = torch.full((5, 7), 3.0, device="cuda")
+    g.gemv_ordered(A, W, y=C2)
+    assert (host_bits(C2) == 0).all()
+    g.gemm_ordered(torch.zeros((0, 4), dtype=torch.bfloat16, device="cuda"),
+                   torch.zeros((4, 7), dtype=torch.bfloat16, device="cuda"))
+
+
+def test_worked_examples_on_gpu(g):
+    from tests.test_oracle_pins import GOLD, bf16_of, hexf
+    w1 = GOLD["W1_order"]
+    a = bf16_of([hexf(v) for v in w1["a"]])[None, :]
+    w = bf16_of([hexf(v) for v in w1["w"]])[:, None]
+    assert hex(host_bits(g.gemm_ordered(dev_bf16(a), dev_bf16(w)))[0, 0]) == w1["expected_bits"]
+    assert hex(host_bits(g.gemv_ordered(dev_bf16(a), dev_bf16(w)))[0, 0]) == w1["expected_bits"]
+    w2 = GOLD["W2_fma"]
+    a = np.array([[hexf(v) for v in w2["a"]]], dtype=np.float32)
+    w = bf16_of([hexf(v) for v in w2["w"]])[:, None]
+    assert "0x%08x" % host_bits(g.gemm_ordered(dev_f32(a), dev_bf16(w)))[0, 0] == w2["expected_bits"]
+
+
+def test_subnormals_kept_and_no_negative_zero(g):
+    from tests.test_oracle_pins import bf16_of
+    a = np.array([[1.0, -1.0, 2.0 ** -100, 2.0 ** -30], [2.0 ** -100, 0, 0, 0]], dtype=np.float32)
+    w = bf16_of([2.0 ** -40, 2.0 ** -40, 2.0 ** -40, -2.0 ** -110])[:, None]
+    ref = f32_bits(oracle.gemm_ordered(a, w))
+    assert np.array_equal(host_bits(g.gemm_ordered(dev_f32(a), dev_bf16(w))), ref)
+    assert ref[1, 0] != 0     # a subnormal result, kept
+
+
+def test_gemv_decode_matches_oracle_and_gemm(g):
+    say("gemv decode x[8,4096] W[4096,4096]")
+    x, W, _ = synth.decode_gemv(0, 8)
+    ref = f32_bits(oracle.gemm_ordered(x, W, threads=16))
+    dx, dW = dev_bf16(x), dev_bf16(W)
+    for M in (1, 4, 8):
+        y = host_bits(g.gemv_ordered(dx[:M], dW))
+        assert np.array_equal(y, ref[:M]), M
+        assert np.array_equal(host_bits(g.gemm_ordered(dx[:M], dW)), ref[:M])
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16])
+def test_gemv_ragged(g, M):
+    x = synth.normal_bf16(M, "gv.x", (M, 777))
+    W = synth.normal_bf16(M, "gv.W", (777, 1000), 0.02)
+    ref = f32_bits(oracle.gemm_ordered(x, W))
+    assert np.array_equal(host_bits(g.gemv_ordered(dev_bf16(x), dev_bf16(W))), ref)
+    # strided and misaligned
+    dxb = dev_bf16(np.pad(x, ((0, 0), (1, 2))))
+    dWb = dev_bf16(np.pad(W, ((0, 0), (3, 0))))
+    assert np.array_equal(host_bits(g.gemv_ordered(dxb[:, 1:778], dWb[:, 3:])), ref)
+
+
+def _pv_problem(seq, L, heads=4):
+    P, V = synth.pv_sequence(0, seq, L, heads=heads)
+    return P, V
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 64, 256])
+def test_pv_solo(g, L):
+    import torch
+    P, V = _pv_problem(0, L)
+    ref = np.stack([f32_bits(oracle.gemm_ordered(P[h], V[h])) for h in range(P.shape[0])])
+    dP, dV = dev_f32(P), dev_bf16(V)
+    O = torch.empty((P.shape[0], L, 128), dtype=torch.float32, device="cuda")
+    g.gemm_ordered_grouped([(dP, dV, O)])
+    assert np.array_equal(host_bits(O), ref)
+
+
+def test_pv_mixed_batches_every_order(g):
+    import torch
+    lens = [15, 16, 1, 64, 256, 15, 3, 100]
+    probs = [_pv_problem(i, L) for i, L in enumerate(lens)]
+    refs = [np.stack([f32_bits(oracle.gemm_ordered(P[h], V[h])) for h in range(P.shape[0])]) for P, V in probs]
+    dev = [(dev_f32(P), dev_bf16(V)) for P, V in probs]
+    rng = np.random.default_rng(0)
+    for trial in range(4):
+        order = rng.permutation(len(lens)) if trial else np.arange(len(lens))
+        outs = {i: torch.full((4, lens[i], 128), float("nan"), device="cuda") for i in order}
+        g.gemm_ordered_grouped([(dev[i][0], dev[i][1], outs[i]) for i in order])
+        for i in order:
+            assert np.array_equal(host_bits(outs[i]), refs[i]), (trial, i)
+
+
+def test_pv_long_sequences_sampled_rows(g):
+    import torch
+    for L in (1024, 5000):
+        say(f"pv L={L}")
+        heads = 2
+        P, V = _pv_problem(1, L, heads=heads)
+        dP, dV = dev_f32(P), dev_bf16(V)
+        O = torch.empty((heads, L, 128), dtype=torch.float32, device="cuda")
+        g.gemm_ordered_grouped([(dP, dV, O)])
+        got = host_bits(O)
+        rows = [0, 1, L // 2, L - 1]
+        for h in range(heads):
+            ref = f32_bits(oracle.gemm_ordered(np.ascontiguousarray(P[h][rows]), V[h]))
+            assert np.array_equal(got[h][rows], ref), (L, h)

@@ -1,0 +1,76 @@
+"""ISA gate over this repository's own gfx950 code objects.
+
+The order contract forbids contraction ("Reproducible GPU inference": no fused
+multiply-add, no fast-math), so the ordered kernels must hold no fused or dot
+instruction and must hold separate binary32 multiplies and adds. The MFMA
+kernel's order is fixed by its opcode ("Taming Bitwise Behavior in GPU Kernels
+with Tensor Core", section 3.2.2: instruction_k), so it must use exactly one
+matrix opcode. No kernel may use atomics (arrival order would move bits).
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BUILD = os.path.join(ROOT, "gemv_gemm_ordered_amd", "_build")
+LLVM = "/opt/rocm/llvm/bin"
+
+# floating-point fused or dot forms (integer address arithmetic such as v_mad_u64_u32 is fine)
+FUSED = re.compile(r"\b(v_(?:pk_)?(?:fma|fmac|mad|mac)_(?:f16|f32|f64|legacy\w*|mix\w*)|v_fma_mix\w*|v_dot\w*"
+                   r"|v_pk_mul_f32|v_pk_add_f32)\b")
+ATOMIC = re.compile(r"\b\w*atomic\w*\b")
+MFMA = re.compile(r"\b(v_mfma\w*|v_smfmac\w*)\b")
+
+
+def disassemble(obj):
+    tmp = obj + ".fatbin"
+    co = obj + ".gfx950.co"
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={tmp}", obj], check=True)
+    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={tmp}", f"--output={co}"], check=True)
+    out = subprocess.run([f"{LLVM}/llvm-objdump", "-d", "--no-show-raw-insn", co], check=True,
+                         capture_output=True, text=True).stdout
+    kernels, cur = {}, None
+    for line in out.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(\w+)>:", line)
+        if m:
+            cur = m.group(1)
+            kernels[cur] = []
+        elif cur and line.strip():
+            kernels[cur].append(line.strip())
+    return kernels
+
+
+@pytest.fixture(scope="module")
+def code():
+    if not os.path.isdir(BUILD):
+        pytest.skip("library not built")
+    return {src: disassemble(os.path.join(BUILD, src + ".o"))
+            for src in ("ordered_gemm.hip", "ordered_gemv.hip", "mfma_invariant.hip", "capi.cpp")}
+
+
+def test_ordered_kernels_have_no_contraction(code):
+    for src in ("ordered_gemm.hip", "ordered_gemv.hip"):
+        ks = [k for k in code[src] if "ordered" in k]
+        assert ks, src
+        for k in ks:
+            text = "\n".join(code[src][k])
+            assert not FUSED.search(text), (k, FUSED.search(text).group(0))
+            assert re.search(r"\bv_mul_f32", text) and re.search(r"\bv_add_f32", text), k
+            assert not MFMA.search(text), k
+
+
+def test_mfma_kernel_uses_one_opcode(code):
+    ks = [k for k in code["mfma_invariant.hip"] if "mfma_invariant" in k]
+    assert len(ks) == 1
+    ops = {m.group(1) for line in code["mfma_invariant.hip"][ks[0]] for m in [MFMA.search(line)] if m}
+    assert ops == {"v_mfma_f32_16x16x32_bf16"}, ops
+
+
+def test_no_atomics_anywhere(code):
+    for src, ks in code.items():
+        for k, lines in ks.items():
+            for line in lines:
+                assert not ATOMIC.search(line), (src, k, line)
