@@ -172,6 +172,9 @@ int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
     if (!y || (K && (!x || !W))) return fail(GGO_EINVAL, "%s: null pointer", fn);
     if (ldx < K || ldw < N || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
     if (K == 0) return launched(fn, fill_zero(y, ldy, M, N, s));
+    if (ldw > gemv_ordered_max_ldw() || K >= (int64_t(1) << 30))
+        return fail(GGO_EUNSUPPORTED, "%s: ldw=%lld or K=%lld too large for 32-bit buffer offsets (gemm_ordered gives the same bits)",
+                    fn, (long long)ldw, (long long)K);
     GemvArgs a;
     a.x = x;
     a.W = W;
@@ -183,9 +186,10 @@ int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
     a.N = (int32_t)N;
     a.K = (int32_t)K;
     a.vec = 0;
-    if (aligned(W, 16) && ldw % 8 == 0) a.vec |= VEC_W;
-    if (aligned(x, 16) && ldx % 8 == 0) a.vec |= VEC_A;
-    if (aligned(y, 16) && ldy % 4 == 0) a.vec |= VEC_C;
+    // wide loads: W as 4-byte column pairs at even n, x as 8-byte runs of 4 k
+    // (same arithmetic and bits either way; only the load width differs)
+    if (aligned(W, 4) && ldw % 2 == 0 && N % 2 == 0 && aligned(x, 8) && ldx % 4 == 0 && K % 4 == 0)
+        a.vec |= VEC_W | VEC_A;
     return launched(fn, launch_gemv_ordered(a, s));
 }
 

@@ -37,6 +37,7 @@ struct GemvArgs {
     uint32_t vec;
 };
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream);
+int gemv_ordered_max_ldw();   // buffer offsets of the GEMV kernel are 32-bit
 
 struct MfmaArgs {
     const uint16_t* A;

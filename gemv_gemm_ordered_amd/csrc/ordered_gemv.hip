@@ -5,12 +5,36 @@
 // (m, n) folds acc = acc + x[m,k]*W[k,n] over k = 0, 1, ..., K-1, product and
 // sum rounded separately, starting from +0.0.
 //
-// Design for gfx950: every output is a K-long dependent chain, so one wave
-// (64 lanes = 64 consecutive columns) owns one row m, and the grid spreads
-// (64-column slice, group of 4 rows) over workgroups so that all M*N chains run
-// at once. The four waves of a workgroup read the same W slice (coalesced
-// 128-byte rows, shared through the CU's L1); their x rows are staged in LDS
-// as binary32 and read as broadcasts.
+// Why the kernel is split into producers and a consumer. Every output is a
+// K-long chain of dependent binary32 adds held in one lane, and a gfx950 wave
+// issues about one VALU instruction every 4.5 clocks, so the chain costs at
+// least K * 4.5 clocks and every other instruction the owning wave issues per
+// k (the multiply, the bf16 widening, the loads) lengthens it. Here the owning
+// wave issues nothing per k but the add, plus one 16-byte LDS read per four k;
+// separate producer waves stream W, widen it, multiply it by x and leave the
+// rounded products in LDS. A product is the same binary32 value whichever
+// lane rounds it, so moving the multiply to another wave moves no bits
+// ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.1:
+// warp specialisation and pipelining leave the dependence tree unchanged).
+//
+// Workgroup = 16 output columns x 8 output rows, six waves:
+//   waves 0, 1   consumers: lane (r, c) = (lane / 16, lane % 16) of wave w owns
+//                y[m0 + 4w + r, n0 + c]
+//   waves 2 - 5  producers: lane q owns the 4(k) x 2(n) block (kq, np) of each
+//                64-k stage, for rows 4h .. 4h+3 (h = 0 for waves 2-3, 1 for 4-5)
+// Stages of products rotate through NBUF LDS buffers; the consumers run two
+// stages behind the producers so their LDS reads overlap the previous stage's
+// adds. W and x are prefetched DEPTH stages ahead in registers. Waves whose
+// rows all lie past M only keep the barrier count.
+//
+// Operands are read with raw buffer loads whose descriptors end exactly at the
+// last element the caller owns, so a load past that end returns 0 without
+// touching memory. That pads K to whole stages with W = 0 and x = 0: the
+// padded products are +0 (0 * 0), and acc + (+0) == acc for every value a
+// +0-started fold can hold (it is never -0), so the padding changes no bit.
+// Columns past N only feed chains that are never stored. The grid is
+// ceil(N/16) x ceil(M/8) workgroups, and each workgroup's column slice is
+// mapped XCD-contiguously so that slices sharing an L2 line run under one L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -18,46 +42,238 @@
 
 namespace {
 
-constexpr int THREADS = 256, ROWS = 4, COLS = 64;
-constexpr int KCH = 1024;   // x staged in LDS in chunks of KCH k per row
+constexpr int NS = 16;                 // output columns per workgroup
+constexpr int RG = 8;                  // output rows per workgroup
+constexpr int KC = 64;                 // k per stage
+constexpr int NBUF = 4;                // product stages resident in LDS
+constexpr int RUN = KC;                // floats per (row, column) run of products
+constexpr int NQ = KC / 4;             // 16-byte consumer reads per stage
+constexpr int CONSUMERS = RG / 4;      // consumer waves (4 rows x 16 columns each)
+constexpr int THREADS = 64 * CONSUMERS + 256;
+constexpr int TASKS = (KC / 4) * (NS / 2);   // 4(k) x 2(n) product blocks per stage
+constexpr int BUF_DWORD3 = 0x00020000; // buffer descriptor word 3: raw 32-bit data, range checked
 
+static_assert(2 * TASKS == 256, "two producer lanes (row halves) per block");
+
+// Position of the 4 products (k4*4 .. k4*4+3) of run `run` (= row*NS + column)
+// inside a stage buffer. The 16-byte slot index is XOR-swizzled so that both
+// the producers' writes (8 lanes: one kq, columns 0,2,..,14 or 1,3,..,15) and
+// the consumers' reads (8 lanes: 8 consecutive runs, one k4) fall in 8
+// distinct groups of 4 banks.
+GGO_DEV int slot(int run, int k4) { return run * RUN + ((k4 ^ ((run + (run >> 3)) & 7)) << 2); }
+
+// One stage of one producer lane, as loaded: W[k+i][n .. n+1] and
+// x[m0+4h+j][k .. k+3]. WIDE: one 4-byte load per W pair and one 8-byte load
+// per x quad (8 loads). Otherwise one 2-byte load per element (24 loads), for
+// operands whose alignment or extents rule the wide loads out.
+template <bool WIDE> struct Fetch;
+template <> struct Fetch<true> {
+    uint32_t w[4];
+    uint2 x[4];
+};
+template <> struct Fetch<false> {
+    uint16_t w[4][2];
+    uint16_t x[4][4];
+};
+
+// Per-lane constants: byte offsets of the lane's W elements inside a stage,
+// the lane's byte offset into a row of x, and the descriptors of its x rows.
+struct Lane {
+    int wof[4][2];
+    int xof;
+    __amdgpu_buffer_rsrc_t xr[4];
+};
+
+// W descriptor of one stage: it starts at row stage*KC and ends right after
+// the last element of W the caller owns (row K-1, column N-1), so rows past K
+// read as 0; stages wholly past K have an empty range.
+GGO_DEV __amdgpu_buffer_rsrc_t w_rsrc(const GemvArgs& a, int stage) {
+    const int rows_left = a.K - stage * KC;
+    const int nrec = rows_left <= 0 ? 0
+                   : rows_left >= KC ? KC * static_cast<int>(a.ldw) * 2
+                                     : ((rows_left - 1) * static_cast<int>(a.ldw) + a.N) * 2;
+    const int64_t row0 = rows_left <= 0 ? 0 : static_cast<int64_t>(stage) * KC;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.W) + row0 * a.ldw, 0, nrec, BUF_DWORD3);
+}
+
+GGO_DEV void fetch(const GemvArgs& a, const Lane& L, int stage, Fetch<true>& f) {
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(a, stage);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.w[i] = __builtin_amdgcn_raw_buffer_load_b32(wr, L.wof[i][0], 0, 0);
+    const int xo = L.xof + stage * KC * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(L.xr[j], xo, 0, 0);
+        f.x[j] = make_uint2(v[0], v[1]);
+    }
+}
+
+GGO_DEV void fetch(const GemvArgs& a, const Lane& L, int stage, Fetch<false>& f) {
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(a, stage);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) f.w[i][j] = __builtin_amdgcn_raw_buffer_load_b16(wr, L.wof[i][j], 0, 0);
+    const int xo = L.xof + stage * KC * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.x[j][i] = __builtin_amdgcn_raw_buffer_load_b16(L.xr[j], xo + 2 * i, 0, 0);
+}
+
+GGO_DEV void unpack_w(const Fetch<true>& f, float (&w0)[4], float (&w1)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w0[i] = bf16_lo(f.w[i]);
+        w1[i] = bf16_hi(f.w[i]);
+    }
+}
+GGO_DEV void unpack_w(const Fetch<false>& f, float (&w0)[4], float (&w1)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w0[i] = bf16_one(f.w[i][0]);
+        w1[i] = bf16_one(f.w[i][1]);
+    }
+}
+GGO_DEV void unpack_x(const Fetch<true>& f, int j, float (&xv)[4]) {
+    xv[0] = bf16_lo(f.x[j].x);
+    xv[1] = bf16_hi(f.x[j].x);
+    xv[2] = bf16_lo(f.x[j].y);
+    xv[3] = bf16_hi(f.x[j].y);
+}
+GGO_DEV void unpack_x(const Fetch<false>& f, int j, float (&xv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = bf16_one(f.x[j][i]);
+}
+
+// Products of one 4(k) x 2(n) block for the lane's live rows, written as
+// 16-byte runs of 4 ascending k.
+template <bool WIDE>
+GGO_DEV void produce(const Fetch<WIDE>& f, float* ps, int kq, int np, int r0, int rows) {
+    float w0[4], w1[4];
+    unpack_w(f, w0, w1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = r0 + j;
+        if (r >= rows) break;   // uniform across the wave
+        float xv[4];
+        unpack_x(f, j, xv);
+        const float4 p0 = make_float4(xv[0] * w0[0], xv[1] * w0[1], xv[2] * w0[2], xv[3] * w0[3]);
+        const float4 p1 = make_float4(xv[0] * w1[0], xv[1] * w1[1], xv[2] * w1[2], xv[3] * w1[3]);
+        const int run = r * NS + 2 * np;
+        *reinterpret_cast<float4*>(ps + slot(run, kq)) = p0;
+        *reinterpret_cast<float4*>(ps + slot(run + 1, kq)) = p1;
+    }
+}
+
+template <bool WIDE>
 __global__ __launch_bounds__(THREADS) void k_gemv_ordered(const GemvArgs a) {
-    __shared__ float xs[ROWS][KCH];
-    const int t = threadIdx.x;
-    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int m = blockIdx.y * ROWS + wv;
-    const int n = blockIdx.x * COLS + (t & 63);
-    const bool live = (m < a.M) && (n < a.N);
-    const int rows_here = a.M - blockIdx.y * ROWS < ROWS ? a.M - blockIdx.y * ROWS : ROWS;
-    const uint16_t* wcol = a.W + (n < a.N ? n : 0);
-    float acc = 0.0f;
+    // prefetch distance of W and x in stages (the wide ring keeps 64 loads in
+    // flight, the element ring 48), and an unroll that makes every ring index static
+    constexpr int DEPTH = WIDE ? 8 : 2;
+    constexpr int UNROLL = WIDE ? 8 : 4;
+    static_assert(UNROLL % NBUF == 0 && UNROLL % DEPTH == 0 && UNROLL % 2 == 0, "");
 
-    for (int k0 = 0; k0 < a.K; k0 += KCH) {
-        const int kb = a.K - k0 < KCH ? a.K - k0 : KCH;
+    __shared__ __attribute__((aligned(16))) float ps[NBUF][RG * NS * RUN];
+
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n0 = xcd_contiguous(blockIdx.x, gridDim.x) * NS;
+    const int m0 = blockIdx.y * RG;
+    const int rows = a.M - m0 < RG ? a.M - m0 : RG;
+    const int nst = (a.K + KC - 1) / KC;
+    // Iteration s (one barrier each): producers form stage s, the consumers
+    // read stage s-1 and fold stage s-2. The count is nst + 2 rounded up to a
+    // whole unroll, so ring indices stay static and the loop body has no early
+    // exit; iterations past the data skip the products and the adds.
+    const int iters = (nst + 2 + UNROLL - 1) / UNROLL * UNROLL;
+
+    // The consumers' stages -2 and -1 (their two-stage lag) read zeros: each
+    // chain's first two steps add +0 to +0.
+    for (int i = t; i < NBUF * RG * NS * RUN / 4; i += THREADS)
+        reinterpret_cast<float4*>(&ps[0][0])[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+
+    // Every role runs its own loop with the same number of barriers (iters,
+    // plus one before the loop). Inside a loop every iteration issues the same
+    // loads and reads (no conditional loads), so no register versions have to
+    // be merged and the prefetch ring stays in flight across barriers.
+    const bool consumer = wave < CONSUMERS;
+    const int first_row = consumer ? 4 * wave : 4 * __builtin_amdgcn_readfirstlane((t - 64 * CONSUMERS) / TASKS);
+    if (first_row >= rows) {   // no live row in this wave
         __syncthreads();
-        for (int i = t; i < rows_here * KCH; i += THREADS) {
-            const int r = i / KCH, kk = i - r * KCH;
-            const int64_t row = blockIdx.y * ROWS + r;
-            xs[r][kk] = kk < kb ? bf16_one(a.x[row * a.ldx + k0 + kk]) : 0.0f;
+        for (int s = 0; s < iters; ++s) __syncthreads();
+    } else if (!consumer) {
+        const int q = t - 64 * CONSUMERS;
+        const int task = q % TASKS;
+        const int kq = task >> 3, np = task & 7, n = n0 + 2 * np;
+        Lane L;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) L.wof[i][j] = ((4 * kq + i) * static_cast<int>(a.ldw) + n + j) * 2;
+        L.xof = 8 * kq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = first_row + j;
+            const bool live = r < rows;
+            L.xr[j] = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(a.x) + (live ? static_cast<int64_t>(m0 + r) * a.ldx : 0), 0,
+                live ? a.K * 2 : 0, BUF_DWORD3);
         }
+        Fetch<WIDE> f[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) fetch(a, L, d, f[d]);
         __syncthreads();
-        if (live) {
-            const uint16_t* wp = wcol + static_cast<int64_t>(k0) * a.ldw;
-#pragma unroll 8
-            for (int kk = 0; kk < kb; ++kk) {
-                const float w = bf16_one(wp[static_cast<int64_t>(kk) * a.ldw]);
-                const float p = xs[wv][kk] * w;   // first rounding
-                acc = acc + p;                    // second rounding
+        for (int s0 = 0; s0 < iters; s0 += UNROLL) {
+#pragma unroll
+            for (int d = 0; d < UNROLL; ++d) {
+                const int s = s0 + d;
+                if (s < nst) produce<WIDE>(f[d % DEPTH], ps[d % NBUF], kq, np, first_row, rows);   // uniform
+                fetch(a, L, s + DEPTH, f[d % DEPTH]);   // empty range past the end: zeros, no memory access
+                __syncthreads();
             }
         }
+    } else {
+        const int run = t;   // = (4 * wave + lane / 16) * NS + lane % 16
+        float acc = 0.0f;    // +0.0: the chain's start
+        float4 cb[2][NQ];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) cb[0][j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __syncthreads();
+        for (int s0 = 0; s0 < iters; s0 += UNROLL) {
+#pragma unroll
+            for (int d = 0; d < UNROLL; ++d) {
+                const int s = s0 + d;
+                const float* src = ps[(d + NBUF - 1) % NBUF];
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) cb[(d + 1) & 1][j] = *reinterpret_cast<const float4*>(src + slot(run, j));
+                if (s < nst + 2) {   // uniform
+#pragma unroll
+                    for (int j = 0; j < NQ; ++j) {     // ascending k
+                        const float4 v = cb[d & 1][j];
+                        acc = acc + v.x;
+                        acc = acc + v.y;
+                        acc = acc + v.z;
+                        acc = acc + v.w;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        const int r = t >> 4, nn = n0 + (t & 15);
+        if (r < rows && nn < a.N) a.y[static_cast<int64_t>(m0 + r) * a.ldy + nn] = acc;
     }
-    if (live) a.y[static_cast<int64_t>(m) * a.ldy + n] = acc;
 }
 
 }  // namespace
 
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
-    const dim3 grid((a.N + COLS - 1) / COLS, (a.M + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL(k_gemv_ordered, grid, dim3(THREADS), 0, stream, a);
+    const dim3 grid((a.N + NS - 1) / NS, (a.M + RG - 1) / RG);
+    if (a.vec & VEC_W)
+        hipLaunchKernelGGL(k_gemv_ordered<true>, grid, dim3(THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_gemv_ordered<false>, grid, dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
+
+int gemv_ordered_max_ldw() { return ((1 << 30) - (1 << 16)) / (KC + 1); }

@@ -129,15 +129,22 @@ def test_gemv_decode_matches_oracle_and_gemm(g):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16])
-def test_gemv_ragged(g, M):
-    x = synth.normal_bf16(M, "gv.x", (M, 777))
-    W = synth.normal_bf16(M, "gv.W", (777, 1000), 0.02)
+@pytest.mark.parametrize("K,N", [(777, 1000), (772, 1000), (64, 16), (4, 2), (1, 1), (1092, 30), (2048, 4097)])
+def test_gemv_ragged(g, M, K, N):
+    # K % 4 == 0 and even N take the wide loads (edges masked), the rest element loads
+    say(f"gemv ragged M={M} K={K} N={N}")
+    x = synth.normal_bf16(M * 7 + K, "gv.x", (M, K))
+    W = synth.normal_bf16(N + K, "gv.W", (K, N), 0.02)
     ref = f32_bits(oracle.gemm_ordered(x, W))
     assert np.array_equal(host_bits(g.gemv_ordered(dev_bf16(x), dev_bf16(W))), ref)
     # strided and misaligned
     dxb = dev_bf16(np.pad(x, ((0, 0), (1, 2))))
     dWb = dev_bf16(np.pad(W, ((0, 0), (3, 0))))
-    assert np.array_equal(host_bits(g.gemv_ordered(dxb[:, 1:778], dWb[:, 3:])), ref)
+    assert np.array_equal(host_bits(g.gemv_ordered(dxb[:, 1:K + 1], dWb[:, 3:])), ref)
+    # strided but aligned (row strides a multiple of 8 elements)
+    dxa = dev_bf16(np.pad(x, ((0, 0), (0, 8 - K % 8 if K % 8 else 8))))
+    dWa = dev_bf16(np.pad(W, ((0, 0), (0, 8 - N % 8 if N % 8 else 8))))
+    assert np.array_equal(host_bits(g.gemv_ordered(dxa[:, :K], dWa[:, :N])), ref)
 
 
 def _pv_problem(seq, L, heads=4):
