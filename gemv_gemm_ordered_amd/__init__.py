@@ -47,12 +47,13 @@ def _load():
     lib.gemm_ordered_grouped.argtypes = [ct.POINTER(Problem), I64, I, P]
     lib.gemv_ordered.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.ggo_test_gemm_mfma_tile128.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.ggo_build_info.restype = ct.c_char_p
     lib.ggo_last_error.restype = ct.c_char_p
     for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
-              "freivalds_prepare", "freivalds_check"):
+              "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check"):
         getattr(lib, f).restype = I
     return lib
 
@@ -60,7 +61,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
-           "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error")
+           "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error")
 
 
 def build_info() -> str:
@@ -170,8 +171,7 @@ def gemv_ordered(x, W, y=None, stream=None):
     return y
 
 
-def gemm_mfma_invariant(A, W, C=None, stream=None):
-    """C = A W on the matrix cores, bits independent of M (A, W bf16; C float32)."""
+def _mfma(fn, A, W, C, stream):
     lda, ldw = _rowmajor(A, "A"), _rowmajor(W, "W")
     M, K = A.shape
     if not (_is_bf16(A) and _is_bf16(W)) or W.shape[0] != K:
@@ -179,9 +179,18 @@ def gemm_mfma_invariant(A, W, C=None, stream=None):
     N = W.shape[1]
     C = _out(C, M, N, A)
     ldc = _rowmajor(C, "C") if M and N else N
-    _raise(lib.gemm_mfma_invariant(A.data_ptr(), lda, W.data_ptr(), ldw, C.data_ptr(), ldc, M, N, K, _stream(stream)),
-           "gemm_mfma_invariant")
+    _raise(getattr(lib, fn)(A.data_ptr(), lda, W.data_ptr(), ldw, C.data_ptr(), ldc, M, N, K, _stream(stream)), fn)
     return C
+
+
+def gemm_mfma_invariant(A, W, C=None, stream=None):
+    """C = A W on the matrix cores, bits independent of M (A, W bf16; C float32)."""
+    return _mfma("gemm_mfma_invariant", A, W, C, stream)
+
+
+def test_gemm_mfma_tile128(A, W, C=None, stream=None):
+    """Test hook: the same descriptor on the 128x128 tile instance (must give the same bits)."""
+    return _mfma("ggo_test_gemm_mfma_tile128", A, W, C, stream)
 
 
 def _np(a, dtype):

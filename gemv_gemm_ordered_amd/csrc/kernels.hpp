@@ -48,5 +48,7 @@ struct MfmaArgs {
     int32_t tiles_m, tiles_n;
     uint32_t vec;
 };
-void mfma_tile_shape(int* bm, int* bn);
+void mfma_tile_shape(int* bm, int* bn);        // 256x128 instance (16-byte aligned operands)
+void mfma_tile_shape_t128(int* bm, int* bn);   // 128x128 instance (any operands)
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream);
+hipError_t launch_gemm_mfma_t128(const MfmaArgs& a, hipStream_t stream);

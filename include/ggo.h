@@ -122,6 +122,10 @@ int gemv_ordered(const uint16_t *x, int64_t ldx,
  * one group of 32 k at a time; a K that is not a multiple of 32 is padded
  * with zeros in its last group; no split of K, no workspace, no atomics. So
  * the bits of C[m, n] depend only on row m of A, column n of W and K.
+ * Operands that are 16-byte aligned with row strides that are multiples of 8
+ * (and below 2^22) run on 256x128 output tiles, all others on 128x128 tiles;
+ * both tile instances give every output the same bits. The choice never
+ * depends on M.
  * The result is within 2*K*2^-24*sum_k |a*w| + 2^-8*|c| of the exact sum c.
  *   A  device, [M, K] bfloat16 bits;  W  device, [K, N] bfloat16 bits;
  *   C  device, [M, N] binary32
@@ -130,6 +134,19 @@ int gemm_mfma_invariant(const uint16_t *A, int64_t lda,
                         const uint16_t *W, int64_t ldw,
                         float *C, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * ggo_test_gemm_mfma_tile128 -- test hook, not a production entry point: the
+ * gemm_mfma_invariant descriptor executed by its second tile instance
+ * (128x128 outputs per workgroup instead of 256x128), for any operands. The
+ * bits must equal gemm_mfma_invariant's; the tests use it to show that the
+ * block sizes are speed knobs only. Same arguments and errors as
+ * gemm_mfma_invariant.
+ */
+int ggo_test_gemm_mfma_tile128(const uint16_t *A, int64_t lda,
+                               const uint16_t *W, int64_t ldw,
+                               float *C, int64_t ldc,
+                               int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
  * Float Freivalds certificate, run on the host.

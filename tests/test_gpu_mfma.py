@@ -100,3 +100,18 @@ def test_7b_projection_sampled(g, n):
     assert_within_bound(full.view(np.float32), A, W, rows)
     sub = host_bits(g.gemm_mfma_invariant(dA[1000:1128], dW))
     assert np.array_equal(sub, full[1000:1128])
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 128, 64), (300, 200, 100), (513, 1000, 1111), (1, 4096, 4096),
+                                   (2048, 4096, 1024), (4096, 4096, 4096), (4096, 11008, 4096), (7, 33, 31)])
+def test_tile_instances_agree_bitwise(g, M, N, K):
+    """The 256x128 and the 128x128 tile instances feed every output the same operand values in the
+    same 32-k groups ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.2.2: block
+    sizes do not enter the order), so their outputs must be identical bit for bit."""
+    say(f"mfma tile instances M={M} N={N} K={K}")
+    A = synth.normal_bf16(M + 1, "ti.A", (M, K))
+    W = synth.normal_bf16(N + 2, "ti.W", (K, N), 0.02)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    c256 = host_bits(g.gemm_mfma_invariant(dA, dW))
+    c128 = host_bits(g.test_gemm_mfma_tile128(dA, dW))
+    assert np.array_equal(c256, c128), f"{np.count_nonzero(c256 != c128)} outputs differ"
