@@ -48,19 +48,20 @@ def _load():
     lib.gemv_ordered.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.ggo_test_gemm_mfma_tile128.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemm_mfma_invariant_wt.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.ggo_build_info.restype = ct.c_char_p
     lib.ggo_last_error.restype = ct.c_char_p
     for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
-              "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check"):
+              "ggo_test_gemm_mfma_tile128", "gemm_mfma_invariant_wt", "freivalds_prepare", "freivalds_check"):
         getattr(lib, f).restype = I
     return lib
 
 
 lib = _load()
 
-EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
+EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant", "gemm_mfma_invariant_wt",
            "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error")
 
 
@@ -186,6 +187,20 @@ def _mfma(fn, A, W, C, stream):
 def gemm_mfma_invariant(A, W, C=None, stream=None):
     """C = A W on the matrix cores, bits independent of M (A, W bf16; C float32)."""
     return _mfma("gemm_mfma_invariant", A, W, C, stream)
+
+
+def gemm_mfma_invariant_wt(A, WT, C=None, stream=None):
+    """C = A W with W given transposed (WT [N, K] bf16, k contiguous): the bits of gemm_mfma_invariant(A, W)."""
+    lda, ldwt = _rowmajor(A, "A"), _rowmajor(WT, "WT")
+    M, K = A.shape
+    if not (_is_bf16(A) and _is_bf16(WT)) or WT.shape[1] != K:
+        raise ValueError("A and WT must be bf16, WT [N, K]")
+    N = WT.shape[0]
+    C = _out(C, M, N, A)
+    ldc = _rowmajor(C, "C") if M and N else N
+    _raise(lib.gemm_mfma_invariant_wt(A.data_ptr(), lda, WT.data_ptr(), ldwt, C.data_ptr(), ldc, M, N, K,
+                                      _stream(stream)), "gemm_mfma_invariant_wt")
+    return C
 
 
 def test_gemm_mfma_tile128(A, W, C=None, stream=None):

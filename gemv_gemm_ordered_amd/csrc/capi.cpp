@@ -137,10 +137,13 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
 }
 
 // The 256x128 instance needs 16-byte aligned operands with row strides that
-// are multiples of 8 and below 2^22 (its buffer offsets are 32-bit); every
-// other call takes the 128x128 instance. Both give every output the same bits
-// (the same operand values in the same groups), so the choice, which never
-// looks at M, moves no bit.
+// are multiples of 8 and below 2^22 (its buffer offsets are 32-bit), and K and
+// N multiples of 8: it loads 16-byte chunks through range-checked buffer
+// descriptors that end at the caller's last element, and the range check
+// drops a whole dword that straddles that end, so no chunk may straddle it.
+// Every other call takes the 128x128 instance. Both give every output the
+// same bits (the same operand values in the same groups), so the choice,
+// which never looks at M, moves no bit.
 int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
              int64_t M, int64_t N, int64_t K, hipStream_t s, bool force_t128) {
     int rc = check_mnk(fn, M, N, K);
@@ -150,7 +153,7 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
     if (lda < K || ldw < N || ldc < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
     if (K == 0) return launched(fn, fill_zero(C, ldc, M, N, s));
     const bool wide = !force_t128 && aligned(A, 16) && lda % 8 == 0 && aligned(W, 16) && ldw % 8 == 0 &&
-                      lda < (int64_t(1) << 22) && ldw < (int64_t(1) << 22);
+                      lda < (int64_t(1) << 22) && ldw < (int64_t(1) << 22) && K % 8 == 0 && N % 8 == 0;
     int bm, bn;
     if (wide)
         mfma_tile_shape(&bm, &bn);
@@ -237,6 +240,43 @@ int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
 int gemm_mfma_invariant(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void* stream) {
     return run_mfma("gemm_mfma_invariant", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), false);
+}
+
+int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, int64_t ldwt, float* C, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, void* stream) {
+    const char* fn = "gemm_mfma_invariant_wt";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = check_mnk(fn, M, N, K);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return ok();
+    if (!C || (K && (!A || !WT))) return fail(GGO_EINVAL, "%s: null pointer", fn);
+    if (lda < K || ldwt < K || ldc < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
+    if (K == 0) return launched(fn, fill_zero(C, ldc, M, N, s));
+    // 16-byte chunks through range-checked descriptors: no chunk may straddle the end of a row of A or W^T
+    if (!aligned(A, 16) || lda % 8 || !aligned(WT, 16) || ldwt % 8 || lda >= (int64_t(1) << 22) ||
+        ldwt >= (int64_t(1) << 22) || K % 8)
+        return fail(GGO_EUNSUPPORTED,
+                    "%s: A and W^T must be 16-byte aligned with row strides that are multiples of 8 and below 2^22, "
+                    "and K a multiple of 8 (gemm_mfma_invariant takes any W [K, N] and gives the same bits)", fn);
+    int bm, bn;
+    mfma_tile_shape(&bm, &bn);
+    MfmaArgs a;
+    a.A = A;
+    a.W = WT;
+    a.C = C;
+    a.lda = lda;
+    a.ldw = ldwt;
+    a.ldc = ldc;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+    if (tm * tn > I32MAX) return fail(GGO_EUNSUPPORTED, "%s: too many tiles", fn);
+    a.tiles_m = (int32_t)tm;
+    a.tiles_n = (int32_t)tn;
+    a.vec = VEC_A | VEC_W;
+    if (aligned(C, 16) && ldc % 4 == 0) a.vec |= VEC_C;
+    return launched(fn, launch_gemm_mfma_invariant_wt(a, s));
 }
 
 int ggo_test_gemm_mfma_tile128(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,

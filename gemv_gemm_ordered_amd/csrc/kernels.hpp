@@ -52,3 +52,4 @@ void mfma_tile_shape(int* bm, int* bn);        // 256x128 instance (16-byte alig
 void mfma_tile_shape_t128(int* bm, int* bn);   // 128x128 instance (any operands)
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_t128(const MfmaArgs& a, hipStream_t stream);
+hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream);   // W given as W^T [N, K]

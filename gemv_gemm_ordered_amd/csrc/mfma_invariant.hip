@@ -168,14 +168,14 @@ __global__ __launch_bounds__(THREADS) void k_gemm_mfma_t128(const MfmaArgs p) {
 // ---------------------------------------------------------------------------
 // 256x128 instance.
 //
-// Tile 256(m) x 128(n) x 64(k), four waves in a 2 x 2 grid, each owning
+// Tile 256(m) x 128(n) x BK(k), four waves in a 2 x 2 grid, each owning
 // 128(m) x 64(n) = 8 x 4 blocks of 16 x 16 outputs (128 accumulator registers
 // per lane). Per 32-k group a wave issues 32 MFMAs against 16 LDS reads, so the
 // LDS read rate needed is about 60% of what a CU delivers.
 //
 // Operands move HBM -> LDS with direct-to-LDS 16-byte buffer loads (no
-// registers), double buffered: the next k-tile is in flight while the current
-// one is multiplied. Buffer descriptors end at the caller's last element, so
+// registers), triple buffered: the next two k-tiles are in flight while the
+// current one is multiplied. Buffer descriptors end at the caller's last element, so
 // rows past M and rows of W past K arrive as zeros; in the last k-tile the A
 // elements with k >= K are zeroed in LDS after they land. Chunks of 8 bf16 are
 // XOR-swizzled inside each LDS row so that the operand reads below are free of
@@ -189,18 +189,38 @@ __global__ __launch_bounds__(THREADS) void k_gemm_mfma_t128(const MfmaArgs p) {
 // gets element i of four consecutive 16-element rows).
 namespace t256 {
 
-constexpr int BM = 256, BN = 128, BK = 64, THREADS = 256;
-constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;   // bf16 per stage (48 KB)
+constexpr int BM = 256, THREADS = 256;
 constexpr int BUF_DWORD3 = 0x00020000;   // buffer descriptor word 3: raw 32-bit data, range checked
 constexpr int WAIT_VM0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima)
+constexpr int WAIT_LGKM0 = 0xC07F;       // s_waitcnt lgkmcnt(0) (vmcnt, expcnt left at their maxima)
 
 typedef __attribute__((address_space(3))) void lds_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// LDS position (in 16-byte chunks) of A chunk (row r, k-chunk c) and of W
-// chunk (k-row k, n-chunk c).
-GGO_DEV int a_phys(int r, int c) { return r * (BK / 8) + (c ^ (r & 7)); }
-GGO_DEV int b_phys(int k, int c) { return k * (BN / 8) + (c ^ ((k & 3) << 1)); }
+// s_waitcnt vmcnt(n), n < 64
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Tile geometry: 256(m) x BN(n) x BK(k), BN in {128, 256}, BK in {32, 64};
+// four waves in a 2 x 2 grid, each owning 128 x BN/2 outputs. WT: the caller
+// passes W transposed ([N, K], k contiguous), and its tile is held like A's.
+template <int BN, int BK, bool WT = false> struct Geo {
+    static constexpr int CA = BK / 8;                      // 16-byte chunks per A row (and per W^T row)
+    static constexpr int CB = WT ? BK / 8 : BN / 8;        // 16-byte chunks per W row (W^T: per row of n)
+    static constexpr int WI = 8, WJ = BN / 32;             // 16 x 16 blocks per wave (rows, columns)
+    static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
+    static constexpr int A_LOADS = BM * CA / THREADS;      // direct-to-LDS loads per thread and tile
+    static constexpr int B_LOADS = BK * BN / 8 / THREADS;
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static_assert(A_LOADS <= 8 && B_LOADS <= 8, "Ctx holds at most 8 offsets per operand");
+    // LDS position (in 16-byte chunks) of A chunk (row r, k-chunk c) and of W
+    // chunk (k-row k, n-chunk c); the XOR keeps the 8 lanes that one 16-byte
+    // read serves in one cycle (and the 16 lanes of one transposing read) on
+    // distinct groups of 4 banks.
+    static GGO_DEV int swz_a(int r) { return CA == 8 ? (r & 7) : ((r >> 1) & 3); }
+    static GGO_DEV int a_phys(int r, int c) { return r * CA + (c ^ swz_a(r)); }
+    static GGO_DEV int b_phys(int k, int c) { return k * CB + (c ^ ((k & 3) << 1)); }   // W, k-major
+    static GGO_DEV int t_phys(int n, int c) { return n * CA + (c ^ swz_a(n)); }         // W^T, like A
+};
 
 // Group-M rasterisation inside each XCD's contiguous range of tiles: 4 tile
 // rows walked column by column, so the tiles in flight on one XCD share few
@@ -215,84 +235,128 @@ GGO_DEV void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
     tn = in / gsize;
 }
 
-// The two stage buffers are separate LDS objects and the k-loop is unrolled
-// by two, so every load and read names its buffer statically: the compiler can
-// then see that the loads into one buffer never alias the reads of the other
-// and keeps the next tile in flight while the current one is multiplied.
-__shared__ __attribute__((aligned(16))) uint16_t lds_stage0[STAGE];
-__shared__ __attribute__((aligned(16))) uint16_t lds_stage1[STAGE];
-
 struct Ctx {
     const MfmaArgs* p;
     int m0, n0, t, wave, wm, wn, lr, lg, nkt, rows_left;
-    int aoff[8], boff[4];
+    int aoff[8], boff[8];
 };
 
-GGO_DEV void issue(const Ctx& c, int kt, uint16_t* sa) {
+template <int BN, int BK, bool WT>
+GGO_DEV void issue(const Ctx& c, int kt, uint16_t* __restrict__ sa) {
+    using G = Geo<BN, BK, WT>;
     const MfmaArgs& p = *c.p;
-    const int k0 = kt * BK;
-    const int nrec_a = c.m0 + BM < p.M ? BM * static_cast<int>(p.lda) * 2
+    // a tile past the end (kt >= nkt) gets empty ranges: its loads write zeros to LDS without touching memory
+    const bool live = kt < c.nkt;
+    const int k0 = live ? kt * BK : 0;
+    const int nrec_a = !live ? 0
+                     : c.m0 + BM < p.M ? BM * static_cast<int>(p.lda) * 2
                                        : ((c.rows_left - 1) * static_cast<int>(p.lda) + (p.K - k0)) * 2;
-    const int nrec_b = k0 + BK < p.K ? BK * static_cast<int>(p.ldw) * 2
+    // W: rows past K are past the range. W^T ([N, K], ldw its row stride): like A, rows past N are.
+    const int nrec_b = !live ? 0
+                     : WT ? (c.n0 + BN < p.N ? BN * static_cast<int>(p.ldw) * 2
+                                             : ((p.N - c.n0 - 1) * static_cast<int>(p.ldw) + (p.K - k0)) * 2)
+                     : k0 + BK < p.K ? BK * static_cast<int>(p.ldw) * 2
                                      : ((p.K - 1 - k0) * static_cast<int>(p.ldw) + (p.N - c.n0)) * 2;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.A) + static_cast<int64_t>(c.m0) * p.lda + k0, 0, nrec_a, BUF_DWORD3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.W) + static_cast<int64_t>(k0) * p.ldw + c.n0, 0, nrec_b, BUF_DWORD3);
-    uint16_t* sb = sa + A_ELEMS;
+        const_cast<uint16_t*>(p.W) + (WT ? static_cast<int64_t>(c.n0) * p.ldw + k0 : static_cast<int64_t>(k0) * p.ldw + c.n0),
+        0, nrec_b, BUF_DWORD3);
+    uint16_t* sb = sa + G::A_ELEMS;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < G::A_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t*)(sa + (j * THREADS + c.wave * 64) * 8), 16, c.aoff[j], 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::B_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_t*)(sb + (j * THREADS + c.wave * 64) * 8), 16, c.boff[j], 0, 0, 0);
 }
 
-// One k-tile: wait for its loads, zero A's k >= K if it is the last partial
-// tile, make it visible to every wave, start the next tile's loads into the
-// other buffer, then fold the two groups of 32 k into the accumulators.
-GGO_DEV void stage(const Ctx& c, int kt, uint16_t* cur, uint16_t* nxt, f32x4 (&acc)[8][4]) {
+// One k-tile (cur and nxt never overlap; saying so lets the compiler keep the
+// loads into nxt in flight while cur is read): wait for its loads, zero A's
+// k >= K if it is the last partial tile, make it visible to every wave, start
+// the loads of tile kt+NST-1 into the buffer of tile kt-1, then fold the
+// tile's groups of 32 k, in ascending order, into the accumulators.
+template <int BN, int BK, int NST, bool WT>
+GGO_DEV void stage(const Ctx& c, int kt, uint16_t* __restrict__ cur, uint16_t* __restrict__ nxt,
+                   f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ]) {
+    using G = Geo<BN, BK, WT>;
     const MfmaArgs& p = *c.p;
-    __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // this thread's loads of tile kt have landed in LDS
+    // this thread's loads of tile kt have landed (those of the next NST-2 tiles may still be in flight)
+    __builtin_amdgcn_s_waitcnt(wait_vm(G::LOADS * (NST - 2)));
     if ((kt + 1) * BK > p.K) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int ph = j * THREADS + c.t, r = ph >> 3, ch = (ph & 7) ^ (r & 7);
+        for (int j = 0; j < G::A_LOADS; ++j) {
+            const int ph = j * THREADS + c.t, r = ph / G::CA, ch = (ph % G::CA) ^ G::swz_a(r);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (kt * BK + 8 * ch + e >= p.K) cur[ph * 8 + e] = 0;
         }
+        if (WT) {   // W^T rows hold k contiguously too: zero its k >= K as well
+#pragma unroll
+            for (int j = 0; j < G::B_LOADS; ++j) {
+                const int ph = j * THREADS + c.t, r = ph / G::CA, ch = (ph % G::CA) ^ G::swz_a(r);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (kt * BK + 8 * ch + e >= p.K) cur[G::A_ELEMS + ph * 8 + e] = 0;
+            }
+        }
     }
-    __syncthreads();
-    if (kt + 1 < c.nkt) issue(c, kt + 1, nxt);   // the buffer of tile kt-1, free since the barrier
+    // Workgroup barrier without a memory fence: a fence would also wait for the
+    // loads of the following tiles, which must stay in flight. Every wave has
+    // waited for its own part of tile kt and for its own LDS writes, which is
+    // all the ordering this barrier has to provide.
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    issue<BN, BK, WT>(c, kt + NST - 1, nxt);   // into the buffer of tile kt-1, free since the barrier (empty past the end)
 
     const uint16_t* sa = cur;
-    const uint16_t* sb = cur + A_ELEMS;
+    const uint16_t* sb = cur + G::A_ELEMS;
 #pragma unroll
     for (int g = 0; g < BK / 32; ++g) {   // ascending groups of 32 k
-        bf16x8 af[8], wf[4];
+        bf16x8 af[G::WI], wf[G::WJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < G::WJ; ++j) {
+            if (WT) {   // W^T: 8 consecutive k of column n are one 16-byte chunk, as for A
+                wf[j] = *reinterpret_cast<const bf16x8*>(sb + G::t_phys(c.wn * (BN / 2) + j * 16 + c.lr, g * 4 + c.lg) * 8);
+                continue;
+            }
             // lanes 4t'+q of each 16-lane group point at k-row g*32 + 8*lg + t' (and +4), columns 4q..4q+3
             const int kr = g * 32 + 8 * c.lg + (c.lr >> 2);
-            const int ch = c.wn * 8 + 2 * j + ((c.lr & 3) >> 1), half = (c.lr & 1) * 4;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + b_phys(kr, ch) * 8 + half));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + b_phys(kr + 4, ch) * 8 + half));
+            const int ch = c.wn * (BN / 16) + 2 * j + ((c.lr & 3) >> 1), half = (c.lr & 1) * 4;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + G::b_phys(kr, ch) * 8 + half));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + G::b_phys(kr + 4, ch) * 8 + half));
             const i16x4 v8[2] = {lo, hi};
             wf[j] = *reinterpret_cast<const bf16x8*>(v8);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            af[i] = *reinterpret_cast<const bf16x8*>(sa + a_phys(c.wm * 128 + i * 16 + c.lr, g * 4 + c.lg) * 8);
+        for (int i = 0; i < G::WI; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(sa + G::a_phys(c.wm * 128 + i * 16 + c.lr, g * 4 + c.lg) * 8);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < G::WI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < G::WJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
     }
 }
 
-__global__ __launch_bounds__(THREADS) void k_gemm_mfma_invariant(const MfmaArgs p) {
+// NST stage buffers: while tile kt is multiplied, the next NST-1 tiles are in
+// flight. The buffers are separate LDS objects and the k-loop is unrolled by
+// NST, so every load and read names its buffer statically: the compiler can
+// then see that the loads into one buffer never alias the reads of another.
+// The stages fill most of the LDS, so one workgroup runs per CU (one wave per
+// SIMD), and registers are not worth saving.
+template <int BN, int BK, int NST, bool WT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_mfma_invariant(const MfmaArgs p) {
+    using G = Geo<BN, BK, WT>;
+    static_assert(NST >= 2 && NST <= 4, "");
+    __shared__ __attribute__((aligned(16))) uint16_t lds_stage0[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_stage1[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_stage2[NST >= 3 ? G::STAGE : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_stage3[NST >= 4 ? G::STAGE : 8];
+    uint16_t* const buf[4] = {lds_stage0, lds_stage1, lds_stage2, lds_stage3};
     Ctx c;
     c.p = &p;
     int tm, tn;
@@ -309,39 +373,49 @@ __global__ __launch_bounds__(THREADS) void k_gemm_mfma_invariant(const MfmaArgs 
     c.rows_left = p.M - c.m0;
     // per-thread constant byte offsets of the chunks this thread loads
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int ph = j * THREADS + c.t, r = ph >> 3, ch = (ph & 7) ^ (r & 7);
+    for (int j = 0; j < G::A_LOADS; ++j) {
+        const int ph = j * THREADS + c.t, r = ph / G::CA, ch = (ph % G::CA) ^ G::swz_a(r);
         c.aoff[j] = (r * static_cast<int>(p.lda) + 8 * ch) * 2;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int ph = j * THREADS + c.t, k = ph >> 4, ch = (ph & 15) ^ ((k & 3) << 1);
-        c.boff[j] = (k * static_cast<int>(p.ldw) + 8 * ch) * 2;
+    for (int j = 0; j < G::B_LOADS; ++j) {
+        const int ph = j * THREADS + c.t;
+        if (WT) {   // row n of W^T, like A
+            const int r = ph / G::CA, ch = (ph % G::CA) ^ G::swz_a(r);
+            c.boff[j] = (r * static_cast<int>(p.ldw) + 8 * ch) * 2;
+        } else {
+            const int k = ph / G::CB, ch = (ph % G::CB) ^ ((k & 3) << 1);
+            c.boff[j] = (k * static_cast<int>(p.ldw) + 8 * ch) * 2;
+        }
     }
 
-    f32x4 acc[8][4];
+    f32x4 acc[G::WI][G::WJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < G::WI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < G::WJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    issue(c, 0, lds_stage0);
+#pragma unroll
+    for (int s = 0; s + 1 < NST; ++s) issue<BN, BK, WT>(c, s, buf[s]);
     int kt = 0;
-    for (; kt + 1 < c.nkt; kt += 2) {
-        stage(c, kt, lds_stage0, lds_stage1, acc);
-        stage(c, kt + 1, lds_stage1, lds_stage0, acc);
+    for (; kt + NST - 1 < c.nkt; kt += NST) {
+#pragma unroll
+        for (int s = 0; s < NST; ++s) stage<BN, BK, NST, WT>(c, kt + s, buf[s], buf[(s + NST - 1) % NST], acc);
     }
-    if (kt < c.nkt) stage(c, kt, lds_stage0, lds_stage1, acc);
+#pragma unroll
+    for (int s = 0; s + 1 < NST; ++s)
+        if (kt + s < c.nkt) stage<BN, BK, NST, WT>(c, kt + s, buf[s], buf[(s + NST - 1) % NST], acc);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the trailing empty-range loads have landed before the workgroup ends
 
     // lane holds C[row][col .. col+3] of each block: row = lane % 16, col = 4 * (lane / 16)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < G::WI; ++i) {
         const int row = c.m0 + c.wm * 128 + i * 16 + c.lr;
         if (row >= p.M) continue;
         float* crow = p.C + static_cast<int64_t>(row) * p.ldc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = c.n0 + c.wn * 64 + j * 16 + 4 * c.lg;
+        for (int j = 0; j < G::WJ; ++j) {
+            const int col = c.n0 + c.wn * (BN / 2) + j * 16 + 4 * c.lg;
             if (col + 4 <= p.N && (p.vec & VEC_C)) {
                 *reinterpret_cast<float4*>(crow + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             } else {
@@ -353,14 +427,24 @@ __global__ __launch_bounds__(THREADS) void k_gemm_mfma_invariant(const MfmaArgs 
     }
 }
 
+// The configuration both entry points run: 256 x 128 tiles, 64-k stages, three in flight.
+constexpr int BN_MAIN = 128, BK_MAIN = 64, NST_MAIN = 3;
+
 }  // namespace t256
 }  // namespace
 
-void mfma_tile_shape(int* bm, int* bn) { *bm = t256::BM; *bn = t256::BN; }
+void mfma_tile_shape(int* bm, int* bn) { *bm = t256::BM; *bn = t256::BN_MAIN; }
 void mfma_tile_shape_t128(int* bm, int* bn) { *bm = t128::BM; *bn = t128::BN; }
 
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(t256::k_gemm_mfma_invariant, dim3(a.tiles_m * a.tiles_n), dim3(t256::THREADS), 0, stream, a);
+    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, false>),
+                       dim3(a.tiles_m * a.tiles_n), dim3(t256::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, true>),
+                       dim3(a.tiles_m * a.tiles_n), dim3(t256::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -123,9 +123,9 @@ int gemv_ordered(const uint16_t *x, int64_t ldx,
  * with zeros in its last group; no split of K, no workspace, no atomics. So
  * the bits of C[m, n] depend only on row m of A, column n of W and K.
  * Operands that are 16-byte aligned with row strides that are multiples of 8
- * (and below 2^22) run on 256x128 output tiles, all others on 128x128 tiles;
- * both tile instances give every output the same bits. The choice never
- * depends on M.
+ * (and below 2^22), with K and N multiples of 8, run on 256x128 output tiles,
+ * all others on 128x128 tiles; both tile instances give every output the same
+ * bits. The choice never depends on M.
  * The result is within 2*K*2^-24*sum_k |a*w| + 2^-8*|c| of the exact sum c.
  *   A  device, [M, K] bfloat16 bits;  W  device, [K, N] bfloat16 bits;
  *   C  device, [M, N] binary32
@@ -134,6 +134,26 @@ int gemm_mfma_invariant(const uint16_t *A, int64_t lda,
                         const uint16_t *W, int64_t ldw,
                         float *C, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * gemm_mfma_invariant_wt -- gemm_mfma_invariant with W supplied transposed:
+ * WT is [N, K] (row n holds column n of W, k contiguous), row stride ldwt >= K.
+ * Weights are fixed across calls, so a caller transposes each W once and
+ * reuses it; with k contiguous in both operands every MFMA fragment is one
+ * 16-byte LDS read (a k-major W needs two transposing 8-byte reads per
+ * fragment, which costs 2.5x as much LDS time). The descriptor is
+ * gemm_mfma_invariant's and every output has exactly its bits:
+ * gemm_mfma_invariant_wt(A, W^T) == gemm_mfma_invariant(A, W) bit for bit.
+ *   A   device, [M, K] bfloat16 bits; 16-byte aligned, lda % 8 == 0, lda < 2^22
+ *   WT  device, [N, K] bfloat16 bits; 16-byte aligned, ldwt % 8 == 0, ldwt < 2^22
+ *   C   device, [M, N] binary32
+ *   K % 8 == 0.
+ * Operands that break these rules give GGO_EUNSUPPORTED.
+ */
+int gemm_mfma_invariant_wt(const uint16_t *A, int64_t lda,
+                           const uint16_t *WT, int64_t ldwt,
+                           float *C, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
  * ggo_test_gemm_mfma_tile128 -- test hook, not a production entry point: the

@@ -103,7 +103,8 @@ def test_7b_projection_sampled(g, n):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 64), (300, 200, 100), (513, 1000, 1111), (1, 4096, 4096),
-                                   (2048, 4096, 1024), (4096, 4096, 4096), (4096, 11008, 4096), (7, 33, 31)])
+                                   (2048, 4096, 1024), (4096, 4096, 4096), (4096, 11008, 4096), (7, 33, 31),
+                                   (513, 1000, 1112), (300, 200, 104), (257, 136, 1000), (1, 8, 8), (255, 1032, 72)])
 def test_tile_instances_agree_bitwise(g, M, N, K):
     """The 256x128 and the 128x128 tile instances feed every output the same operand values in the
     same 32-k groups ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.2.2: block
@@ -115,3 +116,40 @@ def test_tile_instances_agree_bitwise(g, M, N, K):
     c256 = host_bits(g.gemm_mfma_invariant(dA, dW))
     c128 = host_bits(g.test_gemm_mfma_tile128(dA, dW))
     assert np.array_equal(c256, c128), f"{np.count_nonzero(c256 != c128)} outputs differ"
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 128, 64), (300, 200, 104), (513, 1000, 1112), (1, 4096, 4096),
+                                   (2048, 4096, 1024), (4096, 11008, 4096), (7, 40, 32), (130, 137, 1000)])
+def test_transposed_w_entry_gives_the_same_bits(g, M, N, K):
+    """gemm_mfma_invariant_wt(A, W^T) feeds every MFMA the same operand values as
+    gemm_mfma_invariant(A, W), so the outputs must agree bit for bit."""
+    import torch
+    say(f"mfma W^T M={M} N={N} K={K}")
+    A = synth.normal_bf16(M + 3, "wt.A", (M, K))
+    W = synth.normal_bf16(N + 4, "wt.W", (K, N), 0.02)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    ref = host_bits(g.gemm_mfma_invariant(dA, dW))
+    # the W^T entry wants row strides that are multiples of 8: hold A and W^T in padded buffers
+    ld = (K + 7) // 8 * 8
+
+    def padded(x, rows, extra=0):
+        buf = torch.zeros((rows, ld + extra), dtype=torch.bfloat16, device="cuda")
+        buf[:, :K] = x
+        return buf[:, :K]
+
+    Ap, WTp = padded(dA, M), padded(dW.t(), N)
+    assert np.array_equal(host_bits(g.gemm_mfma_invariant_wt(Ap, WTp)), ref)
+    # a wider W^T row stride (still a multiple of 8)
+    assert np.array_equal(host_bits(g.gemm_mfma_invariant_wt(Ap, padded(dW.t(), N, 8))), ref)
+
+
+def test_transposed_w_entry_rejects_misaligned(g):
+    import torch
+    A = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    WT = torch.zeros((8, 65), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(g.GGOError, match="aligned"):
+        g.gemm_mfma_invariant_wt(A, WT[:, 1:])
+    A2 = torch.zeros((4, 16), dtype=torch.bfloat16, device="cuda")[:, :12]   # K = 12: not a multiple of 8
+    WT2 = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")[:, :12]
+    with pytest.raises(g.GGOError, match="multiple of 8"):
+        g.gemm_mfma_invariant_wt(A2, WT2)

@@ -62,11 +62,14 @@ def test_ordered_kernels_have_no_contraction(code):
             assert not MFMA.search(text), k
 
 
-def test_mfma_kernel_uses_one_opcode(code):
-    ks = [k for k in code["mfma_invariant.hip"] if "mfma_invariant" in k]
-    assert len(ks) == 1
-    ops = {m.group(1) for line in code["mfma_invariant.hip"][ks[0]] for m in [MFMA.search(line)] if m}
-    assert ops == {"v_mfma_f32_16x16x32_bf16"}, ops
+def test_mfma_kernels_use_one_opcode(code):
+    """Every matrix-core kernel (both tile instances, both W layouts) issues one and the same
+    opcode, so all of them fold each output with the same instruction_k."""
+    ks = [k for k in code["mfma_invariant.hip"] if "k_gemm_mfma" in k]
+    assert len(ks) >= 3, ks   # 256x128 (W and W^T) and the 128x128 instance
+    for k in ks:
+        ops = {m.group(1) for line in code["mfma_invariant.hip"][k] for m in [MFMA.search(line)] if m}
+        assert ops == {"v_mfma_f32_16x16x32_bf16"}, (k, ops)
 
 
 def test_no_atomics_anywhere(code):
