@@ -30,8 +30,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2516.0          # 256 CU x 4096 flop/clk x 2.4 GHz, dense
-VALU_CONTRACT_PEAK_TFS = 39.3        # unpacked v_mul_f32 + v_add_f32 per MAC (2 flop in 2 issues)
-VALU_NOMINAL_PEAK_TFS = 157.3        # packed FMA
+# The order contract multiplies and adds separately (two binary32 ops per MAC,
+# packed binary32 disabled). gfx950 executes a wave64 binary32 VALU op in two
+# passes of 32 lanes (measured: a SIMD completes one about every 2.2-2.5 clocks
+# with two waves), so 256 CU x 4 SIMD x 32 lanes x 2.4 GHz = 78.6 T ops/s, i.e.
+# 78.6 TFLOP/s counting 2 flop per MAC -- half the 157.3 TFLOP/s nominal (FMA).
+VALU_CONTRACT_PEAK_TFS = 78.6
+VALU_NOMINAL_PEAK_TFS = 157.3
 
 
 def log(*a):
@@ -154,6 +159,156 @@ def paths(g, reps):
     return out
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic of the GEMV kernel from rocprofv3 counters.
+#
+#   rocprofv3 --pmc FETCH_SIZE  ... -- python3 bench.py --counters
+#   rocprofv3 --pmc WRITE_SIZE  ... -- python3 bench.py --counters
+#   python3 bench.py --traffic-summary <fetch dir> <write dir>
+#
+# --counters launches a fixed sequence: COPY_REPS plain copies of COPY_BYTES
+# (torch's copy kernel: it reads and writes exactly COPY_BYTES), then
+# COUNTER_REPS GEMV launches for each M (rotating W). The summary scales each
+# GEMV counter value by what the same counter reads for the copy, writes
+# profiles/gemv_ordered_traffic.json (tagged with the SHA-256 of the GEMV
+# source) and a markdown summary; the bench reports the traffic only while the
+# library's GEMV source still has that hash.
+# ---------------------------------------------------------------------------
+COPY_BYTES = 256 << 20
+COPY_REPS = 3
+COUNTER_REPS = 4
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemv_ordered_traffic.json")
+GEMV_SOURCE = os.path.join(ROOT, "gemv_gemm_ordered_amd", "csrc", "ordered_gemv.hip")
+
+
+def gemv_source_sha256() -> str:
+    import hashlib
+    with open(GEMV_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def run_counters():
+    import torch
+
+    import gemv_gemm_ordered_amd as g
+    import synth
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    small = src[:(32 << 20) // 4]
+    small_dst = dst[:(32 << 20) // 4]
+    x, W, _ = synth.decode_gemv(0, 8)
+    dx = dev_bf16(x)
+    dWs = [dev_bf16(W)] + [None] * 3
+    for i in range(1, 4):
+        dWs[i] = dWs[0].clone()
+    ys = {M: torch.empty((M, 4096), device="cuda") for M in (1, 4, 8)}
+    torch.cuda.synchronize()
+    # calibration kernels, in this order: the runtime's copy blit, a plain
+    # elementwise copy (x + 0) of COPY_BYTES, the same of 32 MiB
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):
+        torch.add(small, 0.0, out=small_dst)
+    torch.cuda.synchronize()
+    i = 0
+    for M in (1, 4, 8):
+        for _ in range(COUNTER_REPS):
+            g.gemv_ordered(dx[:M], dWs[i % 4], y=ys[M])
+            i += 1
+        torch.cuda.synchronize()
+    print("counters sequence done", flush=True)
+
+
+def _counter_values(directory, counter):
+    """Per-dispatch values of `counter` (summed over its instances), in dispatch order, with kernel names."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    per = {}
+    for row in csv.DictReader(open(files[0])):
+        if row["Counter_Name"] != counter:
+            continue
+        d = int(row["Dispatch_Id"])
+        name, val = row["Kernel_Name"], float(row["Counter_Value"])
+        prev = per.get(d, (name, 0.0))
+        per[d] = (name, prev[1] + val)
+    return [per[d] for d in sorted(per)]
+
+
+def traffic_summary(fetch_dir, write_dir):
+    import statistics
+    out = {"source_sha256": gemv_source_sha256(), "copy_bytes": COPY_BYTES, "units": "bytes per launch"}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        seq = _counter_values(directory, counter)
+        # the last 3 * COPY_REPS dispatches before the GEMVs are the calibration copies:
+        # runtime blit (COPY_BYTES), elementwise copy (COPY_BYTES), elementwise copy (32 MiB)
+        others = [v for n, v in seq if "gemv" not in n]
+        gemvs = [v for n, v in seq if "gemv" in n]
+        if len(others) < 3 * COPY_REPS or len(gemvs) != 3 * COUNTER_REPS:
+            raise SystemExit(f"{counter}: unexpected dispatch sequence ({len(others)} others, {len(gemvs)} GEMVs)")
+        blit, plain, small = (others[len(others) - 3 * COPY_REPS + i * COPY_REPS:][:COPY_REPS] for i in range(3))
+        kib = statistics.median(plain)
+        factor = COPY_BYTES / (kib * 1024.0)   # bytes per counted KiB, from the plain elementwise copy
+        out[counter] = {"copy_counter_kib": kib, "bytes_per_counted_kib": factor,
+                        "check_blit_counter_kib": statistics.median(blit),
+                        "check_32MiB_copy_counter_kib": statistics.median(small)}
+        for j, M in enumerate((1, 4, 8)):
+            vals = gemvs[j * COUNTER_REPS:(j + 1) * COUNTER_REPS]
+            out.setdefault("per_M", {}).setdefault(str(M), {})[counter] = {
+                "counter_kib": statistics.median(vals), "bytes": statistics.median(vals) * 1024.0 * factor}
+    for M, rec in out["per_M"].items():
+        rec["algorithmic_bytes"] = gemv_bytes(int(M))
+        rec["hbm_bytes"] = rec["FETCH_SIZE"]["bytes"] + rec["WRITE_SIZE"]["bytes"]
+        rec["hbm_over_algorithmic"] = rec["hbm_bytes"] / rec["algorithmic_bytes"]
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    lines = ["# k_gemv_ordered — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
+             "Commands (from the repository root, on one MI355X):", "",
+             "    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/traffic_fetch -o run -- python3 $REPO/bench.py --counters",
+             "    cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/traffic_write -o run -- python3 $REPO/bench.py --counters",
+             "    python3 bench.py --traffic-summary gpurun_out/traffic_fetch gpurun_out/traffic_write", "",
+             f"Calibration: a plain elementwise copy of {COPY_BYTES >> 20} MiB (reads and writes {COPY_BYTES} "
+             f"bytes) reads FETCH_SIZE = {out['FETCH_SIZE']['copy_counter_kib']:.0f} KiB and WRITE_SIZE = "
+             f"{out['WRITE_SIZE']['copy_counter_kib']:.0f} KiB, so one counted KiB is "
+             f"{out['FETCH_SIZE']['bytes_per_counted_kib']:.3f} KiB fetched and "
+             f"{out['WRITE_SIZE']['bytes_per_counted_kib']:.3f} KiB written. Checks: the runtime's copy blit of "
+             f"the same size reads {out['FETCH_SIZE']['check_blit_counter_kib']:.0f} / "
+             f"{out['WRITE_SIZE']['check_blit_counter_kib']:.0f} KiB, an elementwise copy of 32 MiB "
+             f"{out['FETCH_SIZE']['check_32MiB_copy_counter_kib']:.0f} / "
+             f"{out['WRITE_SIZE']['check_32MiB_copy_counter_kib']:.0f} KiB.", "",
+             "| M | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|"]
+    for M, rec in sorted(out["per_M"].items(), key=lambda kv: int(kv[0])):
+        lines.append(f"| {M} | {rec['FETCH_SIZE']['counter_kib']:.0f} | {rec['WRITE_SIZE']['counter_kib']:.0f} | "
+                     f"{rec['hbm_bytes']:.0f} | {rec['algorithmic_bytes']} | {rec['hbm_over_algorithmic']:.3f} |")
+    lines += ["", f"GEMV source SHA-256: `{out['source_sha256']}` (the bench reports `traffic` only for this source)."]
+    with open(os.path.join(ROOT, "profiles", "gemv_ordered_decode_4096x4096_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_per_launch(ms):
+    """Mean counted HBM bytes per launch over the step's M values, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != gemv_source_sha256():
+        return None
+    try:
+        return sum(t["per_M"][str(M)]["hbm_bytes"] for M in ms) / len(ms)
+    except KeyError:
+        return None
+
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,7 +317,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-paths", action="store_true", help="skip the other paths' throughput")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of one graph replay")
+    ap.add_argument("--counters", action="store_true",
+                    help="run the fixed launch sequence for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 counter directories into profiles/gemv_ordered_traffic.json and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.counters:
+        run_counters()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library's path has no cross-GPU step, and this "
               "benchmark reports one GPU's throughput (--gpus 1).", file=sys.stderr)
@@ -267,7 +432,7 @@ def main():
                    "K": K, "N": N, "M_per_step": list(ms), "w_copies": copies,
                    "graph": run is not None, "parity": parity},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(ms),
                      "kernel": "k_gemv_ordered", "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch": step_bytes / len(ms)},
         "cpu_baseline": cpu,
