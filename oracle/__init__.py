@@ -39,6 +39,7 @@ def _bind(lib):
     lib.oracle_gemm_ordered.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_gemm_f64.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_gemm_absdot_f64.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
+    lib.oracle_gemv_tree.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.oracle_freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.oracle_freivalds_check.restype = I
@@ -104,6 +105,32 @@ def gemm_absdot_f64(A: np.ndarray, W: np.ndarray, threads: int = 1) -> np.ndarra
     A, W = _check(A, W)
     out = np.empty((A.shape[0], W.shape[1]), dtype=np.float64)
     return _rows(load().oracle_gemm_absdot_f64, A, W, out, threads)
+
+
+def gemv_tree(x: np.ndarray, WT: np.ndarray, threads: int = 1, lib=None) -> np.ndarray:
+    """The tree-ordered GEMV: x [M, K] bf16 bits, WT [N, K] bf16 bits (W transposed) -> float32 [M, N].
+
+    ``threads > 1`` splits the outputs' n range over threads; every output is computed whole by one
+    call, so the bytes equal a single-threaded run."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    WT = np.ascontiguousarray(WT, dtype=np.uint16)
+    assert x.ndim == 2 and WT.ndim == 2 and x.shape[1] == WT.shape[1], (x.shape, WT.shape)
+    M, K = x.shape
+    N = WT.shape[0]
+    out = np.empty((M, N), dtype=np.float32)
+    fn = (lib or load()).oracle_gemv_tree
+
+    def run(n0, n1):
+        if n1 > n0 and M > 0:
+            fn(_ptr(x), K, _ptr(WT[n0:]), K, _ptr(out[:, n0:]), N, M, n1 - n0, K)
+
+    if threads <= 1 or N < 2:
+        run(0, N)
+    else:
+        step = (N + threads - 1) // threads
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda n0: run(n0, min(N, n0 + step)), range(0, N, step)))
+    return out
 
 
 def freivalds_prepare(W: np.ndarray, r: np.ndarray):

@@ -25,6 +25,17 @@
  *    ascending in binary64. This is the reference the MFMA path's error bound
  *    is stated against.
  *
+ *  - oracle_gemv_tree: the tree-ordered GEMV. "Taming Bitwise Behavior in GPU
+ *    Kernels with Tensor Core", section 3.2.2 (the GEMV paragraph and Figure
+ *    2(d)): the lanes deal the k axis among themselves tile by tile, each
+ *    taking every countth tile, fold their own tiles as a chain of fused
+ *    multiply-adds, and then combine their totals through a butterfly; section
+ *    5.1 pins the butterfly to offsets counting up from 1, which makes it a
+ *    balanced pairwise tree whose first level adds neighbours. The tile
+ *    width (8 k), the number of chains (256) and the operand layout (W given
+ *    as its transpose, k contiguous) are this library's reading; they are
+ *    fixed for every shape, so the order depends on K alone.
+ *
  *  - oracle_freivalds_*: the float Freivalds certificate of "Same Bits on the
  *    CPU and the GPU" (section "The CPU as a checker: a float Freivalds
  *    certificate"): a +-1 vector r, the product of r with W precomputed once
@@ -127,6 +138,51 @@ void oracle_gemm_absdot_f64(const void *A, int a_dtype, int64_t lda,
             const uint16_t *wrow = W + k * ldw;
             for (int64_t n = 0; n < N; ++n)
                 s[n] += a * fabs((double)widen_bf16(wrow[n]));
+        }
+    }
+}
+
+/*
+ * Tree-ordered GEMV. x is [M, K] bfloat16 (row stride ldx), WT is the weight
+ * transposed, [N, K] bfloat16 (row stride ldwt), y is [M, N] binary32.
+ *
+ * Tile t holds k = 8t .. 8t+7 (the last tile stops at K). Chain p, for
+ * p = 0 .. 255, takes the tiles t = p, p + 256, p + 512, ... in ascending
+ * order and folds every k of them in ascending order as
+ *     acc = fmaf(x[m,k], WT[n,k], acc),   acc = +0.0f at the start,
+ * one rounding per step (fmaf is the correctly rounded C99 fused
+ * multiply-add). A chain with no tiles stays +0.0f. Then the 256 chain totals
+ * are reduced by halving: level 1 forms part[2i] + part[2i+1], level 2 adds
+ * neighbouring level-1 sums, ..., and level 8 gives y[m, n]. Every addition
+ * rounds to binary32 (nearest even).
+ */
+#define TREE_TILE 8
+#define TREE_CHAINS 256
+
+void oracle_gemv_tree(const uint16_t *x, int64_t ldx,
+                      const uint16_t *WT, int64_t ldwt,
+                      float *y, int64_t ldy,
+                      int64_t M, int64_t N, int64_t K)
+{
+    float part[TREE_CHAINS];
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * ldx;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t *wr = WT + n * ldwt;
+            for (int64_t p = 0; p < TREE_CHAINS; ++p) {
+                float acc = 0.0f;
+                for (int64_t t = p; t * TREE_TILE < K; t += TREE_CHAINS) {
+                    const int64_t k0 = t * TREE_TILE;
+                    const int64_t k1 = k0 + TREE_TILE < K ? k0 + TREE_TILE : K;
+                    for (int64_t k = k0; k < k1; ++k)
+                        acc = fmaf(widen_bf16(xr[k]), widen_bf16(wr[k]), acc);
+                }
+                part[p] = acc;
+            }
+            for (int64_t width = TREE_CHAINS; width > 1; width /= 2)
+                for (int64_t i = 0; i < width / 2; ++i)
+                    part[i] = part[2 * i] + part[2 * i + 1];
+            y[m * ldy + n] = part[0];
         }
     }
 }
