@@ -1,17 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the batch-invariant matmul library on one MI355X.
 
-Headline workload (one "step"): the decode GEMV of x[M, 4096] (bf16) by
-W[4096, 4096] (bf16), binary32 fold, for M = 1, 4 and 8, through gemv_ordered.
-Sixteen copies of W (512 MiB, twice the 256 MB Infinity Cache) are rotated so
-every launch streams its W from HBM. The value is GB/s of algorithmic traffic
-(2KN + 2MK + 4MN bytes per launch) over the timed steps. The timed steps are
-captured once in a HIP graph and replayed, so host launch overhead is not
-timed; HIP events on the launch stream bracket the replay.
+Headline workload (one "step"): the decode GEMV of x[M, 4096] (bf16) by a
+4096 x 4096 bf16 weight, binary32 result, for M = 1, 4 and 8, through
+gemv_tree (the tree order; the weight stored as a linear layer stores it,
+[N, K] with k contiguous). Sixteen copies of the weight (512 MiB, twice the
+256 MB Infinity Cache) are rotated so every launch streams its weight from
+HBM. The value is GB/s of algorithmic traffic (2KN + 2MK + 4MN bytes per
+launch) over the timed steps. The timed steps are captured once in a HIP graph
+and replayed, so host launch overhead is not timed; HIP events on the launch
+stream bracket the replay.
 
 Beside it, in the same JSON line:
-  roofline      the GEMV kernel against 8 TB/s HBM
-  cpu_baseline  the CPU oracle on the same step, one core, for ~10 s
+  roofline      the tree GEMV kernel against 8 TB/s HBM
+  cpu_baseline  the CPU oracle of the same step, one core, for ~10 s
+  per_M         per-M time of gemv_tree, of gemv_ordered (the one-lane chain
+                contract, weight [K, N]) and of torch.mm (hipBLASLt, not batch
+                invariant) on the same data
   certificate   Freivalds checks of sampled rows (honest pass, planted fault caught)
   paths         the other paths at their workloads: ordered GEMM and MFMA GEMM
                 TFLOP/s (MLP up-projection, 7B projections), the value product,
@@ -64,24 +69,46 @@ def time_region(fn, reps: int, warmup: int = 2) -> float:
     return s.elapsed_time(e) / reps
 
 
+def graph_time(fn, reps: int) -> float:
+    """Mean ms per call of fn(i) for i = 0 .. reps-1, captured once in a HIP graph and replayed
+    (HIP events on the current stream), so host launch overhead is not timed."""
+    import torch
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(reps):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    graph.replay()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / reps
+
+
 def gemv_bytes(M, K=4096, N=4096):
     return 2 * K * N + 2 * M * K + 4 * M * N
 
 
-def cpu_baseline(x, W, ms, seconds):
+def cpu_baseline(x, WT, ms, seconds):
+    """The oracle of the headline step (oracle.gemv_tree), one thread, whole steps until `seconds` pass."""
     import oracle
     steps, t0 = 0, time.perf_counter()
     while True:
         for M in ms:
-            oracle.gemm_ordered(x[:M], W, threads=1)
+            oracle.gemv_tree(x[:M], WT, threads=1)
         steps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
             break
     gbs = steps * sum(gemv_bytes(M) for M in ms) / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full decode steps (M={','.join(map(str, ms))}, K=N=4096), plain C oracle "
-                      f"single-threaded, {dt:.1f} s"}
+            "sample": f"{steps} full decode steps (M={','.join(map(str, ms))}, K=N=4096) of the tree-order "
+                      f"oracle, plain C, single-threaded, {dt:.1f} s"}
 
 
 def certificate(g, x, W, r, ys, ms):
@@ -160,7 +187,7 @@ def paths(g, reps):
 
 
 # ---------------------------------------------------------------------------
-# HBM traffic of the GEMV kernel from rocprofv3 counters.
+# HBM traffic of the tree GEMV kernel from rocprofv3 counters.
 #
 #   rocprofv3 --pmc FETCH_SIZE  ... -- python3 bench.py --counters
 #   rocprofv3 --pmc WRITE_SIZE  ... -- python3 bench.py --counters
@@ -170,15 +197,15 @@ def paths(g, reps):
 # (torch's copy kernel: it reads and writes exactly COPY_BYTES), then
 # COUNTER_REPS GEMV launches for each M (rotating W). The summary scales each
 # GEMV counter value by what the same counter reads for the copy, writes
-# profiles/gemv_ordered_traffic.json (tagged with the SHA-256 of the GEMV
+# profiles/gemv_tree_traffic.json (tagged with the SHA-256 of the kernel
 # source) and a markdown summary; the bench reports the traffic only while the
-# library's GEMV source still has that hash.
+# library's kernel source still has that hash.
 # ---------------------------------------------------------------------------
 COPY_BYTES = 256 << 20
 COPY_REPS = 3
 COUNTER_REPS = 4
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemv_ordered_traffic.json")
-GEMV_SOURCE = os.path.join(ROOT, "gemv_gemm_ordered_amd", "csrc", "ordered_gemv.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemv_tree_traffic.json")
+GEMV_SOURCE = os.path.join(ROOT, "gemv_gemm_ordered_amd", "csrc", "tree_gemv.hip")
 
 
 def gemv_source_sha256() -> str:
@@ -188,6 +215,7 @@ def gemv_source_sha256() -> str:
 
 
 def run_counters():
+    import numpy as np
     import torch
 
     import gemv_gemm_ordered_amd as g
@@ -198,7 +226,7 @@ def run_counters():
     small_dst = dst[:(32 << 20) // 4]
     x, W, _ = synth.decode_gemv(0, 8)
     dx = dev_bf16(x)
-    dWs = [dev_bf16(W)] + [None] * 3
+    dWs = [dev_bf16(np.ascontiguousarray(W.T))] + [None] * 3
     for i in range(1, 4):
         dWs[i] = dWs[0].clone()
     ys = {M: torch.empty((M, 4096), device="cuda") for M in (1, 4, 8)}
@@ -217,7 +245,7 @@ def run_counters():
     i = 0
     for M in (1, 4, 8):
         for _ in range(COUNTER_REPS):
-            g.gemv_ordered(dx[:M], dWs[i % 4], y=ys[M])
+            g.gemv_tree(dx[:M], dWs[i % 4], y=ys[M])
             i += 1
         torch.cuda.synchronize()
     print("counters sequence done", flush=True)
@@ -268,7 +296,7 @@ def traffic_summary(fetch_dir, write_dir):
         rec["hbm_over_algorithmic"] = rec["hbm_bytes"] / rec["algorithmic_bytes"]
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
-    lines = ["# k_gemv_ordered — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
+    lines = ["# k_gemv_tree — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
              "Commands (from the repository root, on one MI355X):", "",
              "    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/traffic_fetch -o run -- python3 $REPO/bench.py --counters",
              "    cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/traffic_write -o run -- python3 $REPO/bench.py --counters",
@@ -287,8 +315,9 @@ def traffic_summary(fetch_dir, write_dir):
     for M, rec in sorted(out["per_M"].items(), key=lambda kv: int(kv[0])):
         lines.append(f"| {M} | {rec['FETCH_SIZE']['counter_kib']:.0f} | {rec['WRITE_SIZE']['counter_kib']:.0f} | "
                      f"{rec['hbm_bytes']:.0f} | {rec['algorithmic_bytes']} | {rec['hbm_over_algorithmic']:.3f} |")
-    lines += ["", f"GEMV source SHA-256: `{out['source_sha256']}` (the bench reports `traffic` only for this source)."]
-    with open(os.path.join(ROOT, "profiles", "gemv_ordered_decode_4096x4096_traffic.md"), "w") as f:
+    lines += ["", f"Kernel source (tree_gemv.hip) SHA-256: `{out['source_sha256']}` (the bench reports `traffic` only "
+                  "for this source)."]
+    with open(os.path.join(ROOT, "profiles", "gemv_tree_decode_4096x4096_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -320,7 +349,7 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="run the fixed launch sequence for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 counter directories into profiles/gemv_ordered_traffic.json and exit")
+                    help="turn two rocprofv3 counter directories into profiles/gemv_tree_traffic.json and exit")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
@@ -344,17 +373,18 @@ def main():
     ms = (1, 4, 8)
     log("generating decode workload")
     x, W, r = synth.decode_gemv(0, 8)
+    WT = np.ascontiguousarray(W.T)
     dx = dev_bf16(x)
     copies = 16
-    dW0 = dev_bf16(W)
-    dWs = [dW0] + [dW0.clone() for _ in range(copies - 1)]
+    dWT0 = dev_bf16(WT)
+    dWTs = [dWT0] + [dWT0.clone() for _ in range(copies - 1)]
     ys = {M: torch.empty((M, N), device="cuda") for M in ms}
     step_bytes = sum(gemv_bytes(M) for M in ms)
     counter = [0]
 
     def step():
         for M in ms:
-            g.gemv_ordered(dx[:M], dWs[counter[0] % copies], y=ys[M])
+            g.gemv_tree(dx[:M], dWTs[counter[0] % copies], y=ys[M])
             counter[0] += 1
 
     log(f"warmup {args.warmup} steps")
@@ -362,6 +392,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    graph = None
     if args.no_graph:
         run = None
     else:
@@ -392,26 +423,40 @@ def main():
     avg_launch_us = 1e3 * ms_total / (args.steps * len(ms))
 
     # parity spot check of the timed kernel's last outputs against the oracle
-    ref = oracle.gemm_ordered(x[:8][[0, 7]], W, threads=2).view(np.uint32)
+    ref = oracle.gemv_tree(x[:8][[0, 7]], WT, threads=4).view(np.uint32)
     got = ys[8].cpu().numpy().view(np.uint32)[[0, 7]]
     parity = "bit-exact (rows 0 and 7 of M=8 vs CPU oracle)" if np.array_equal(got, ref) else "MISMATCH"
+    del graph
 
-    # per-M kernel time (events around 16 launches each, rotating W)
+    # per-M time (64 launches per M, rotating weights, one graph replay each): the tree GEMV, the
+    # ordered GEMV on W [K, N] (the one-lane chain contract) and hipBLASLt (not batch invariant)
+    dW0 = dev_bf16(W)
+    dWs = [dW0] + [dW0.clone() for _ in range(copies - 1)]
     per_m = {}
     for M in ms:
-        i = [0]
+        rec = {}
+        for name, fn in (("tree", lambda i: g.gemv_tree(dx[:M], dWTs[i % copies], y=ys[M])),
+                         ("ordered", lambda i: g.gemv_ordered(dx[:M], dWs[i % copies], y=ys[M])),
+                         ("hipblaslt", lambda i: torch.mm(dx[:M], dWTs[i % copies].t(), out_dtype=torch.float32))):
+            try:
+                t = graph_time(fn, 64)
+            except RuntimeError as err:      # a library that cannot be captured is timed eagerly
+                log(f"{name} M={M}: graph capture failed ({err}); eager timing")
+                i = [0]
 
-        def one():
-            g.gemv_ordered(dx[:M], dWs[i[0] % copies], y=ys[M])
-            i[0] += 1
-        t = time_region(one, 32)
-        per_m[str(M)] = {"us": round(1e3 * t, 2), "GBps": round(gemv_bytes(M) / t / 1e6, 1),
+                def one():
+                    fn(i[0])
+                    i[0] += 1
+                t = time_region(one, 64)
+            rec[name] = {"us": round(1e3 * t, 2), "GBps": round(gemv_bytes(M) / t / 1e6, 1),
                          "frac_hbm": round(gemv_bytes(M) / t / 1e6 / HBM_PEAK_GBS, 4)}
+        per_m[str(M)] = rec
+    del dWs
 
     cert = certificate(g, x, W, r, ys, ms)
     extra = {} if args.no_paths else paths(g, 10)
     log("cpu baseline")
-    cpu = cpu_baseline(x, W, ms, args.cpu_seconds)
+    cpu = cpu_baseline(x, WT, ms, args.cpu_seconds)
 
     achieved = (step_bytes / len(ms)) / (avg_launch_us * 1e-6) / 1e9
     line = {
@@ -427,13 +472,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded splitmix64/Box-Muller; x ~ N(0,1), W ~ N(0,0.02), bf16)",
-        "config": {"workload": "decode GEMV, gemv_ordered: x[M,4096] bf16 x W[4096,4096] bf16 -> y f32, "
-                               "M in {1,4,8} per step, 16 rotated W copies",
+        "config": {"workload": "decode GEMV, gemv_tree: x[M,4096] bf16 x W^T[4096,4096] bf16 -> y f32, "
+                               "M in {1,4,8} per step, 16 rotated weight copies",
                    "K": K, "N": N, "M_per_step": list(ms), "w_copies": copies,
                    "graph": run is not None, "parity": parity},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(ms),
-                     "kernel": "k_gemv_ordered", "avg_launch_us": round(avg_launch_us, 3),
+                     "kernel": "k_gemv_tree", "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch": step_bytes / len(ms)},
         "cpu_baseline": cpu,
         "per_M": per_m,

@@ -46,6 +46,7 @@ def _load():
     lib.gemm_ordered.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_ordered_grouped.argtypes = [ct.POINTER(Problem), I64, I, P]
     lib.gemv_ordered.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemv_tree.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.ggo_test_gemm_mfma_tile128.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant_wt.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
@@ -53,7 +54,7 @@ def _load():
     lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.ggo_build_info.restype = ct.c_char_p
     lib.ggo_last_error.restype = ct.c_char_p
-    for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
+    for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemm_mfma_invariant",
               "ggo_test_gemm_mfma_tile128", "gemm_mfma_invariant_wt", "freivalds_prepare", "freivalds_check"):
         getattr(lib, f).restype = I
     return lib
@@ -61,7 +62,8 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant", "gemm_mfma_invariant_wt",
+EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemm_mfma_invariant",
+           "gemm_mfma_invariant_wt",
            "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error")
 
 
@@ -87,7 +89,7 @@ def _is_bf16(t) -> bool:
 def _rowmajor(t, name):
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D, got {tuple(t.shape)}")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit stride along its last axis")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -169,6 +171,21 @@ def gemv_ordered(x, W, y=None, stream=None):
     ldy = _rowmajor(y, "y") if M and N else N
     _raise(lib.gemv_ordered(x.data_ptr(), ldx, W.data_ptr(), ldw, y.data_ptr(), ldy, M, N, K, _stream(stream)),
            "gemv_ordered")
+    return y
+
+
+def gemv_tree(x, WT, y=None, stream=None):
+    """y = x W for x bf16 [M <= 16, K] and the weight given transposed, WT bf16 [N, K] (k contiguous):
+    the tree order (8-k tiles dealt over 256 fused chains, count-up pairwise tree), bits independent of M."""
+    ldx, ldwt = _rowmajor(x, "x"), _rowmajor(WT, "WT")
+    M, K = x.shape
+    if not (_is_bf16(x) and _is_bf16(WT)) or WT.shape[1] != K:
+        raise ValueError("x and WT must be bf16, WT [N, K]")
+    N = WT.shape[0]
+    y = _out(y, M, N, x)
+    ldy = _rowmajor(y, "y") if M and N else N
+    _raise(lib.gemv_tree(x.data_ptr(), ldx, WT.data_ptr(), ldwt, y.data_ptr(), ldy, M, N, K, _stream(stream)),
+           "gemv_tree")
     return y
 
 

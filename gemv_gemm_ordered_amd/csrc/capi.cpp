@@ -237,6 +237,34 @@ int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
     return launched(fn, launch_gemv_ordered(a, s));
 }
 
+int gemv_tree(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy, int64_t M,
+              int64_t N, int64_t K, void* stream) {
+    const char* fn = "gemv_tree";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = check_mnk(fn, M, N, K);
+    if (rc) return rc;
+    if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d", fn, (long long)M, GGO_GEMV_MAX_M);
+    if (M == 0 || N == 0) return ok();
+    if (!y || (K && (!x || !WT))) return fail(GGO_EINVAL, "%s: null pointer", fn);
+    if (ldx < K || ldwt < K || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
+    if (K == 0) return launched(fn, fill_zero(y, ldy, M, N, s));
+    if (K > gemv_tree_max_k())
+        return fail(GGO_EUNSUPPORTED, "%s: K=%lld too large for 32-bit byte offsets along a row", fn, (long long)K);
+    TreeArgs a;
+    a.x = x;
+    a.WT = WT;
+    a.y = y;
+    a.ldx = ldx;
+    a.ldwt = ldwt;
+    a.ldy = ldy;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    // 16-byte tile loads when no tile can straddle the end of a row (same arithmetic and bits either way)
+    a.wide = aligned(x, 16) && ldx % 8 == 0 && aligned(WT, 16) && ldwt % 8 == 0 && K % 8 == 0;
+    return launched(fn, launch_gemv_tree(a, s));
+}
+
 int gemm_mfma_invariant(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void* stream) {
     return run_mfma("gemm_mfma_invariant", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), false);

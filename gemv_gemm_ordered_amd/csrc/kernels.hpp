@@ -39,6 +39,17 @@ struct GemvArgs {
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream);
 int gemv_ordered_max_ldw();   // buffer offsets of the GEMV kernel are 32-bit
 
+struct TreeArgs {
+    const uint16_t* x;
+    const uint16_t* WT;
+    float* y;
+    int64_t ldx, ldwt, ldy;
+    int32_t M, N, K;
+    int32_t wide;     // 16-byte loads allowed (alignment, strides and K multiples of 8)
+};
+hipError_t launch_gemv_tree(const TreeArgs& a, hipStream_t stream);
+int gemv_tree_max_k();   // byte offsets along a row are 32-bit
+
 struct MfmaArgs {
     const uint16_t* A;
     const uint16_t* W;

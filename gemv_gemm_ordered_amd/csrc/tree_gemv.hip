@@ -1,0 +1,237 @@
+// Tree-ordered GEMV for decode shapes: y[m, n] = sum_k x[m, k] * WT[n, k], with the weight given
+// transposed ([N, K], k contiguous: the layout of a linear layer's weight).
+//
+// The order ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.2.2, the GEMV
+// paragraph and Figure 2(d); section 5.1 for the pinned butterfly). It depends on K alone, never on
+// M, N, the workgroup shape or the launch:
+//   * the k axis is cut into tiles of 8; chain p (0 <= p < 256) takes the tiles p, p + 256,
+//     p + 512, ... and folds their k in ascending order with one fused multiply-add per k,
+//     acc = fma(x, w, acc), starting from +0;
+//   * the 256 chain totals are added by a balanced pairwise tree that pairs neighbours first
+//     (chains 2i and 2i+1, then neighbouring pairs, ...).
+// bfloat16 products are exact in binary32, so each fused step rounds only the sum.
+//
+// Mapping. A workgroup is four waves and owns R consecutive outputs n, for every row m of x (MT is
+// M rounded up to a power of two; rows past M read as zero and are not stored). Lane l of wave w
+// is chain p = 64 w + l. Step j of the lane loads tile p + 256 j of its R weight rows and of the
+// MT rows of x, 16 bytes each (a wave reads 1 KiB of one weight row per load), and folds the tile
+// into R x MT accumulators. The steps of a lane never wait on another lane.
+//
+// The tree then runs on the lanes. Within a wave the first six levels pair lanes l and l xor 1,
+// then l xor 2, ..., l xor 32, the count-up tree of section 5.1's wave reduction; since every lane
+// holds R x MT accumulators, each level also hands half of them to the partner lane, so a level
+// costs half the adds of the one before (a reduce-scatter). The last two levels add the four wave
+// totals, (w0 + w1) + (w2 + w3), read back from LDS.
+//
+// Loads go through raw buffer descriptors, one per row, whose range is exactly the K elements of
+// that row (empty for rows past M or N): a load past K returns 0 without touching memory, and a
+// +0 product leaves every accumulator's bits unchanged (a chain started at +0 never holds -0).
+// The wide instances load 16 bytes per row and tile and need K, both row strides multiples of 8
+// and 16-byte aligned operands (then no load straddles the end of a row); the narrow instances load
+// 2 bytes per element and take any operands.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr int TILE = 8;                 // k per tile
+constexpr int CHAINS = 256;             // chains per output
+constexpr int WAVES = CHAINS / 64;      // one chain per lane
+constexpr int THREADS = 64 * WAVES;
+constexpr int STEP_BYTES = TILE * CHAINS * 2;   // bytes of a row covered by one step of all chains
+constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range checked
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+GGO_DEV rsrc_t row_rsrc(const uint16_t* row, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row), 0, bytes, BUF_DWORD3);
+}
+
+// Cache policy of the weight loads: nontemporal (each weight byte is read once per call).
+constexpr int AUX_STREAM = 2;
+
+// One tile (8 bf16) of one row, as 4 dwords: dword i holds k0 + 2i (low half) and k0 + 2i + 1.
+template <bool WIDE, int AUX = 0>
+GGO_DEV void load_tile(rsrc_t r, int off, uint32_t (&d)[4]) {
+    if constexpr (WIDE) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+        d[0] = v[0];
+        d[1] = v[1];
+        d[2] = v[2];
+        d[3] = v[3];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * i, 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * i + 2, 0, 0);
+            d[i] = lo | (hi << 16);
+        }
+    }
+}
+
+template <int MT, int R, bool WIDE>
+GGO_DEV void load_step(const rsrc_t (&wr)[R], const rsrc_t (&xr)[MT], int off, uint32_t (&w)[R][4],
+                       uint32_t (&x)[MT][4]) {
+    // x first: a wait for the x tiles (hits in L2) then never waits behind weight rows from HBM
+#pragma unroll
+    for (int m = 0; m < MT; ++m) load_tile<WIDE>(xr[m], off, x[m]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_tile<WIDE, AUX_STREAM>(wr[r], off, w[r]);
+}
+
+GGO_DEV float elem(const uint32_t (&d)[4], int e) { return (e & 1) ? bf16_hi(d[e >> 1]) : bf16_lo(d[e >> 1]); }
+
+// Fold one tile into the accumulators: k ascending inside the tile, one fma per k.
+template <int MT, int R>
+GGO_DEV void fold_tile(float (&acc)[R][MT], const uint32_t (&w)[R][4], const uint32_t (&x)[MT][4]) {
+#pragma unroll
+    for (int e = 0; e < TILE; ++e) {
+        float xf[MT], wf[R];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xf[m] = elem(x[m], e);
+#pragma unroll
+        for (int r = 0; r < R; ++r) wf[r] = elem(w[r], e);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] = __builtin_fmaf(xf[m], wf[r], acc[r][m]);
+    }
+}
+
+template <int CTRL>
+GGO_DEV float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// The value lane (l xor D) holds. DPP for partners inside a row of 16 lanes: quad_perm [1,0,3,2]
+// and [2,3,0,1] for D = 1, 2; for D = 4 the quad mirror followed by the half-row mirror
+// (l -> l^3 -> (l^3)^7 = l^4); row_ror:8 for D = 8. D = 16 and 32 go through ds_bpermute.
+template <int D>
+GGO_DEV float xor_lane(float v) {
+    if constexpr (D == 1) return dpp<0xb1>(v);
+    else if constexpr (D == 2) return dpp<0x4e>(v);
+    else if constexpr (D == 4) return dpp<0x141>(dpp<0x1b>(v));
+    else if constexpr (D == 8) return dpp<0x128>(v);
+    else return __shfl_xor(v, D);
+}
+
+// Count-up tree over the 64 lanes of a wave for each of the C values a lane holds (v[0 .. C)),
+// one level per lane bit D = 1, 2, 4, ..., 32: the partial sums over aligned blocks of D lanes are
+// added in pairs, (block) + (block next to it), exactly the tree of the DPP row_shr 1, 2, 4, 8 and
+// row_bcast 15, 31 reduction. While a lane still holds several values, each level also halves
+// them (a reduce-scatter): the lane with bit D clear keeps the lower half of the indices, its
+// partner the upper half, and each adds the partner's copy of what it keeps. After the C = 2^a
+// values are down to one, the remaining levels add the partner's value. At the end lane l holds
+// the total of value index bitrev_a(l mod C), the same in every lane with the same low a bits.
+template <int C, int D, int N>
+GGO_DEV void wave_tree_scatter(float (&v)[N], int lane) {
+    if constexpr (D < 64) {
+        if constexpr (C > 1) {
+            const bool upper = (lane & D) != 0;
+#pragma unroll
+            for (int i = 0; i < C / 2; ++i) {
+                const float keep = upper ? v[C / 2 + i] : v[i];
+                const float send = upper ? v[i] : v[C / 2 + i];
+                v[i] = keep + xor_lane<D>(send);
+            }
+            wave_tree_scatter<C / 2, 2 * D>(v, lane);
+        } else {
+            v[0] = v[0] + xor_lane<D>(v[0]);
+            wave_tree_scatter<1, 2 * D>(v, lane);
+        }
+    }
+}
+
+template <int C>
+GGO_DEV int scatter_index(int lane) {
+    int idx = 0;
+#pragma unroll
+    for (int b = 1; b < C; b <<= 1) idx = (idx << 1) | ((lane & b) ? 1 : 0);
+    return idx;
+}
+
+template <int MT, int R, bool WIDE>
+__global__ __launch_bounds__(THREADS) void k_gemv_tree(TreeArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = wave * 64 + lane;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * R;
+    const int kbytes = a.K * 2;
+
+    rsrc_t wr[R], xr[MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wr[r] = row_rsrc(a.WT + (n0 + r) * a.ldwt, n0 + r < a.N ? kbytes : 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xr[m] = row_rsrc(a.x + m * a.ldx, m < a.M ? kbytes : 0);
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+    // Two steps in flight: step j + 1 is requested before step j is folded. Steps past K (the
+    // padding to an even count, and the one requested after the last) read as zero.
+    const int steps = (a.K + TILE * CHAINS - 1) / (TILE * CHAINS);
+    int off = p * TILE * 2;
+    uint32_t wA[R][4], xA[MT][4], wB[R][4], xB[MT][4];
+    load_step<MT, R, WIDE>(wr, xr, off, wA, xA);
+    // (The scheduling barriers keep each request ahead of the fold that precedes it in the source;
+    // left alone, the scheduler sinks the loads of step j + 1 below the fold of step j.)
+    for (int j = 0; j < steps; j += 2) {
+        load_step<MT, R, WIDE>(wr, xr, off + STEP_BYTES, wB, xB);
+        __builtin_amdgcn_sched_barrier(0);
+        fold_tile<MT, R>(acc, wA, xA);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step<MT, R, WIDE>(wr, xr, off + 2 * STEP_BYTES, wA, xA);
+        __builtin_amdgcn_sched_barrier(0);
+        fold_tile<MT, R>(acc, wB, xB);
+        __builtin_amdgcn_sched_barrier(0);
+        off += 2 * STEP_BYTES;
+    }
+
+    constexpr int V = R * MT;
+    static_assert(V <= 64 && (V & (V - 1)) == 0, "one wave total per lane at most, a power of two");
+    float v[V];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) v[r * MT + m] = acc[r][m];
+    wave_tree_scatter<V, 1>(v, lane);
+    __shared__ float red[WAVES][V];
+    if (lane < V) red[wave][scatter_index<V>(lane)] = v[0];
+    __syncthreads();
+    for (int i = threadIdx.x; i < R * MT; i += THREADS) {
+        const int r = i / MT, m = i % MT;
+        if (m < a.M && n0 + r < a.N)
+            a.y[m * a.ldy + n0 + r] = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
+    }
+}
+
+template <int MT, bool WIDE>
+hipError_t launch_mt(const TreeArgs& a, hipStream_t stream) {
+    // Rows per workgroup: 4 keeps more workgroups (and loads) in flight; at MT = 8 the x tiles,
+    // reloaded once per R rows, cost more than that, and 8 rows still fit the registers.
+    constexpr int R = MT == 8 ? 8 : 4;
+    const int64_t blocks = (a.N + R - 1) / R;
+    hipLaunchKernelGGL((k_gemv_tree<MT, R, WIDE>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool WIDE>
+hipError_t launch_w(const TreeArgs& a, hipStream_t stream) {
+    if (a.M <= 1) return launch_mt<1, WIDE>(a, stream);
+    if (a.M <= 2) return launch_mt<2, WIDE>(a, stream);
+    if (a.M <= 4) return launch_mt<4, WIDE>(a, stream);
+    if (a.M <= 8) return launch_mt<8, WIDE>(a, stream);
+    return launch_mt<16, WIDE>(a, stream);
+}
+
+}  // namespace
+
+int gemv_tree_max_k() { return (1 << 29) - 3 * TILE * CHAINS; }
+
+hipError_t launch_gemv_tree(const TreeArgs& a, hipStream_t stream) {
+    return a.wide ? launch_w<true>(a, stream) : launch_w<false>(a, stream);
+}

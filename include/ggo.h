@@ -110,6 +110,40 @@ int gemv_ordered(const uint16_t *x, int64_t ldx,
                  int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * gemv_tree -- tree-ordered GEMV for decode shapes, batch invariant, with the
+ * weight supplied transposed (WT [N, K], k contiguous: a linear layer's
+ * weight layout), so that every output streams one contiguous row.
+ * Source: "Taming Bitwise Behavior in GPU Kernels with Tensor Core", section
+ * 3.2.2 (the GEMV paragraph and Figure 2(d)): the lanes deal the k axis among
+ * themselves tile by tile, each taking every countth tile, fold their tiles
+ * as a chain of fused multiply-adds and combine their totals with a
+ * butterfly; section 5.1: the pinned butterfly counts its offsets up from 1,
+ * a balanced tree that adds neighbours first. This library fixes:
+ *   tile t = k in [8t, 8t + 8); chain p (0 <= p < 256) takes tiles p, p + 256,
+ *   p + 512, ... and folds every k of them in ascending order as
+ *   acc = fma(x[m,k], WT[n,k], acc) from acc = +0 (one rounding per step);
+ *   y[m, n] = the balanced pairwise tree over the 256 chain totals, level 1
+ *   adding chains 2i and 2i+1 (binary32 adds, round to nearest even).
+ * The order depends on K alone: y's bits do not change with M, N, the other
+ * rows of x or the launch, and equal the CPU oracle's bit for bit. They are
+ * a different order from gemm_ordered / gemv_ordered, so the two contracts
+ * give different bits.
+ *   x   device, [M, K] bfloat16 bits, row stride ldx >= K
+ *   WT  device, [N, K] bfloat16 bits, row stride ldwt >= K
+ *   y   device, [M, N] binary32, row stride ldy >= N; written, never read
+ *   0 <= M <= GGO_GEMV_MAX_M, else GGO_EUNSUPPORTED (M = 0 or N = 0: no-op;
+ *   K = 0: y = +0). K above 2^29 - 6144 gives GGO_EUNSUPPORTED.
+ * Any alignment and stride is served; 16-byte aligned x and WT with row
+ * strides and K multiples of 8 take 16-byte loads (same bits). No workspace,
+ * no atomics; the call is asynchronous on `stream` (a hipStream_t, NULL for
+ * the default stream) and reads nothing outside the rows it is given.
+ */
+int gemv_tree(const uint16_t *x, int64_t ldx,
+              const uint16_t *WT, int64_t ldwt,
+              float *y, int64_t ldy,
+              int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * gemm_mfma_invariant -- bfloat16 matrix-core product, batch invariant.
  * Source: "Taming Bitwise Behavior in GPU Kernels with Tensor Core", sections
  * 3.2.1 and 3.2.2: a matrix instruction folds a fixed group of instruction_k

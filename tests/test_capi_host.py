@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemm_mfma_invariant",
+    for n in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemm_mfma_invariant",
               "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error"):
         assert n in names, names
 
@@ -61,6 +61,10 @@ def test_bad_arguments_are_rejected_without_touching_the_gpu(g):
     assert lib.gemm_ordered(1, 0, 4, 1, 8, 1, 8, 4, 8, 8, null) == -1     # lda < K
     assert lib.gemm_ordered(null, 0, 8, 1, 8, 1, 8, 4, 8, 8, null) == -1  # null A
     assert lib.gemv_ordered(1, 8, 1, 8, 1, 8, 17, 8, 8, null) == -2
+    assert lib.gemv_tree(1, 8, 1, 8, 1, 8, 17, 8, 8, null) == -2           # M > 16
+    assert lib.gemv_tree(1, 8, 1, 4, 1, 8, 4, 8, 8, null) == -1            # ldwt < K
+    assert lib.gemv_tree(1, 8, 1, 8, 1, 4, 4, 8, 8, null) == -1            # ldy < N
+    assert lib.gemv_tree(1, 1 << 30, 1, 1 << 30, 1, 8, 1, 8, 1 << 30, null) == -2   # K too large
     assert lib.gemm_mfma_invariant(1, 8, 1, 4, 1, 8, 4, 8, 8, null) == -1  # ldw < N
     assert lib.gemm_ordered_grouped(null, 1, 0, null) == -1
     arr = (g.Problem * 1)()
@@ -68,6 +72,8 @@ def test_bad_arguments_are_rejected_without_touching_the_gpu(g):
     # empty problems are valid and launch nothing
     assert lib.gemm_ordered(null, 0, 8, null, 8, null, 8, 0, 8, 8, null) == 0
     assert lib.gemv_ordered(null, 8, null, 8, null, 8, 0, 8, 8, null) == 0
+    assert lib.gemv_tree(null, 8, null, 8, null, 8, 0, 8, 8, null) == 0
+    assert lib.gemv_tree(null, 8, null, 8, null, 8, 3, 0, 8, null) == 0
     assert lib.gemm_mfma_invariant(null, 8, null, 8, null, 8, 5, 0, 8, null) == 0
     assert lib.ggo_last_error() == b""
 

@@ -5,7 +5,11 @@ multiply-add, no fast-math), so the ordered kernels must hold no fused or dot
 instruction and must hold separate binary32 multiplies and adds. The MFMA
 kernel's order is fixed by its opcode ("Taming Bitwise Behavior in GPU Kernels
 with Tensor Core", section 3.2.2: instruction_k), so it must use exactly one
-matrix opcode. No kernel may use atomics (arrival order would move bits).
+matrix opcode. The tree-ordered GEMV folds each chain with one fused multiply-add
+per k (section 3.2.2 of the same page, the scalar path's chain of fused
+multiply-adds), so its floating-point arithmetic must be v_fma_f32 and plain
+v_add_f32 only: no separate multiply, no packed, dot or matrix instruction.
+No kernel may use atomics (arrival order would move bits).
 """
 import os
 import re
@@ -48,7 +52,7 @@ def code():
     if not os.path.isdir(BUILD):
         pytest.skip("library not built")
     return {src: disassemble(os.path.join(BUILD, src + ".o"))
-            for src in ("ordered_gemm.hip", "ordered_gemv.hip", "mfma_invariant.hip", "capi.cpp")}
+            for src in ("ordered_gemm.hip", "ordered_gemv.hip", "tree_gemv.hip", "mfma_invariant.hip", "capi.cpp")}
 
 
 def test_ordered_kernels_have_no_contraction(code):
@@ -60,6 +64,20 @@ def test_ordered_kernels_have_no_contraction(code):
             assert not FUSED.search(text), (k, FUSED.search(text).group(0))
             assert re.search(r"\bv_mul_f32", text) and re.search(r"\bv_add_f32", text), k
             assert not MFMA.search(text), k
+
+
+def test_tree_kernels_use_single_fma_and_add(code):
+    ks = [k for k in code["tree_gemv.hip"] if "k_gemv_tree" in k]
+    assert len(ks) == 10, ks   # M tiers 1, 2, 4, 8, 16, each with 16-byte and 2-byte loads
+    float_op = re.compile(r"\bv_(?:pk_)?[a-z0-9]+_f(?:16|32|64)\w*")
+    for k in ks:
+        text = "\n".join(code["tree_gemv.hip"][k])
+        ops = {m.group(0) for m in float_op.finditer(text)}
+        ops = {o for o in ops if not o.startswith(("v_cvt", "v_cmp"))}
+        assert ops <= {"v_fma_f32", "v_add_f32", "v_add_f32_e32", "v_add_f32_e64", "v_add_f32_dpp",
+                       "v_fmac_f32", "v_fmac_f32_e32", "v_fmac_f32_e64"}, (k, ops)
+        assert re.search(r"\bv_fmac?_f32", text), k
+        assert not MFMA.search(text) and not re.search(r"\bv_dot", text), k
 
 
 def test_mfma_kernels_use_one_opcode(code):
