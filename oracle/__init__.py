@@ -40,6 +40,7 @@ def _bind(lib):
     lib.oracle_gemm_f64.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_gemm_absdot_f64.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_gemv_tree.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
+    lib.oracle_gemm_mfma.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.oracle_freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.oracle_freivalds_check.restype = I
@@ -105,6 +106,29 @@ def gemm_absdot_f64(A: np.ndarray, W: np.ndarray, threads: int = 1) -> np.ndarra
     A, W = _check(A, W)
     out = np.empty((A.shape[0], W.shape[1]), dtype=np.float64)
     return _rows(load().oracle_gemm_absdot_f64, A, W, out, threads)
+
+
+def gemm_mfma(A: np.ndarray, W: np.ndarray, threads: int = 1, lib=None) -> np.ndarray:
+    """Bit model of the matrix-core product (A [M, K], W [K, N] bf16 bits) -> float32 [M, N]."""
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    assert A.ndim == 2 and W.ndim == 2 and A.shape[1] == W.shape[0], (A.shape, W.shape)
+    M, K = A.shape
+    N = W.shape[1]
+    out = np.empty((M, N), dtype=np.float32)
+    fn = (lib or load()).oracle_gemm_mfma
+
+    def run(r0, r1):
+        if r1 > r0 and N > 0:
+            fn(_ptr(A[r0:]), K, _ptr(W), N, _ptr(out[r0:]), N, r1 - r0, N, K)
+
+    if threads <= 1 or M < 2:
+        run(0, M)
+    else:
+        step = (M + threads - 1) // threads
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda r0: run(r0, min(M, r0 + step)), range(0, M, step)))
+    return out
 
 
 def gemv_tree(x: np.ndarray, WT: np.ndarray, threads: int = 1, lib=None) -> np.ndarray:

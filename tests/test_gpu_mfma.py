@@ -153,3 +153,61 @@ def test_transposed_w_entry_rejects_misaligned(g):
     WT2 = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")[:, :12]
     with pytest.raises(g.GGOError, match="multiple of 8"):
         g.gemm_mfma_invariant_wt(A2, WT2)
+
+
+# ---- bit for bit against the CPU bit model of the matrix instruction (oracle.gemm_mfma) ----
+
+def _wt(dW):
+    return dW.t().contiguous()
+
+
+def test_gpt2_bits_equal_cpu_model(g):
+    A, W = synth.gpt2_projection(0, 512)
+    say("mfma gpt2 512x768x768 vs bit model")
+    ref = oracle.gemm_mfma(A, W, threads=16).view(np.uint32)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    for name, C in (("256x128", g.gemm_mfma_invariant(dA, dW)), ("128x128", g.test_gemm_mfma_tile128(dA, dW)),
+                    ("W^T", g.gemm_mfma_invariant_wt(dA, _wt(dW)))):
+        got = host_bits(C)
+        assert np.array_equal(got, ref), f"{name}: {np.count_nonzero(got != ref)} outputs differ from the model"
+    for M in (1, 7, 64, 257):
+        assert np.array_equal(host_bits(g.gemm_mfma_invariant(dA[:M], dW)), ref[:M]), M
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 333, 129), (130, 70, 33), (1, 1000, 4095), (256, 129, 31),
+                                   (300, 200, 1000), (513, 1000, 1112), (5, 64, 8)])
+def test_ragged_bits_equal_cpu_model(g, M, N, K):
+    A = synth.normal_bf16(M + N + K, "mfma.bits.A", (M, K))
+    W = synth.normal_bf16(M + N + K, "mfma.bits.W", (K, N), 0.02)
+    say(f"mfma ragged {M}x{N}x{K} vs bit model")
+    ref = oracle.gemm_mfma(A, W, threads=16).view(np.uint32)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    assert np.array_equal(host_bits(g.gemm_mfma_invariant(dA, dW)), ref)
+    assert np.array_equal(host_bits(g.test_gemm_mfma_tile128(dA, dW)), ref)
+    if K % 8 == 0:
+        assert np.array_equal(host_bits(g.gemm_mfma_invariant_wt(dA, _wt(dW))), ref)
+
+
+def test_wide_exponent_range_bits_equal_cpu_model(g):
+    # operands over 2^-60 .. 2^60 and subnormal products: the alignment, truncation and subnormal steps
+    rng = np.random.default_rng(9)
+    A = synth.f32_to_bf16_bits((rng.standard_normal((64, 256)) * 2.0 ** rng.integers(-60, 60, (64, 256))).astype(np.float32))
+    W = synth.f32_to_bf16_bits((rng.standard_normal((256, 96)) * 2.0 ** rng.integers(-60, 20, (256, 96))).astype(np.float32))
+    ref = oracle.gemm_mfma(A, W, threads=16).view(np.uint32)
+    assert np.array_equal(host_bits(g.gemm_mfma_invariant(dev_bf16(A), dev_bf16(W))), ref)
+
+
+@pytest.mark.parametrize("name,M,n", [("mlp_up", 2048, 4096), ("7b", 4096, 4096), ("7b", 4096, 11008)])
+def test_full_size_sampled_rows_equal_cpu_model(g, name, M, n):
+    if name == "mlp_up":
+        A, W = synth.mlp_up(0, M)
+    else:
+        A, W = synth.proj_7b(0, n=n, m=M)
+    rows = np.array([0, 1, M // 2, M - 1])
+    say(f"mfma {name} {M}x{n} sampled rows vs bit model")
+    ref = oracle.gemm_mfma(A[rows], W, threads=16).view(np.uint32)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    got = host_bits(g.gemm_mfma_invariant(dA, dW))[rows]
+    assert np.array_equal(got, ref)
+    got_wt = host_bits(g.gemm_mfma_invariant_wt(dA, _wt(dW)))[rows]
+    assert np.array_equal(got_wt, ref)
