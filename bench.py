@@ -20,6 +20,7 @@ Beside it, in the same JSON line:
   certificate   Freivalds checks of sampled rows (honest pass, planted fault caught)
   paths         the other paths at their workloads: ordered GEMM and MFMA GEMM
                 TFLOP/s (MLP up-projection, 7B projections), the value product,
+                the fused epilogue against the same steps as separate kernels,
                 and torch.matmul (hipBLASLt, not batch invariant) on the same shapes
 """
 from __future__ import annotations
@@ -174,6 +175,36 @@ def paths(g, reps):
         rec["mfma_vs_hipblaslt"] = round(tb / t, 3)
         out[f"{name}_M{M}_N{N}_K{K}"] = rec
         del A, W, C
+    # fused epilogue (bias, activation, residual, bf16 output) against the same steps as separate kernels
+    F = torch.nn.functional
+    N = K = 4096
+    WTs = [randn_bf16((N, K), 0.02) for _ in range(16)]
+    x8 = randn_bf16((8, K), 1.0)
+    bias = torch.randn(N, device="cuda")
+    res = torch.randn(8, N, device="cuda")
+    for M in (1, 8):
+        x, r = x8[:M], res[:M]
+        fused = graph_time(lambda i: g.gemv_tree_ep(x, WTs[i % 16], bias=bias, act="silu", residual=r, out="bf16"), 64)
+        split = graph_time(lambda i: (F.silu(g.gemv_tree(x, WTs[i % 16]) + bias) + r).to(torch.bfloat16), 64)
+        blas = graph_time(lambda i: (F.silu(torch.mm(x, WTs[i % 16].t(), out_dtype=torch.float32) + bias) + r)
+                          .to(torch.bfloat16), 64)
+        out[f"epilogue_decode_M{M}_silu_bias_residual_bf16"] = {
+            "fused_us": round(1e3 * fused, 2), "tree_then_torch_epilogue_us": round(1e3 * split, 2),
+            "hipblaslt_then_torch_epilogue_us": round(1e3 * blas, 2)}
+    del WTs
+    A = randn_bf16((4096, 4096), 1.0)
+    W = randn_bf16((4096, 4096), 0.02)
+    b2 = torch.randn(4096, device="cuda")
+    r2 = torch.randn(4096, 4096, device="cuda")
+    gelu = lambda y: F.gelu(y, approximate="tanh")
+    fused = graph_time(lambda i: g.gemm_mfma_invariant_ep(A, W, bias=b2, act="gelu_tanh", residual=r2, out="bf16"), 8)
+    split = graph_time(lambda i: (gelu(g.gemm_mfma_invariant(A, W) + b2) + r2).to(torch.bfloat16), 8)
+    plain = graph_time(lambda i: g.gemm_mfma_invariant(A, W), 8)
+    blas = graph_time(lambda i: (gelu(mm_blaslt(A, W) + b2) + r2).to(torch.bfloat16), 8)
+    out["epilogue_prefill_4096cube_gelu_bias_residual_bf16"] = {
+        "fused_us": round(1e3 * fused, 1), "mfma_then_torch_epilogue_us": round(1e3 * split, 1),
+        "mfma_alone_us": round(1e3 * plain, 1), "hipblaslt_then_torch_epilogue_us": round(1e3 * blas, 1)}
+    del A, W, r2
     # attention value product, 32 heads, head_dim 128
     for L in (256, 1024):
         P = torch.softmax(torch.randn((32, L, L), device="cuda"), dim=-1)

@@ -29,6 +29,15 @@ class GGOError(RuntimeError):
     pass
 
 
+class Epilogue(ct.Structure):
+    """Mirror of ``ggo_epilogue``."""
+    _fields_ = [("bias", ct.c_void_p), ("residual", ct.c_void_p), ("ldr", ct.c_int64),
+                ("act", ct.c_int), ("out_dtype", ct.c_int)]
+
+
+ACTS = {"none": 0, "relu": 1, "silu": 2, "gelu_tanh": 3}
+
+
 class Problem(ct.Structure):
     """Mirror of ``ggo_problem``."""
     _fields_ = [("A", ct.c_void_p), ("W", ct.c_void_p), ("C", ct.c_void_p),
@@ -47,6 +56,8 @@ def _load():
     lib.gemm_ordered_grouped.argtypes = [ct.POINTER(Problem), I64, I, P]
     lib.gemv_ordered.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemv_tree.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemv_tree_ep.argtypes = [P, I64, P, I64, ct.POINTER(Epilogue), P, I64, I64, I64, I64, P]
+    lib.gemm_mfma_invariant_ep.argtypes = [P, I64, P, I64, ct.POINTER(Epilogue), P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.ggo_test_gemm_mfma_tile128.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant_wt.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
@@ -54,7 +65,8 @@ def _load():
     lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.ggo_build_info.restype = ct.c_char_p
     lib.ggo_last_error.restype = ct.c_char_p
-    for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemm_mfma_invariant",
+    for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
+              "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
               "ggo_test_gemm_mfma_tile128", "gemm_mfma_invariant_wt", "freivalds_prepare", "freivalds_check"):
         getattr(lib, f).restype = I
     return lib
@@ -62,7 +74,8 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemm_mfma_invariant",
+EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
+           "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
            "gemm_mfma_invariant_wt",
            "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error")
 
@@ -187,6 +200,64 @@ def gemv_tree(x, WT, y=None, stream=None):
     _raise(lib.gemv_tree(x.data_ptr(), ldx, WT.data_ptr(), ldwt, y.data_ptr(), ldy, M, N, K, _stream(stream)),
            "gemv_tree")
     return y
+
+
+def _epilogue(M, N, like, bias, act, residual, out, y):
+    """Build the ggo_epilogue and the output tensor (float32, or bfloat16 for out='bf16')."""
+    torch = _torch()
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {sorted(ACTS)}")
+    if out not in ("f32", "bf16"):
+        raise ValueError("out must be 'f32' or 'bf16'")
+    keep = []
+    e = Epilogue(None, None, 0, ACTS[act], GGO_BF16 if out == "bf16" else GGO_F32)
+    if bias is not None:
+        if bias.dtype != torch.float32 or tuple(bias.shape) != (N,) or not bias.is_cuda or (N > 1 and bias.stride(0) != 1):
+            raise ValueError(f"bias must be a contiguous float32 device tensor [{N}]")
+        e.bias = bias.data_ptr()
+        keep.append(bias)
+    if residual is not None:
+        if residual.dtype != torch.float32 or tuple(residual.shape) != (M, N):
+            raise ValueError(f"residual must be float32 [{M}, {N}]")
+        e.residual = residual.data_ptr()
+        e.ldr = _rowmajor(residual, "residual") if M and N else N
+        keep.append(residual)
+    want = torch.bfloat16 if out == "bf16" else torch.float32
+    if y is None:
+        y = torch.empty((M, N), dtype=want, device=like.device)
+    elif y.dtype != want or tuple(y.shape) != (M, N):
+        raise ValueError(f"output must be {want} [{M}, {N}]")
+    return e, y, keep
+
+
+def gemv_tree_ep(x, WT, bias=None, act="none", residual=None, out="f32", y=None, stream=None):
+    """gemv_tree followed, in the same kernel, by y = act(y + bias) + residual (fixed order), stored as
+    float32 or bfloat16 (out='bf16')."""
+    ldx, ldwt = _rowmajor(x, "x"), _rowmajor(WT, "WT")
+    M, K = x.shape
+    if not (_is_bf16(x) and _is_bf16(WT)) or WT.shape[1] != K:
+        raise ValueError("x and WT must be bf16, WT [N, K]")
+    N = WT.shape[0]
+    e, y, keep = _epilogue(M, N, x, bias, act, residual, out, y)
+    ldy = _rowmajor(y, "y") if M and N else N
+    _raise(lib.gemv_tree_ep(x.data_ptr(), ldx, WT.data_ptr(), ldwt, ct.byref(e), y.data_ptr(), ldy, M, N, K,
+                            _stream(stream)), "gemv_tree_ep")
+    return y
+
+
+def gemm_mfma_invariant_ep(A, W, bias=None, act="none", residual=None, out="f32", C=None, stream=None):
+    """gemm_mfma_invariant followed, in the same kernel, by C = act(C + bias) + residual (fixed order),
+    stored as float32 or bfloat16 (out='bf16')."""
+    lda, ldw = _rowmajor(A, "A"), _rowmajor(W, "W")
+    M, K = A.shape
+    if not (_is_bf16(A) and _is_bf16(W)) or W.shape[0] != K:
+        raise ValueError("A and W must be bf16, W [K, N]")
+    N = W.shape[1]
+    e, C, keep = _epilogue(M, N, A, bias, act, residual, out, C)
+    ldc = _rowmajor(C, "C") if M and N else N
+    _raise(lib.gemm_mfma_invariant_ep(A.data_ptr(), lda, W.data_ptr(), ldw, ct.byref(e), C.data_ptr(), ldc, M, N, K,
+                                      _stream(stream)), "gemm_mfma_invariant_ep")
+    return C
 
 
 def _mfma(fn, A, W, C, stream):

@@ -62,6 +62,41 @@ hipError_t fill_zero(float* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s)
     return hipGetLastError();
 }
 
+// The value of an empty fold (+0) passed through a fused epilogue.
+__global__ void k_epi_zero(void* C, int64_t ldc, int M, int N, Epi ep) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(M) * N;
+    if (i < total) {
+        const int64_t m = i / N, n = i - m * N;
+        epi_store(ep, C, ldc, m, n, 0.0f);
+    }
+}
+
+hipError_t epi_zero(void* C, int64_t ldc, int64_t M, int64_t N, const Epi& ep, hipStream_t s) {
+    if (epi_identity(ep)) return fill_zero(static_cast<float*>(C), ldc, M, N, s);
+    const int64_t blocks = (M * N + 255) / 256;
+    hipLaunchKernelGGL(k_epi_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, C, ldc, static_cast<int>(M),
+                       static_cast<int>(N), ep);
+    return hipGetLastError();
+}
+
+Epi no_epi() { return Epi{nullptr, nullptr, 0, GGO_ACT_NONE, 0}; }
+
+// Check a caller's epilogue (NULL means none) and turn it into the kernels' form.
+int make_epi(const char* fn, const ggo_epilogue* e, int64_t N, Epi* out) {
+    *out = no_epi();
+    if (!e) return GGO_OK;
+    if (e->act < GGO_ACT_NONE || e->act > GGO_ACT_GELU_TANH) return fail(GGO_EINVAL, "%s: unknown activation %d", fn, e->act);
+    if (e->out_dtype != GGO_F32 && e->out_dtype != GGO_BF16) return fail(GGO_EINVAL, "%s: out_dtype must be GGO_F32 or GGO_BF16", fn);
+    if (e->residual && e->ldr < N) return fail(GGO_EINVAL, "%s: residual row stride below N", fn);
+    out->bias = e->bias;
+    out->res = e->residual;
+    out->ldr = e->residual ? e->ldr : 0;
+    out->act = e->act;
+    out->out_bf16 = e->out_dtype == GGO_BF16;
+    return GGO_OK;
+}
+
 int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, OrdProblem& p, int64_t& tiles) {
     int rc = check_mnk(fn, q.M, q.N, q.K);
     if (rc) return rc;
@@ -144,14 +179,14 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
 // Every other call takes the 128x128 instance. Both give every output the
 // same bits (the same operand values in the same groups), so the choice,
 // which never looks at M, moves no bit.
-int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
-             int64_t M, int64_t N, int64_t K, hipStream_t s, bool force_t128) {
+int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, void* C, int64_t ldc,
+             int64_t M, int64_t N, int64_t K, hipStream_t s, bool force_t128, const Epi& ep) {
     int rc = check_mnk(fn, M, N, K);
     if (rc) return rc;
     if (M == 0 || N == 0) return ok();
     if (!C || (K && (!A || !W))) return fail(GGO_EINVAL, "%s: null pointer", fn);
     if (lda < K || ldw < N || ldc < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
-    if (K == 0) return launched(fn, fill_zero(C, ldc, M, N, s));
+    if (K == 0) return launched(fn, epi_zero(C, ldc, M, N, ep, s));
     const bool wide = !force_t128 && aligned(A, 16) && lda % 8 == 0 && aligned(W, 16) && ldw % 8 == 0 &&
                       lda < (int64_t(1) << 22) && ldw < (int64_t(1) << 22) && K % 8 == 0 && N % 8 == 0;
     int bm, bn;
@@ -177,6 +212,10 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
     if (aligned(A, 16) && lda % 8 == 0) a.vec |= VEC_A;
     if (aligned(W, 8) && ldw % 4 == 0) a.vec |= VEC_W;
     if (aligned(C, 16) && ldc % 4 == 0) a.vec |= VEC_C;
+    a.ep = ep;
+    if ((!ep.bias || aligned(ep.bias, 16)) && (!ep.res || (aligned(ep.res, 16) && ep.ldr % 4 == 0)) &&
+        aligned(C, ep.out_bf16 ? 8 : 16) && ldc % 4 == 0)
+        a.vec |= VEC_EP;
     return launched(fn, wide ? launch_gemm_mfma_invariant(a, s) : launch_gemm_mfma_t128(a, s));
 }
 
@@ -237,17 +276,15 @@ int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
     return launched(fn, launch_gemv_ordered(a, s));
 }
 
-int gemv_tree(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy, int64_t M,
-              int64_t N, int64_t K, void* stream) {
-    const char* fn = "gemv_tree";
-    hipStream_t s = static_cast<hipStream_t>(stream);
+static int run_tree(const char* fn, const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, void* y, int64_t ldy,
+                    int64_t M, int64_t N, int64_t K, hipStream_t s, const Epi& ep) {
     int rc = check_mnk(fn, M, N, K);
     if (rc) return rc;
     if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d", fn, (long long)M, GGO_GEMV_MAX_M);
     if (M == 0 || N == 0) return ok();
     if (!y || (K && (!x || !WT))) return fail(GGO_EINVAL, "%s: null pointer", fn);
     if (ldx < K || ldwt < K || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
-    if (K == 0) return launched(fn, fill_zero(y, ldy, M, N, s));
+    if (K == 0) return launched(fn, epi_zero(y, ldy, M, N, ep, s));
     if (K > gemv_tree_max_k())
         return fail(GGO_EUNSUPPORTED, "%s: K=%lld too large for 32-bit byte offsets along a row", fn, (long long)K);
     TreeArgs a;
@@ -262,12 +299,34 @@ int gemv_tree(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, 
     a.K = (int32_t)K;
     // 16-byte tile loads when no tile can straddle the end of a row (same arithmetic and bits either way)
     a.wide = aligned(x, 16) && ldx % 8 == 0 && aligned(WT, 16) && ldwt % 8 == 0 && K % 8 == 0;
+    a.ep = ep;
     return launched(fn, launch_gemv_tree(a, s));
+}
+
+int gemv_tree(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy, int64_t M,
+              int64_t N, int64_t K, void* stream) {
+    return run_tree("gemv_tree", x, ldx, WT, ldwt, y, ldy, M, N, K, static_cast<hipStream_t>(stream), no_epi());
+}
+
+int gemv_tree_ep(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, const ggo_epilogue* ep, void* y,
+                 int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+    Epi e;
+    int rc = make_epi("gemv_tree_ep", ep, N, &e);
+    if (rc) return rc;
+    return run_tree("gemv_tree_ep", x, ldx, WT, ldwt, y, ldy, M, N, K, static_cast<hipStream_t>(stream), e);
+}
+
+int gemm_mfma_invariant_ep(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const ggo_epilogue* ep,
+                           void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+    Epi e;
+    int rc = make_epi("gemm_mfma_invariant_ep", ep, N, &e);
+    if (rc) return rc;
+    return run_mfma("gemm_mfma_invariant_ep", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), false, e);
 }
 
 int gemm_mfma_invariant(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void* stream) {
-    return run_mfma("gemm_mfma_invariant", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), false);
+    return run_mfma("gemm_mfma_invariant", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), false, no_epi());
 }
 
 int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, int64_t ldwt, float* C, int64_t ldc,
@@ -304,12 +363,13 @@ int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, i
     a.tiles_n = (int32_t)tn;
     a.vec = VEC_A | VEC_W;
     if (aligned(C, 16) && ldc % 4 == 0) a.vec |= VEC_C;
+    a.ep = no_epi();
     return launched(fn, launch_gemm_mfma_invariant_wt(a, s));
 }
 
 int ggo_test_gemm_mfma_tile128(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                                int64_t M, int64_t N, int64_t K, void* stream) {
-    return run_mfma("ggo_test_gemm_mfma_tile128", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), true);
+    return run_mfma("ggo_test_gemm_mfma_tile128", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), true, no_epi());
 }
 
 const char* ggo_build_info(void) { return GGO_BUILD_INFO; }

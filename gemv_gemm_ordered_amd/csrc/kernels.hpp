@@ -4,8 +4,9 @@
 #include <stdint.h>
 
 #include "../../include/ggo.h"
+#include "epilogue.hpp"
 
-enum : uint32_t { VEC_A = 1u, VEC_W = 2u, VEC_C = 4u };
+enum : uint32_t { VEC_A = 1u, VEC_W = 2u, VEC_C = 4u, VEC_EP = 8u };   // VEC_EP: 4-wide epilogue loads/stores
 
 // One ordered problem as the kernel sees it (passed by value in the kernel arguments).
 struct OrdProblem {
@@ -42,10 +43,11 @@ int gemv_ordered_max_ldw();   // buffer offsets of the GEMV kernel are 32-bit
 struct TreeArgs {
     const uint16_t* x;
     const uint16_t* WT;
-    float* y;
+    void* y;          // binary32, or bfloat16 when ep.out_bf16
     int64_t ldx, ldwt, ldy;
     int32_t M, N, K;
     int32_t wide;     // 16-byte loads allowed (alignment, strides and K multiples of 8)
+    Epi ep;
 };
 hipError_t launch_gemv_tree(const TreeArgs& a, hipStream_t stream);
 int gemv_tree_max_k();   // byte offsets along a row are 32-bit
@@ -53,11 +55,12 @@ int gemv_tree_max_k();   // byte offsets along a row are 32-bit
 struct MfmaArgs {
     const uint16_t* A;
     const uint16_t* W;
-    float* C;
+    void* C;          // binary32, or bfloat16 when ep.out_bf16
     int64_t lda, ldw, ldc;
     int32_t M, N, K;
     int32_t tiles_m, tiles_n;
     uint32_t vec;
+    Epi ep;
 };
 void mfma_tile_shape(int* bm, int* bn);        // 256x128 instance (16-byte aligned operands)
 void mfma_tile_shape_t128(int* bm, int* bn);   // 128x128 instance (any operands)

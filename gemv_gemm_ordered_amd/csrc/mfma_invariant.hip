@@ -158,7 +158,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_mfma_t128(const MfmaArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-                if (row < p.M && col < p.N) p.C[static_cast<int64_t>(row) * p.ldc + col] = acc[i][j][r];
+                if (row < p.M && col < p.N) epi_store(p.ep, p.C, p.ldc, row, col, acc[i][j][r]);
             }
         }
 }
@@ -408,11 +408,48 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the trailing empty-range loads have landed before the workgroup ends
 
     // lane holds C[row][col .. col+3] of each block: row = lane % 16, col = 4 * (lane / 16)
+    if (!epi_identity(p.ep)) {
+        // Fused epilogue. Each wave stages half of its 128 x (BN/2) results at a time in LDS (the operand
+        // ring is free now), then walks them row-major in a plain loop: coalesced bias / residual loads
+        // and stores, and the epilogue's code appears once instead of once per accumulator.
+        constexpr int RS = BN / 2 + 4;   // floats per staged row; +4 spreads 16 rows over the banks
+        static_assert(2 * 64 * RS * 4 <= G::STAGE * 2, "two wave regions per stage buffer");
+        __syncthreads();                 // every wave has finished reading the last stage
+        float* region = reinterpret_cast<float*>(c.wave < 2 ? buf[0] : buf[1]) + (c.wave & 1) * 64 * RS;
+        const int lane = c.t & 63;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int ii = 0; ii < G::WI / 2; ++ii)
+#pragma unroll
+                for (int j = 0; j < G::WJ; ++j)
+                    *reinterpret_cast<float4*>(region + (ii * 16 + c.lr) * RS + j * 16 + 4 * c.lg) =
+                        make_float4(acc[half * (G::WI / 2) + ii][j][0], acc[half * (G::WI / 2) + ii][j][1],
+                                    acc[half * (G::WI / 2) + ii][j][2], acc[half * (G::WI / 2) + ii][j][3]);
+            __syncthreads();
+#pragma unroll 1
+            for (int e = lane; e < 64 * (BN / 8); e += 64) {
+                const int rl = e / (BN / 8), c4 = e % (BN / 8);
+                const int row = c.m0 + c.wm * 128 + half * 64 + rl;
+                const int col = c.n0 + c.wn * (BN / 2) + 4 * c4;
+                if (row >= p.M || col >= p.N) continue;
+                const float4 y = *reinterpret_cast<const float4*>(region + rl * RS + 4 * c4);
+                if (col + 4 <= p.N && (p.vec & VEC_EP)) {
+                    epi_store4(p.ep, p.C, p.ldc, row, col, y.x, y.y, y.z, y.w);
+                } else {
+                    const float yv[4] = {y.x, y.y, y.z, y.w};
+                    for (int r = 0; r < 4 && col + r < p.N; ++r) epi_store(p.ep, p.C, p.ldc, row, col + r, yv[r]);
+                }
+            }
+            __syncthreads();             // before the next half overwrites the region
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < G::WI; ++i) {
         const int row = c.m0 + c.wm * 128 + i * 16 + c.lr;
         if (row >= p.M) continue;
-        float* crow = p.C + static_cast<int64_t>(row) * p.ldc;
+        float* crow = static_cast<float*>(p.C) + static_cast<int64_t>(row) * p.ldc;
 #pragma unroll
         for (int j = 0; j < G::WJ; ++j) {
             const int col = c.n0 + c.wn * (BN / 2) + j * 16 + 4 * c.lg;

@@ -28,7 +28,8 @@
 // +0 product leaves every accumulator's bits unchanged (a chain started at +0 never holds -0).
 // The wide instances load 16 bytes per row and tile and need K, both row strides multiples of 8
 // and 16-byte aligned operands (then no load straddles the end of a row); the narrow instances load
-// 2 bytes per element and take any operands.
+// 2 bytes per element and take any operands. The result of each output goes through the fused
+// epilogue (epilogue.hpp) on its way out.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -152,7 +153,7 @@ GGO_DEV int scatter_index(int lane) {
     return idx;
 }
 
-template <int MT, int R, bool WIDE>
+template <int MT, int R, bool WIDE, bool EPI>
 __global__ __launch_bounds__(THREADS) void k_gemv_tree(TreeArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p = wave * 64 + lane;
@@ -204,8 +205,11 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree(TreeArgs a) {
     __syncthreads();
     for (int i = threadIdx.x; i < R * MT; i += THREADS) {
         const int r = i / MT, m = i % MT;
-        if (m < a.M && n0 + r < a.N)
-            a.y[m * a.ldy + n0 + r] = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
+        if (m < a.M && n0 + r < a.N) {
+            const float v = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
+            if constexpr (EPI) epi_store(a.ep, a.y, a.ldy, m, n0 + r, v);
+            else static_cast<float*>(a.y)[m * a.ldy + n0 + r] = v;
+        }
     }
 }
 
@@ -215,7 +219,10 @@ hipError_t launch_mt(const TreeArgs& a, hipStream_t stream) {
     // reloaded once per R rows, cost more than that, and 8 rows still fit the registers.
     constexpr int R = MT == 8 ? 8 : 4;
     const int64_t blocks = (a.N + R - 1) / R;
-    hipLaunchKernelGGL((k_gemv_tree<MT, R, WIDE>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+    if (epi_identity(a.ep))
+        hipLaunchKernelGGL((k_gemv_tree<MT, R, WIDE, false>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemv_tree<MT, R, WIDE, true>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

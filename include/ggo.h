@@ -144,6 +144,61 @@ int gemv_tree(const uint16_t *x, int64_t ldx,
               int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * Fused epilogue, for the callers that follow a matmul with a bias, an
+ * activation and a residual add ("Taming Bitwise Behavior in GPU Kernels
+ * with Tensor Core", sections 1 and 7.3: a GEMM fused with the operation
+ * that follows it, still bit-exact, wins by saving a launch). Each result
+ * y[m, n] of the fold, in this fixed order, every step skipped when absent:
+ *     v = y + bias[n];  v = act(v);  v = v + residual[m, n];
+ *     store v as binary32, or as bfloat16 rounded to nearest even.
+ * The pages name no activation; this library defines each as a fixed
+ * sequence of binary32 operations (round to nearest even, division correctly
+ * rounded, fma only where written), so CPU and GPU give the same bits:
+ *   exp(x): n = rint(x*RN(log2 e)); r = fma(-n, ln2_hi, x);
+ *           r = fma(-n, RN(ln2 - ln2_hi), r) with ln2_hi = 0x3f317200;
+ *           p = the degree-7 Taylor polynomial of e^r (coefficients RN(1/i!)),
+ *           Horner with fma; exp = (p * 2^floor(n/2)) * 2^(n - floor(n/2));
+ *           x > 88.75 gives +inf, x < -104 gives +0.
+ *   GGO_ACT_RELU:      v > 0 ? v : +0
+ *   GGO_ACT_SILU:      v / (1 + exp(-v))
+ *   GGO_ACT_GELU_TANH: u = RN(sqrt(2/pi)) * (v + RN(0.044715) * ((v*v)*v));
+ *                      0.5 * (v * (1 + (1 - 2 / (exp(2*u) + 1))))
+ */
+#define GGO_ACT_NONE      0
+#define GGO_ACT_RELU      1
+#define GGO_ACT_SILU      2
+#define GGO_ACT_GELU_TANH 3
+
+typedef struct ggo_epilogue {
+    const float *bias;      /* device, [N] binary32, or NULL */
+    const float *residual;  /* device, [M, N] binary32, row stride ldr >= N, or NULL */
+    int64_t ldr;
+    int act;                /* GGO_ACT_*, else GGO_EINVAL */
+    int out_dtype;          /* GGO_F32 or GGO_BF16: the element type of the output, else GGO_EINVAL */
+} ggo_epilogue;
+
+/*
+ * gemv_tree_ep -- gemv_tree with the fused epilogue `ep` (host struct, read
+ * during the call; NULL = none, the same as gemv_tree). y is binary32 or
+ * bfloat16 as ep->out_dtype says, row stride ldy >= N. The fold's bits are
+ * gemv_tree's; the epilogue adds its own fixed steps.
+ */
+int gemv_tree_ep(const uint16_t *x, int64_t ldx,
+                 const uint16_t *WT, int64_t ldwt,
+                 const ggo_epilogue *ep, void *y, int64_t ldy,
+                 int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * gemm_mfma_invariant_ep -- gemm_mfma_invariant with the fused epilogue `ep`
+ * (NULL = none). C is binary32 or bfloat16 as ep->out_dtype says. The fold's
+ * bits are gemm_mfma_invariant's, whatever the tile instance.
+ */
+int gemm_mfma_invariant_ep(const uint16_t *A, int64_t lda,
+                           const uint16_t *W, int64_t ldw,
+                           const ggo_epilogue *ep, void *C, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * gemm_mfma_invariant -- bfloat16 matrix-core product, batch invariant.
  * Source: "Taming Bitwise Behavior in GPU Kernels with Tensor Core", sections
  * 3.2.1 and 3.2.2: a matrix instruction folds a fixed group of instruction_k

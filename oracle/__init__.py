@@ -41,6 +41,9 @@ def _bind(lib):
     lib.oracle_gemm_absdot_f64.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_gemv_tree.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
     lib.oracle_gemm_mfma.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
+    lib.oracle_epilogue.argtypes = [P, I64, I64, I64, P, I, P, I64, I, P, I64]
+    lib.oracle_ep_exp.argtypes = [ct.c_float]
+    lib.oracle_ep_exp.restype = ct.c_float
     lib.oracle_freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.oracle_freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.oracle_freivalds_check.restype = I
@@ -106,6 +109,27 @@ def gemm_absdot_f64(A: np.ndarray, W: np.ndarray, threads: int = 1) -> np.ndarra
     A, W = _check(A, W)
     out = np.empty((A.shape[0], W.shape[1]), dtype=np.float64)
     return _rows(load().oracle_gemm_absdot_f64, A, W, out, threads)
+
+
+ACTS = {"none": 0, "relu": 1, "silu": 2, "gelu_tanh": 3}
+
+
+def epilogue(Y: np.ndarray, bias=None, act: str = "none", residual=None, out: str = "f32", lib=None) -> np.ndarray:
+    """The fused epilogue applied to a binary32 result Y [M, N]: float32 [M, N], or bf16 bits (uint16)."""
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    M, N = Y.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    r = None if residual is None else np.ascontiguousarray(residual, dtype=np.float32)
+    assert b is None or b.shape == (N,)
+    assert r is None or r.shape == (M, N)
+    o = np.empty((M, N), dtype=np.uint16 if out == "bf16" else np.float32)
+    (lib or load()).oracle_epilogue(_ptr(Y), N, M, N, None if b is None else _ptr(b), ACTS[act],
+                                    None if r is None else _ptr(r), N, 1 if out == "bf16" else 0, _ptr(o), N)
+    return o
+
+
+def ep_exp(x: float, lib=None) -> float:
+    return float((lib or load()).oracle_ep_exp(float(x)))
 
 
 def gemm_mfma(A: np.ndarray, W: np.ndarray, threads: int = 1, lib=None) -> np.ndarray:

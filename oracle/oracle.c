@@ -47,6 +47,13 @@
  *    pairs and ties); each step is pinned by a hand-derived value in
  *    tests/test_oracle_mfma.py.
  *
+ *  - oracle_epilogue: the fused epilogue (bias, activation, residual, bf16
+ *    output) in its fixed order, "Taming Bitwise Behavior in GPU Kernels with
+ *    Tensor Core", sections 1 and 7.3 (a GEMM fused with the operation that
+ *    follows it, kept bit-exact). The pages name no activation; each one is
+ *    this library's definition as a fixed sequence of binary32 operations,
+ *    written out below step by step.
+ *
  *  - oracle_freivalds_*: the float Freivalds certificate of "Same Bits on the
  *    CPU and the GPU" (section "The CPU as a checker: a float Freivalds
  *    certificate"): a +-1 vector r, the product of r with W precomputed once
@@ -429,6 +436,115 @@ void oracle_gemm_mfma(const uint16_t *A, int64_t lda,
             memcpy(&C[m * ldc + n], &acc, sizeof acc);
         }
 }
+
+/*
+ * Epilogue. For each y[m, n] (binary32, row stride ldy):
+ *     v = y;  if bias: v = v + bias[n];  v = act(v);  if residual: v = v + residual[m, n];
+ * then out[m, n] = v (binary32) or its bfloat16, rounded to nearest even (NaN -> 0x7fc0).
+ * act: 0 none, 1 relu (v > 0 ? v : +0), 2 silu (v / (1 + exp(-v))), 3 gelu, tanh form
+ * (u = RN(sqrt(2/pi)) * (v + RN(0.044715) * ((v*v)*v)); 0.5 * (v * (1 + (1 - 2 / (exp(2u) + 1))))).
+ * exp: n = rint(x * RN(log2 e)); r = fma(-n, ln2_hi, x); r = fma(-n, ln2_lo, r), the two-constant
+ * reduction of Cody and Waite (1980) with ln2_hi = 0.693145751953125 and ln2_lo = RN(ln 2 - ln2_hi);
+ * p = sum_{i=0..7} r^i / i! (the Taylor polynomial, coefficients RN(1/i!)), evaluated by Horner's rule
+ * with fma; result (p * 2^a) * 2^b, a = floor(n/2), b = n - a. x > 88.75 gives +inf, x < -104 +0.
+ * Every operation is binary32, round to nearest even (fmaf rounds once; nearbyintf rounds to the
+ * nearest integer, ties to even, in the default rounding mode).
+ */
+static float pow2f_exact(int k)     /* 2^k for -126 <= k <= 127 */
+{
+    uint32_t u = (uint32_t)(k + 127) << 23;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float ep_exp(float x)
+{
+    if (x != x)
+        return x;
+    if (x > 88.75f)
+        return INFINITY;
+    if (x < -104.0f)
+        return 0.0f;
+    const float log2e = 1.44269502162933349609375f;            /* RN(1/ln 2) */
+    const float ln2_hi = 0.693145751953125f;                   /* 0x3f317200 */
+    const float ln2_lo = 1.428606765330187045037746429443359375e-6f;  /* RN(ln 2 - ln2_hi) */
+    const float t = x * log2e;
+    const float n = nearbyintf(t);
+    float r = fmaf(-n, ln2_hi, x);
+    r = fmaf(-n, ln2_lo, r);
+    /* 1/7!, 1/6!, ..., 1/2!, 1, 1, each rounded to binary32 */
+    const float c7 = 1.0f / 5040.0f, c6 = 1.0f / 720.0f, c5 = 1.0f / 120.0f, c4 = 1.0f / 24.0f, c3 = 1.0f / 6.0f;
+    float p = c7;
+    p = fmaf(p, r, c6);
+    p = fmaf(p, r, c5);
+    p = fmaf(p, r, c4);
+    p = fmaf(p, r, c3);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    const int ni = (int)n;
+    const int a = (ni >= 0) ? ni / 2 : -((-ni + 1) / 2);       /* floor(n / 2) */
+    const int b = ni - a;
+    const float s1 = p * pow2f_exact(a);
+    return s1 * pow2f_exact(b);
+}
+
+static float ep_act(float v, int act)
+{
+    if (act == 1)
+        return v > 0.0f ? v : 0.0f;
+    if (act == 2) {
+        const float e = ep_exp(-v);
+        const float d = 1.0f + e;
+        return v / d;
+    }
+    if (act == 3) {
+        const float c1 = 0.79788458347320556640625f;           /* RN(sqrt(2/pi)) */
+        const float c2 = 0.0447149984538555145263671875f;      /* RN(0.044715) */
+        float c = v * v;
+        c = c * v;
+        c = c2 * c;
+        c = v + c;
+        const float u = c1 * c;
+        const float e = ep_exp(2.0f * u);
+        const float th = 1.0f - 2.0f / (e + 1.0f);
+        const float h = 1.0f + th;
+        return 0.5f * (v * h);
+    }
+    return v;
+}
+
+static uint16_t to_bf16_rne(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return 0x7fc0;
+    const uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7fffu + lsb) >> 16);
+}
+
+void oracle_epilogue(const float *Y, int64_t ldy, int64_t M, int64_t N,
+                     const float *bias, int act, const float *residual, int64_t ldr,
+                     int out_bf16, void *out, int64_t ldo)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float v = Y[m * ldy + n];
+            if (bias)
+                v = v + bias[n];
+            v = ep_act(v, act);
+            if (residual)
+                v = v + residual[m * ldr + n];
+            if (out_bf16)
+                ((uint16_t *)out)[m * ldo + n] = to_bf16_rne(v);
+            else
+                ((float *)out)[m * ldo + n] = v;
+        }
+}
+
+float oracle_ep_exp(float x) { return ep_exp(x); }
 
 /*
  * Freivalds precompute, once per matrix. With y = x W (y over the output

@@ -67,10 +67,19 @@ def test_ordered_kernels_have_no_contraction(code):
 
 
 def test_tree_kernels_use_single_fma_and_add(code):
+    """The instances without an epilogue (template flag EPI = false, mangled ...Lb0EEEv8TreeArgs) hold
+    the fold and the tree alone: their binary32 arithmetic is v_fma_f32 / v_fmac_f32 and v_add_f32 only.
+    The epilogue instances add the epilogue's own operations after the fold; they are checked for no
+    packed, dot or matrix instruction."""
     ks = [k for k in code["tree_gemv.hip"] if "k_gemv_tree" in k]
-    assert len(ks) == 10, ks   # M tiers 1, 2, 4, 8, 16, each with 16-byte and 2-byte loads
-    float_op = re.compile(r"\bv_(?:pk_)?[a-z0-9]+_f(?:16|32|64)\w*")
+    assert len(ks) == 20, ks   # M tiers 1, 2, 4, 8, 16 x 16-byte / 2-byte loads x with / without epilogue
+    plain = [k for k in ks if k.endswith("Lb0EEEv8TreeArgs")]
+    assert len(plain) == 10, plain
     for k in ks:
+        text = "\n".join(code["tree_gemv.hip"][k])
+        assert not MFMA.search(text) and not re.search(r"\bv_dot|\bv_pk_(?:fma|mul|add)_f32", text), k
+    float_op = re.compile(r"\bv_(?:pk_)?[a-z0-9]+_f(?:16|32|64)\w*")
+    for k in plain:
         text = "\n".join(code["tree_gemv.hip"][k])
         ops = {m.group(0) for m in float_op.finditer(text)}
         ops = {o for o in ops if not o.startswith(("v_cvt", "v_cmp"))}
