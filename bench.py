@@ -205,6 +205,7 @@ def paths(g, reps):
         "fused_us": round(1e3 * fused, 1), "mfma_then_torch_epilogue_us": round(1e3 * split, 1),
         "mfma_alone_us": round(1e3 * plain, 1), "hipblaslt_then_torch_epilogue_us": round(1e3 * blas, 1)}
     del A, W, r2
+    out["certificate_decode_loop_7b_layer"] = cert_loop(g)
     # attention value product, 32 heads, head_dim 128
     for L in (256, 1024):
         P = torch.softmax(torch.randn((32, L, L), device="cuda"), dim=-1)
@@ -215,6 +216,54 @@ def paths(g, reps):
         out[f"pv_L{L}_h32"] = {"ordered_tflops": round(flop / t / 1e9, 2), "ms": round(t, 4)}
         del P, V, O
     return out
+
+
+def cert_loop(g, tokens=48):
+    """Decode loop over the seven projections of a 7B layer (q, k, v, o 4096x4096; gate, up 4096->11008;
+    down 11008->4096), one row per token through gemv_tree, without and with the certificate engine
+    (every output row copied asynchronously and checked on host threads against t sign vectors)."""
+    import numpy as np
+    import torch
+    shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]   # (N, K) of W^T
+    WTs = [(torch.randn(n, k, device="cuda") * 0.02).to(torch.bfloat16) for n, k in shapes]
+    xs = [[torch.randn(1, k, device="cuda").to(torch.bfloat16) for _ in range(4)] for _, k in shapes]
+    res = {"matrices": len(shapes), "tokens": tokens, "rows_per_token": len(shapes)}
+
+    def run(eng, mids):
+        keep = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for tok in range(tokens):
+            rows = []
+            for i in range(len(shapes)):
+                x = xs[i][tok % 4]
+                y = g.gemv_tree(x, WTs[i])
+                rows.append((x[0], y[0]))
+            if eng is not None:            # one gather launch per token for all seven rows
+                eng.submit_rows(mids, [r[0] for r in rows], [r[1] for r in rows], token=tok)
+                keep.append(rows)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        st = eng.drain() if eng is not None else None
+        t2 = time.perf_counter()
+        return (t1 - t0) / tokens, t2 - t1, st
+
+    run(None, None)
+    base, _, _ = run(None, None)
+    res["no_certificate_us_per_token"] = round(1e6 * base, 1)
+    Wh = [w.view(torch.int16).cpu().numpy().view(np.uint16) for w in WTs]
+    for t in (1, 4):
+        eng = g.CertEngine(11008, 11008, slots=64, workers=4)
+        rng = np.random.default_rng(t)
+        mids = [eng.add_matrix(w, rng.choice(np.int8([-1, 1]), size=(t, w.shape[0])), transposed=True) for w in Wh]
+        per_tok, drain, st = run(eng, mids)
+        res[f"t{t}"] = {"us_per_token": round(1e6 * per_tok, 1), "drain_after_gpu_ms": round(1e3 * drain, 2),
+                        "rows_checked": st["checked"], "failed": st["failed"],
+                        "max_honest_ratio": round(st["max_honest_ratio"], 5),
+                        "host_check_us_per_row": round(1e6 * st["check_seconds"] / max(1, st["checked"]), 1),
+                        "escape_probability_of_a_cancelling_fault": 2.0 ** -t}
+        eng.close()
+    return res
 
 
 # ---------------------------------------------------------------------------

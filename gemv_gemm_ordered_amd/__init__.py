@@ -38,6 +38,12 @@ class Epilogue(ct.Structure):
 ACTS = {"none": 0, "relu": 1, "silu": 2, "gelu_tanh": 3}
 
 
+class CertStats(ct.Structure):
+    """Mirror of ``ggo_cert_stats``."""
+    _fields_ = [("submitted", ct.c_int64), ("checked", ct.c_int64), ("failed", ct.c_int64),
+                ("max_honest_ratio", ct.c_double), ("check_seconds", ct.c_double), ("copy_error", ct.c_int)]
+
+
 class Problem(ct.Structure):
     """Mirror of ``ggo_problem``."""
     _fields_ = [("A", ct.c_void_p), ("W", ct.c_void_p), ("C", ct.c_void_p),
@@ -50,6 +56,9 @@ class Problem(ct.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc for gfx950) first")
+    # torch first: its HIP runtime is then the one libggo.so binds to, so device memory, streams and
+    # launches all live in one runtime (loading the library first brings in a second one)
+    import torch  # noqa: F401
     lib = ct.CDLL(LIB_PATH)
     P, I64, I = ct.c_void_p, ct.c_int64, ct.c_int
     lib.gemm_ordered.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64, P]
@@ -63,6 +72,21 @@ def _load():
     lib.gemm_mfma_invariant_wt.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
+    PP = ct.POINTER(ct.c_void_p)
+    lib.ggo_cert_create.argtypes = [I64, I64, I64, I, ct.c_double, PP]
+    lib.ggo_cert_create_host.argtypes = [I64, I64, I64, I, ct.c_double, PP]
+    lib.ggo_cert_add_matrix.argtypes = [P, P, I64, I, I64, I64, P, I64, ct.POINTER(I)]
+    lib.ggo_cert_submit.argtypes = [P, I, P, P, I64, P]
+    lib.ggo_cert_submit_host.argtypes = [P, I, P, P, I64]
+    lib.ggo_cert_submit_rows.argtypes = [P, I64, P, P, P, I64, P]
+    lib.ggo_cert_drain.argtypes = [P, ct.POINTER(CertStats)]
+    lib.ggo_cert_failures.argtypes = [P, P, P, I64]
+    lib.ggo_cert_failures.restype = I64
+    lib.ggo_cert_destroy.argtypes = [P]
+    lib.ggo_cert_destroy.restype = None
+    for f in ("ggo_cert_create", "ggo_cert_create_host", "ggo_cert_add_matrix", "ggo_cert_submit",
+              "ggo_cert_submit_rows", "ggo_cert_submit_host", "ggo_cert_drain"):
+        getattr(lib, f).restype = I
     lib.ggo_build_info.restype = ct.c_char_p
     lib.ggo_last_error.restype = ct.c_char_p
     for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
@@ -77,7 +101,10 @@ lib = _load()
 EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
            "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
            "gemm_mfma_invariant_wt",
-           "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error")
+           "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error",
+           "ggo_cert_create", "ggo_cert_create_host", "ggo_cert_add_matrix", "ggo_cert_submit", "ggo_cert_submit_rows",
+           "ggo_cert_submit_host",
+           "ggo_cert_drain", "ggo_cert_failures", "ggo_cert_destroy")
 
 
 def build_info() -> str:
@@ -328,3 +355,82 @@ def freivalds_check(prep, r, x, y, c_f: float = 0.125):
                              x.ctypes.data, y.ctypes.data, float(c_f), out.ctypes.data)
     _raise(rc, "freivalds_check")
     return bool(rc), float(out[0]), float(out[1]), float(out[2]), float(out[3])
+
+
+class CertEngine:
+    """The certificate engine of ``ggo_cert_*``: register matrices (host bf16 weights and t sign vectors
+    each), submit sampled output rows from the device (asynchronous copies on the engine's own stream)
+    or from the host, drain, and read the failures."""
+
+    def __init__(self, max_K, max_N, slots=64, workers=2, c_f=0.125, host_only=False):
+        h = ct.c_void_p()
+        create = lib.ggo_cert_create_host if host_only else lib.ggo_cert_create
+        rc = create(max_K, max_N, slots, workers, float(c_f), ct.byref(h))
+        if rc < 0:
+            raise GGOError(f"ggo_cert_create failed ({rc})")
+        self.h = h
+        self.K = {}
+        self.N = {}
+
+    def add_matrix(self, W, r, transposed=False):
+        """W: host bf16 bits, [K, N] (or [N, K] with transposed=True); r: [t, N] signs (+1/-1)."""
+        W = _np(W, np.uint16)
+        W = np.ascontiguousarray(W)
+        r = np.ascontiguousarray(np.atleast_2d(r), dtype=np.int8)
+        N, K = (W.shape if transposed else W.shape[::-1])
+        if r.shape[1] != N:
+            raise ValueError(f"r must have {N} columns")
+        mid = ct.c_int()
+        _raise(lib.ggo_cert_add_matrix(self.h, W.ctypes.data, W.shape[1], int(transposed), K, N, r.ctypes.data,
+                                       r.shape[0], ct.byref(mid)), "ggo_cert_add_matrix")
+        self.K[mid.value], self.N[mid.value] = K, N
+        return mid.value
+
+    def submit(self, mid, x_row, y_row, token, stream=None):
+        """x_row: device bf16 [K], y_row: device float32 [N] (contiguous)."""
+        if x_row.numel() != self.K[mid] or y_row.numel() != self.N[mid] or not x_row.is_contiguous() \
+                or not y_row.is_contiguous():
+            raise ValueError("x_row / y_row must be contiguous rows of the matrix's K / N")
+        _raise(lib.ggo_cert_submit(self.h, mid, x_row.data_ptr(), y_row.data_ptr(), int(token), _stream(stream)),
+               "ggo_cert_submit")
+
+    def submit_rows(self, mids, x_rows, y_rows, token, stream=None):
+        """Several rows (<= 16) of one token in one call: one gather launch on the engine's stream."""
+        n = len(mids)
+        for mid, x, y in zip(mids, x_rows, y_rows):
+            if x.numel() != self.K[mid] or y.numel() != self.N[mid] or not x.is_contiguous() or not y.is_contiguous():
+                raise ValueError("x / y must be contiguous rows of the matrix's K / N")
+        ids = (ct.c_int * n)(*mids)
+        xs = (ct.c_void_p * n)(*[x.data_ptr() for x in x_rows])
+        ys = (ct.c_void_p * n)(*[y.data_ptr() for y in y_rows])
+        _raise(lib.ggo_cert_submit_rows(self.h, n, ids, xs, ys, int(token), _stream(stream)), "ggo_cert_submit_rows")
+
+    def submit_host(self, mid, x_row, y_row, token):
+        x = np.ascontiguousarray(_np(x_row, np.uint16)).reshape(-1)
+        y = np.ascontiguousarray(_np(y_row, np.float32)).reshape(-1)
+        if x.size != self.K[mid] or y.size != self.N[mid]:
+            raise ValueError("row sizes do not match the matrix")
+        _raise(lib.ggo_cert_submit_host(self.h, mid, x.ctypes.data, y.ctypes.data, int(token)), "ggo_cert_submit_host")
+
+    def drain(self):
+        st = CertStats()
+        _raise(lib.ggo_cert_drain(self.h, ct.byref(st)), "ggo_cert_drain")
+        return {f: getattr(st, f) for f, _ in CertStats._fields_}
+
+    def failures(self, cap=1 << 16):
+        toks = np.empty(cap, dtype=np.int64)
+        mats = np.empty(cap, dtype=np.int32)
+        n = lib.ggo_cert_failures(self.h, toks.ctypes.data, mats.ctypes.data, cap)
+        n = min(n, cap)
+        return list(zip(toks[:n].tolist(), mats[:n].tolist()))
+
+    def close(self):
+        if self.h:
+            lib.ggo_cert_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,389 @@
+// Certificate engine for a decode loop ("Same Bits on the CPU and the GPU", section "The CPU as a
+// checker: a float Freivalds certificate", and the costs it lists as unpaid: hooking the check into
+// the engine through asynchronous copies on the launch path, and checking more than one sign vector
+// or matrix per token, because a fault whose contributions cancel under one r escapes with
+// probability 1/2).
+//
+// Per registered matrix the engine holds t independent sign vectors r_1..r_t over the output index
+// and, in binary64, s_i = W r_i, q_k = ||W[k,:]||_2 and a_k = sum_n |w_kn| (freivalds_prepare's
+// quantities). A submit copies one sampled row x (K bf16) and its output row y (N binary32) from the
+// device into a pinned host slot, on the engine's own stream after an event recorded on the caller's
+// stream, so the caller's next kernels do not wait for the copy. Worker threads wait for each slot's
+// copy, run freivalds_check once per sign vector (the check fails if any vector rejects) and return
+// the slot. When every slot is in use, submit waits for a worker (back pressure), so the ring bounds
+// both host memory and how far the checks may trail the GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <condition_variable>
+#include <cstring>
+#include <deque>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "../../include/ggo.h"
+
+namespace {
+
+struct Matrix {
+    int64_t K = 0, N = 0;
+    int nr = 0;
+    std::vector<int8_t> r;     // nr x N
+    std::vector<double> s;     // nr x K
+    std::vector<double> q, a;  // K
+};
+
+struct Slot {
+    uint16_t* x = nullptr;     // pinned, max_K
+    float* y = nullptr;        // pinned, max_N
+    uint16_t* x_dev = nullptr; // the same memory as the GPU addresses it
+    float* y_dev = nullptr;
+    hipEvent_t done = nullptr; // the copies into this slot have landed
+    int matrix = -1;
+    int64_t token = 0;
+    bool device = true;        // false: filled from host memory by ggo_cert_submit_host
+};
+
+}  // namespace
+
+struct ggo_cert {
+    int64_t max_K = 0, max_N = 0;
+    double c_f = 0.125;
+    bool host_only = false;            // slots in ordinary memory; only ggo_cert_submit_host
+    std::mutex submit_mu;              // one submit at a time uses ready_evt
+    hipStream_t copy_stream = nullptr;
+    hipEvent_t ready_evt = nullptr;    // recorded on the caller's stream, waited on by copy_stream
+    std::vector<Matrix> mats;
+    std::vector<Slot> slots;
+    std::mutex mu;
+    std::condition_variable cv_work, cv_free, cv_idle;
+    std::deque<int> free_slots, queued;
+    int64_t in_flight = 0;             // submitted and not yet checked
+    bool stop = false;
+    std::vector<std::thread> workers;
+    // statistics (under mu)
+    int64_t submitted = 0, checked = 0, failed = 0;
+    double max_ratio = 0.0, check_seconds = 0.0;
+    std::vector<std::pair<int64_t, int>> failures;   // (token, matrix), oldest first
+    int copy_error = 0;
+};
+
+namespace {
+
+void worker_loop(ggo_cert* c) {
+    std::vector<double> out(4);
+    for (;;) {
+        int id;
+        {
+            std::unique_lock<std::mutex> lk(c->mu);
+            c->cv_work.wait(lk, [&] { return c->stop || !c->queued.empty(); });
+            if (c->queued.empty()) return;   // stop requested and nothing left
+            id = c->queued.front();
+            c->queued.pop_front();
+        }
+        Slot& sl = c->slots[id];
+        bool copy_ok = true;
+        if (sl.device) copy_ok = hipEventSynchronize(sl.done) == hipSuccess;
+        const Matrix& m = c->mats[sl.matrix];
+        bool pass = true;
+        double worst = 0.0;
+        const auto t0 = std::chrono::steady_clock::now();
+        if (copy_ok) {
+            for (int v = 0; v < m.nr; ++v) {
+                const int rc = freivalds_check(m.s.data() + v * m.K, m.q.data(), m.a.data(), m.r.data() + v * m.N,
+                                               m.K, m.N, sl.x, sl.y, c->c_f, out.data());
+                if (rc < 0) copy_ok = false;
+                if (rc != 1) pass = false;
+                if (out[1] > 0.0) worst = std::max(worst, out[0] / out[1]);
+            }
+        }
+        const double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+        {
+            std::lock_guard<std::mutex> lk(c->mu);
+            c->checked += 1;
+            c->check_seconds += dt;
+            if (!copy_ok) c->copy_error = 1;
+            if (!pass || !copy_ok) {
+                c->failed += 1;
+                c->failures.emplace_back(sl.token, sl.matrix);
+            } else if (worst > c->max_ratio) {
+                c->max_ratio = worst;
+            }
+            c->free_slots.push_back(id);
+            c->in_flight -= 1;
+        }
+        c->cv_free.notify_one();
+        c->cv_idle.notify_all();
+    }
+}
+
+// Take a free slot, waiting for a worker to return one if the ring is full.
+int take_slot(ggo_cert* c) {
+    std::unique_lock<std::mutex> lk(c->mu);
+    c->cv_free.wait(lk, [&] { return !c->free_slots.empty(); });
+    const int id = c->free_slots.front();
+    c->free_slots.pop_front();
+    c->in_flight += 1;
+    c->submitted += 1;
+    return id;
+}
+
+void enqueue(ggo_cert* c, int id) {
+    {
+        std::lock_guard<std::mutex> lk(c->mu);
+        c->queued.push_back(id);
+    }
+    c->cv_work.notify_one();
+}
+
+// One launch copies every row of a batch into its pinned slot (host memory the GPU writes through its
+// mapping), instead of two runtime copies per row: 2 x rows segments, one per blockIdx.y.
+constexpr int MAX_BATCH = 16;
+struct GatherSeg {
+    const uint16_t* src;
+    uint16_t* dst;
+    int64_t count;   // 16-bit elements
+};
+struct GatherArgs {
+    GatherSeg seg[2 * MAX_BATCH];
+};
+
+__global__ void k_cert_gather(GatherArgs a) {
+    const GatherSeg s = a.seg[blockIdx.y];
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < s.count;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        s.dst[i] = s.src[i];
+}
+
+inline double widen(uint16_t b) {
+    const uint32_t u = static_cast<uint32_t>(b) << 16;
+    float f;
+    std::memcpy(&f, &u, sizeof f);
+    return static_cast<double>(f);
+}
+
+}  // namespace
+
+extern "C" {
+
+static int create(int64_t max_K, int64_t max_N, int64_t nslots, int nworkers, double c_f, bool host_only,
+                  ggo_cert** out) {
+    if (!out || max_K < 1 || max_N < 1 || nslots < 1 || nslots > 4096 || nworkers < 1 || nworkers > 64 || !(c_f > 0.0))
+        return GGO_EINVAL;
+    *out = nullptr;
+    ggo_cert* c = new ggo_cert;
+    c->max_K = max_K;
+    c->max_N = max_N;
+    c->c_f = c_f;
+    c->host_only = host_only;
+    c->slots.resize(static_cast<size_t>(nslots));
+    int rc = GGO_OK;
+    for (int64_t i = 0; i < nslots && rc == GGO_OK; ++i) {
+        Slot& s = c->slots[i];
+        if (host_only) {
+            s.x = new uint16_t[static_cast<size_t>(max_K)];
+            s.y = new float[static_cast<size_t>(max_N)];
+        } else if (hipHostMalloc(reinterpret_cast<void**>(&s.x), static_cast<size_t>(max_K) * 2) != hipSuccess ||
+                   hipHostMalloc(reinterpret_cast<void**>(&s.y), static_cast<size_t>(max_N) * 4) != hipSuccess ||
+                   hipHostGetDevicePointer(reinterpret_cast<void**>(&s.x_dev), s.x, 0) != hipSuccess ||
+                   hipHostGetDevicePointer(reinterpret_cast<void**>(&s.y_dev), s.y, 0) != hipSuccess ||
+                   hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess) {
+            rc = GGO_ELAUNCH;
+        }
+        c->free_slots.push_back(static_cast<int>(i));
+    }
+    if (rc == GGO_OK && !host_only &&
+        (hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess ||
+         hipEventCreateWithFlags(&c->ready_evt, hipEventDisableTiming) != hipSuccess))
+        rc = GGO_ELAUNCH;
+    if (rc != GGO_OK) {
+        ggo_cert_destroy(c);
+        return rc;
+    }
+    for (int i = 0; i < nworkers; ++i) c->workers.emplace_back(worker_loop, c);
+    *out = c;
+    return GGO_OK;
+}
+
+int ggo_cert_create(int64_t max_K, int64_t max_N, int64_t nslots, int nworkers, double c_f, ggo_cert** out) {
+    return create(max_K, max_N, nslots, nworkers, c_f, false, out);
+}
+
+int ggo_cert_create_host(int64_t max_K, int64_t max_N, int64_t nslots, int nworkers, double c_f, ggo_cert** out) {
+    return create(max_K, max_N, nslots, nworkers, c_f, true, out);
+}
+
+int ggo_cert_add_matrix(ggo_cert* c, const uint16_t* W, int64_t ld, int transposed, int64_t K, int64_t N,
+                        const int8_t* r, int64_t nr, int* id) {
+    if (!c || !W || !r || !id || K < 1 || N < 1 || nr < 1 || nr > 64 || K > c->max_K || N > c->max_N) return GGO_EINVAL;
+    if (ld < (transposed ? K : N)) return GGO_EINVAL;
+    for (int64_t i = 0; i < nr * N; ++i)
+        if (r[i] != 1 && r[i] != -1) return GGO_EINVAL;
+    Matrix m;
+    m.K = K;
+    m.N = N;
+    m.nr = static_cast<int>(nr);
+    m.r.assign(r, r + nr * N);
+    m.s.assign(static_cast<size_t>(nr * K), 0.0);
+    m.q.assign(static_cast<size_t>(K), 0.0);
+    m.a.assign(static_cast<size_t>(K), 0.0);
+    // s_v[k] = sum_n w[k,n] r_v[n], q[k] = ||w[k,:]||_2, a[k] = sum_n |w[k,n]|, each summed over n in
+    // ascending order in binary64 (the order freivalds_prepare uses)
+    for (int64_t k = 0; k < K; ++k) {
+        double qk = 0.0, ak = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double w = widen(transposed ? W[n * ld + k] : W[k * ld + n]);
+            qk += w * w;
+            ak += std::fabs(w);
+            for (int64_t v = 0; v < nr; ++v) m.s[v * K + k] += r[v * N + n] > 0 ? w : -w;
+        }
+        m.q[k] = std::sqrt(qk);
+        m.a[k] = ak;
+    }
+    std::lock_guard<std::mutex> lk(c->mu);
+    c->mats.push_back(std::move(m));
+    *id = static_cast<int>(c->mats.size()) - 1;
+    return GGO_OK;
+}
+
+int ggo_cert_submit(ggo_cert* c, int id, const uint16_t* x_dev, const float* y_dev, int64_t token, void* stream) {
+    if (!c || c->host_only || !x_dev || !y_dev || id < 0 || id >= static_cast<int>(c->mats.size())) return GGO_EINVAL;
+    const Matrix& m = c->mats[id];
+    std::lock_guard<std::mutex> one_submit(c->submit_mu);
+    const int sid = take_slot(c);
+    Slot& s = c->slots[sid];
+    s.matrix = id;
+    s.token = token;
+    s.device = true;
+    hipStream_t caller = static_cast<hipStream_t>(stream);
+    hipError_t e = hipEventRecord(c->ready_evt, caller);
+    if (e == hipSuccess) e = hipStreamWaitEvent(c->copy_stream, c->ready_evt, 0);
+    if (e == hipSuccess) e = hipMemcpyAsync(s.x, x_dev, static_cast<size_t>(m.K) * 2, hipMemcpyDeviceToHost, c->copy_stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(s.y, y_dev, static_cast<size_t>(m.N) * 4, hipMemcpyDeviceToHost, c->copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(s.done, c->copy_stream);
+    if (e != hipSuccess) {
+        std::lock_guard<std::mutex> lk(c->mu);
+        c->free_slots.push_back(sid);
+        c->in_flight -= 1;
+        c->submitted -= 1;
+        c->copy_error = 1;
+        return GGO_ELAUNCH;
+    }
+    enqueue(c, sid);
+    return GGO_OK;
+}
+
+int ggo_cert_submit_rows(ggo_cert* c, int64_t n, const int* ids, const uint16_t* const* x_dev,
+                         const float* const* y_dev, int64_t token, void* stream) {
+    if (!c || c->host_only || n < 1 || n > MAX_BATCH || !ids || !x_dev || !y_dev) return GGO_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= static_cast<int>(c->mats.size()) || !x_dev[i] || !y_dev[i]) return GGO_EINVAL;
+    std::lock_guard<std::mutex> one_submit(c->submit_mu);
+    int sid[MAX_BATCH];
+    GatherArgs ga;
+    int64_t longest = 1;
+    for (int64_t i = 0; i < n; ++i) {
+        const Matrix& m = c->mats[ids[i]];
+        sid[i] = take_slot(c);
+        Slot& s = c->slots[sid[i]];
+        s.matrix = ids[i];
+        s.token = token;
+        s.device = true;
+        ga.seg[2 * i] = GatherSeg{x_dev[i], s.x_dev, m.K};
+        ga.seg[2 * i + 1] = GatherSeg{reinterpret_cast<const uint16_t*>(y_dev[i]), reinterpret_cast<uint16_t*>(s.y_dev),
+                                      2 * m.N};
+        longest = std::max(longest, 2 * m.N);
+        longest = std::max(longest, m.K);
+    }
+    hipStream_t caller = static_cast<hipStream_t>(stream);
+    hipError_t e = hipEventRecord(c->ready_evt, caller);
+    if (e == hipSuccess) e = hipStreamWaitEvent(c->copy_stream, c->ready_evt, 0);
+    if (e == hipSuccess) {
+        const unsigned bx = static_cast<unsigned>(std::min<int64_t>((longest + 255) / 256, 64));
+        hipLaunchKernelGGL(k_cert_gather, dim3(bx, static_cast<unsigned>(2 * n)), dim3(256), 0, c->copy_stream, ga);
+        e = hipGetLastError();
+    }
+    for (int64_t i = 0; i < n && e == hipSuccess; ++i) e = hipEventRecord(c->slots[sid[i]].done, c->copy_stream);
+    if (e != hipSuccess) {
+        std::lock_guard<std::mutex> lk(c->mu);
+        for (int64_t i = 0; i < n; ++i) {
+            c->free_slots.push_back(sid[i]);
+            c->in_flight -= 1;
+            c->submitted -= 1;
+        }
+        c->copy_error = 1;
+        return GGO_ELAUNCH;
+    }
+    for (int64_t i = 0; i < n; ++i) enqueue(c, sid[i]);
+    return GGO_OK;
+}
+
+int ggo_cert_submit_host(ggo_cert* c, int id, const uint16_t* x, const float* y, int64_t token) {
+    if (!c || !x || !y || id < 0 || id >= static_cast<int>(c->mats.size())) return GGO_EINVAL;
+    const Matrix& m = c->mats[id];
+    const int sid = take_slot(c);
+    Slot& s = c->slots[sid];
+    s.matrix = id;
+    s.token = token;
+    s.device = false;
+    std::memcpy(s.x, x, static_cast<size_t>(m.K) * 2);
+    std::memcpy(s.y, y, static_cast<size_t>(m.N) * 4);
+    enqueue(c, sid);
+    return GGO_OK;
+}
+
+int ggo_cert_drain(ggo_cert* c, ggo_cert_stats* out) {
+    if (!c) return GGO_EINVAL;
+    std::unique_lock<std::mutex> lk(c->mu);
+    c->cv_idle.wait(lk, [&] { return c->in_flight == 0; });
+    if (out) {
+        out->submitted = c->submitted;
+        out->checked = c->checked;
+        out->failed = c->failed;
+        out->max_honest_ratio = c->max_ratio;
+        out->check_seconds = c->check_seconds;
+        out->copy_error = c->copy_error;
+    }
+    return GGO_OK;
+}
+
+int64_t ggo_cert_failures(ggo_cert* c, int64_t* tokens, int* matrices, int64_t cap) {
+    if (!c || cap < 0 || (cap && (!tokens || !matrices))) return GGO_EINVAL;
+    std::lock_guard<std::mutex> lk(c->mu);
+    const int64_t n = std::min<int64_t>(cap, static_cast<int64_t>(c->failures.size()));
+    for (int64_t i = 0; i < n; ++i) {
+        tokens[i] = c->failures[i].first;
+        matrices[i] = c->failures[i].second;
+    }
+    return static_cast<int64_t>(c->failures.size());
+}
+
+void ggo_cert_destroy(ggo_cert* c) {
+    if (!c) return;
+    {
+        std::lock_guard<std::mutex> lk(c->mu);
+        c->stop = true;
+    }
+    c->cv_work.notify_all();
+    for (auto& t : c->workers) t.join();
+    if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
+    for (auto& s : c->slots) {
+        if (c->host_only) {
+            delete[] s.x;
+            delete[] s.y;
+            continue;
+        }
+        if (s.x) hipHostFree(s.x);
+        if (s.y) hipHostFree(s.y);
+        if (s.done) hipEventDestroy(s.done);
+    }
+    if (c->ready_evt) hipEventDestroy(c->ready_evt);
+    if (c->copy_stream) hipStreamDestroy(c->copy_stream);
+    delete c;
+}
+
+}  // extern "C"

@@ -303,6 +303,65 @@ const char *ggo_build_info(void);
 /* Message of the calling thread's last failing call ("" when none). */
 const char *ggo_last_error(void);
 
+/*
+ * Certificate engine for a decode loop ("Same Bits on the CPU and the GPU",
+ * section "The CPU as a checker: a float Freivalds certificate": the check
+ * hooked into the launch path through asynchronous copies, and several
+ * sign vectors per matrix, since a fault whose contributions cancel under one
+ * r escapes with probability 1/2 -- with t independent vectors, 2^-t).
+ *
+ * ggo_cert_create: max_K / max_N bound the registered matrices; `slots`
+ *   pinned host slots (each max_K bf16 + max_N binary32) form the ring of
+ *   rows in flight; `workers` host threads run the checks; c_f is the gate
+ *   constant of freivalds_check. Owns one non-blocking HIP stream (default
+ *   priority) for its copies. GGO_EINVAL for bad sizes, GGO_ELAUNCH when the
+ *   HIP runtime refuses an allocation.
+ * ggo_cert_create_host: the same engine without the GPU (ordinary memory;
+ *   only ggo_cert_submit_host), for outputs already on the host.
+ * ggo_cert_add_matrix: host W, bf16, [K, N] with row stride ld, or its
+ *   transpose [N, K] when `transposed` (a linear layer's weight, as gemv_tree
+ *   takes it); r: nr x N signs (each +1 or -1, nr <= 64). Precomputes
+ *   s_v = W r_v, q and a in binary64 (freivalds_prepare's definitions) and
+ *   returns the matrix id.
+ * ggo_cert_submit: queue the check of one output row: x_dev (device, K bf16)
+ *   and y_dev (device, N binary32) are copied to a slot on the engine's stream
+ *   after all work already queued on `stream`; the caller's stream does not
+ *   wait for the copy. The buffers must stay unchanged until that work and
+ *   the copy have run. Blocks only while every slot is in use. One submit at
+ *   a time (calls are serialised inside).
+ * ggo_cert_submit_rows: ggo_cert_submit for n <= 16 rows at once (ids[i],
+ *   x_dev[i], y_dev[i]): one kernel on the engine's stream writes all of them
+ *   into their pinned slots, so a token's rows cost one launch instead of two
+ *   runtime copies each.
+ * ggo_cert_submit_host: the same from host buffers (copied before return).
+ * ggo_cert_drain: wait until every submitted check has run; fill `out`.
+ *   A row fails when any of its matrix's sign vectors rejects it (or its copy
+ *   failed: copy_error).
+ * ggo_cert_failures: copy up to `cap` (token, matrix) pairs of failed rows,
+ *   oldest first; returns how many failures there are in all.
+ * ggo_cert_destroy: stop the workers (after the queued checks) and free all.
+ */
+typedef struct ggo_cert ggo_cert;
+
+typedef struct ggo_cert_stats {
+    int64_t submitted, checked, failed;
+    double max_honest_ratio;   /* largest rho / sigma over the rows that passed */
+    double check_seconds;      /* host time spent in the checks */
+    int copy_error;
+} ggo_cert_stats;
+
+int ggo_cert_create(int64_t max_K, int64_t max_N, int64_t slots, int workers, double c_f, ggo_cert **out);
+int ggo_cert_create_host(int64_t max_K, int64_t max_N, int64_t slots, int workers, double c_f, ggo_cert **out);
+int ggo_cert_add_matrix(ggo_cert *c, const uint16_t *W, int64_t ld, int transposed, int64_t K, int64_t N,
+                        const int8_t *r, int64_t nr, int *id);
+int ggo_cert_submit(ggo_cert *c, int id, const uint16_t *x_dev, const float *y_dev, int64_t token, void *stream);
+int ggo_cert_submit_rows(ggo_cert *c, int64_t n, const int *ids, const uint16_t *const *x_dev,
+                         const float *const *y_dev, int64_t token, void *stream);
+int ggo_cert_submit_host(ggo_cert *c, int id, const uint16_t *x, const float *y, int64_t token);
+int ggo_cert_drain(ggo_cert *c, ggo_cert_stats *out);
+int64_t ggo_cert_failures(ggo_cert *c, int64_t *tokens, int *matrices, int64_t cap);
+void ggo_cert_destroy(ggo_cert *c);
+
 #ifdef __cplusplus
 }
 #endif

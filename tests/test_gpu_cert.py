@@ -1,0 +1,75 @@
+"""The certificate engine in a decode loop on the GPU: every output row of every matrix of every token is
+copied asynchronously (engine stream, after the GEMV on the caller's stream) and checked on host
+threads; faults planted on the device outputs of chosen tokens are exactly the failures reported."""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_util import dev_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gemv_gemm_ordered_amd as g
+    return g
+
+
+def test_decode_loop_catches_exactly_the_planted_faults(g):
+    import torch
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]   # (N, K) of W^T
+    WTs = [synth.normal_bf16(1 + i, "cert.WT", (n, k), 0.02) for i, (n, k) in enumerate(shapes)]
+    eng = g.CertEngine(11008, 11008, slots=32, workers=4)
+    mids = [eng.add_matrix(wt, np.stack([synth.rademacher(9 + i, "cert.r", wt.shape[0]) for i in range(2)]),
+                           transposed=True) for wt in WTs]
+    dW = [dev_bf16(wt) for wt in WTs]
+    keep, planted = [], set()
+    rng = np.random.default_rng(1)
+    say("cert decode loop: 24 tokens x 3 matrices")
+    for tok in range(24):
+        for i, (n, k) in enumerate(shapes):
+            x = dev_bf16(synth.normal_bf16(100 * tok + i, "cert.x", (1, k)))
+            y = g.gemv_tree(x, dW[i])
+            if tok % 5 == 3 and i == tok % 3:
+                # +0.05: above the detection floor tau = c_f * 2^-24 sqrt(K) sum_k |x_k| ||W[k,:]||_2 of
+                # every matrix here (about 0.009 at K = 11008, 0.002 at K = 4096)
+                y[0, int(rng.integers(0, n))] += 0.05
+                planted.add((tok, mids[i]))
+            eng.submit(mids[i], x[0], y[0], token=tok)
+            keep.append((x, y))                  # the rows must outlive their copies
+    st = eng.drain()
+    torch.cuda.synchronize()
+    assert st["submitted"] == st["checked"] == 72 and not st["copy_error"]
+    assert set(eng.failures()) == planted and st["failed"] == len(planted)
+    assert 0 < st["max_honest_ratio"] < 0.125
+    eng.close()
+
+
+def test_batched_rows_catch_exactly_the_planted_faults(g):
+    import torch
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
+    WTs = [synth.normal_bf16(7 + i, "certb.WT", (n, k), 0.02) for i, (n, k) in enumerate(shapes)]
+    eng = g.CertEngine(11008, 11008, slots=16, workers=3)
+    mids = [eng.add_matrix(wt, synth.rademacher(30 + i, "certb.r", wt.shape[0])[None, :], transposed=True)
+            for i, wt in enumerate(WTs)]
+    dW = [dev_bf16(wt) for wt in WTs]
+    keep, planted = [], set()
+    say("cert batched rows: 30 tokens x 3 matrices")
+    for tok in range(30):
+        xs, ys = [], []
+        for i, (n, k) in enumerate(shapes):
+            x = dev_bf16(synth.normal_bf16(1000 + 7 * tok + i, "certb.x", (1, k)))
+            y = g.gemv_tree(x, dW[i])
+            if tok % 4 == 1 and i == (tok // 4) % 3:
+                y[0, (97 * tok) % n] -= 0.05
+                planted.add((tok, mids[i]))
+            xs.append(x[0])
+            ys.append(y[0])
+        eng.submit_rows(mids, xs, ys, token=tok)
+        keep.append((xs, ys))
+    st = eng.drain()
+    torch.cuda.synchronize()
+    assert st["submitted"] == st["checked"] == 90 and not st["copy_error"]
+    assert set(eng.failures()) == planted
+    eng.close()
