@@ -239,51 +239,79 @@ struct Ctx {
     const MfmaArgs* p;
     int m0, n0, t, wave, wm, wn, lr, lg, nkt, rows_left;
     int aoff[8], boff[8];
+    // Byte offsets inside a stage buffer of this lane's fragment reads: A's block row 0 for each group of
+    // 32 k (block row i adds a constant), and W's block column j (group g and the +4 k-rows add
+    // constants) -- or, for W^T, block column 0 for each group. Every read is then one of these plus an
+    // immediate, and the per-lane part of the swizzle is paid once.
+    int ra[2], rw[8];
 };
+
+// Base address and byte range of tile kt's operand panels, for the buffer
+// descriptors of its loads. A tile past the end (kt >= nkt) gets empty ranges:
+// its loads write zeros to LDS without touching memory.
+struct Panels {
+    uint16_t *a, *b;
+    int na, nb;
+};
+
+template <int BN, int BK, bool WT>
+GGO_DEV Panels panels(const Ctx& c, int kt) {
+    const MfmaArgs& p = *c.p;
+    const bool live = kt < c.nkt;
+    const int k0 = live ? kt * BK : 0;
+    Panels r;
+    r.na = !live ? 0
+         : c.m0 + BM < p.M ? BM * static_cast<int>(p.lda) * 2
+                           : ((c.rows_left - 1) * static_cast<int>(p.lda) + (p.K - k0)) * 2;
+    // W: rows past K are past the range. W^T ([N, K], ldw its row stride): like A, rows past N are.
+    r.nb = !live ? 0
+         : WT ? (c.n0 + BN < p.N ? BN * static_cast<int>(p.ldw) * 2
+                                 : ((p.N - c.n0 - 1) * static_cast<int>(p.ldw) + (p.K - k0)) * 2)
+         : k0 + BK < p.K ? BK * static_cast<int>(p.ldw) * 2
+                         : ((p.K - 1 - k0) * static_cast<int>(p.ldw) + (p.N - c.n0)) * 2;
+    r.a = const_cast<uint16_t*>(p.A) + static_cast<int64_t>(c.m0) * p.lda + k0;
+    r.b = const_cast<uint16_t*>(p.W) + (WT ? static_cast<int64_t>(c.n0) * p.ldw + k0 : static_cast<int64_t>(k0) * p.ldw + c.n0);
+    return r;
+}
+
+// LDS destination of this wave's direct-to-LDS load l of a tile (A's chunks first, then W's): each load
+// instruction writes 64 consecutive 16-byte chunks.
+template <int BN, int BK, bool WT>
+GGO_DEV lds_t* load_dst(const Ctx& c, uint16_t* __restrict__ sa, int l) {
+    using G = Geo<BN, BK, WT>;
+    return (lds_t*)(l < G::A_LOADS ? sa + (l * THREADS + c.wave * 64) * 8
+                                   : sa + G::A_ELEMS + ((l - G::A_LOADS) * THREADS + c.wave * 64) * 8);
+}
 
 template <int BN, int BK, bool WT>
 GGO_DEV void issue(const Ctx& c, int kt, uint16_t* __restrict__ sa) {
     using G = Geo<BN, BK, WT>;
-    const MfmaArgs& p = *c.p;
-    // a tile past the end (kt >= nkt) gets empty ranges: its loads write zeros to LDS without touching memory
-    const bool live = kt < c.nkt;
-    const int k0 = live ? kt * BK : 0;
-    const int nrec_a = !live ? 0
-                     : c.m0 + BM < p.M ? BM * static_cast<int>(p.lda) * 2
-                                       : ((c.rows_left - 1) * static_cast<int>(p.lda) + (p.K - k0)) * 2;
-    // W: rows past K are past the range. W^T ([N, K], ldw its row stride): like A, rows past N are.
-    const int nrec_b = !live ? 0
-                     : WT ? (c.n0 + BN < p.N ? BN * static_cast<int>(p.ldw) * 2
-                                             : ((p.N - c.n0 - 1) * static_cast<int>(p.ldw) + (p.K - k0)) * 2)
-                     : k0 + BK < p.K ? BK * static_cast<int>(p.ldw) * 2
-                                     : ((p.K - 1 - k0) * static_cast<int>(p.ldw) + (p.N - c.n0)) * 2;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.A) + static_cast<int64_t>(c.m0) * p.lda + k0, 0, nrec_a, BUF_DWORD3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.W) + (WT ? static_cast<int64_t>(c.n0) * p.ldw + k0 : static_cast<int64_t>(k0) * p.ldw + c.n0),
-        0, nrec_b, BUF_DWORD3);
-    uint16_t* sb = sa + G::A_ELEMS;
+    const Panels pn = panels<BN, BK, WT>(c, kt);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(pn.a, 0, pn.na, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(pn.b, 0, pn.nb, BUF_DWORD3);
 #pragma unroll
-    for (int j = 0; j < G::A_LOADS; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t*)(sa + (j * THREADS + c.wave * 64) * 8), 16, c.aoff[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < G::B_LOADS; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_t*)(sb + (j * THREADS + c.wave * 64) * 8), 16, c.boff[j], 0, 0, 0);
+    for (int l = 0; l < G::LOADS; ++l) {
+        if (l < G::A_LOADS)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, load_dst<BN, BK, WT>(c, sa, l), 16, c.aoff[l], 0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, load_dst<BN, BK, WT>(c, sa, l), 16, c.boff[l - G::A_LOADS], 0, 0, 0);
+    }
 }
 
-// One k-tile (cur and nxt never overlap; saying so lets the compiler keep the
-// loads into nxt in flight while cur is read): wait for its loads, zero A's
-// k >= K if it is the last partial tile, make it visible to every wave, start
-// the loads of tile kt+NST-1 into the buffer of tile kt-1, then fold the
-// tile's groups of 32 k, in ascending order, into the accumulators.
+// Wait for this thread's loads of tile kt (those of the next NST-2 tiles may
+// still be in flight), zero A's k >= K if it is the last partial tile, and
+// make the tile visible to every wave. Workgroup barrier without a memory
+// fence: a fence would also wait for the loads of the following tiles, which
+// must stay in flight. Every wave has waited for its own part of tile kt, for
+// its own LDS writes and for its own reads of the tile before it, which is
+// all the ordering this barrier has to provide: after it, tile kt can be read
+// and the buffer of tile kt-1 can be refilled.
 template <int BN, int BK, int NST, bool WT>
-GGO_DEV void stage(const Ctx& c, int kt, uint16_t* __restrict__ cur, uint16_t* __restrict__ nxt,
-                   f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ]) {
+GGO_DEV void land(const Ctx& c, int kt, uint16_t* __restrict__ cur) {
     using G = Geo<BN, BK, WT>;
     const MfmaArgs& p = *c.p;
-    // this thread's loads of tile kt have landed (those of the next NST-2 tiles may still be in flight)
     __builtin_amdgcn_s_waitcnt(wait_vm(G::LOADS * (NST - 2)));
-    if ((kt + 1) * BK > p.K) {
+    if (kt < c.nkt && (kt + 1) * BK > p.K) {
 #pragma unroll
         for (int j = 0; j < G::A_LOADS; ++j) {
             const int ph = j * THREADS + c.t, r = ph / G::CA, ch = (ph % G::CA) ^ G::swz_a(r);
@@ -301,44 +329,179 @@ GGO_DEV void stage(const Ctx& c, int kt, uint16_t* __restrict__ cur, uint16_t* _
             }
         }
     }
-    // Workgroup barrier without a memory fence: a fence would also wait for the
-    // loads of the following tiles, which must stay in flight. Every wave has
-    // waited for its own part of tile kt and for its own LDS writes, which is
-    // all the ordering this barrier has to provide.
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
-    issue<BN, BK, WT>(c, kt + NST - 1, nxt);   // into the buffer of tile kt-1, free since the barrier (empty past the end)
+}
 
-    const uint16_t* sa = cur;
-    const uint16_t* sb = cur + G::A_ELEMS;
+// The operand fragments of one group of 32 k: per lane 8 consecutive k of one
+// row of A per 16-row block, and of one column of W per 16-column block (W's
+// as two 4-k halves, one per transposing read, unless W^T is given).
+template <int BN, int BK, bool WT> struct Frags {
+    bf16x8 a[Geo<BN, BK, WT>::WI];
+    i16x4 wl[Geo<BN, BK, WT>::WJ], wh[Geo<BN, BK, WT>::WJ];
+};
+
+// LDS read instructions per group: A's blocks, then W's (two per block unless W^T is given).
+template <int BN, int BK, bool WT>
+constexpr int reads_per_group() { return Geo<BN, BK, WT>::WI + (WT ? 1 : 2) * Geo<BN, BK, WT>::WJ; }
+
+// Read r of group g of the tile in `buf` into f. The order (A block 0, then
+// W's blocks, then A's other blocks) is the order the MFMAs need them in.
+template <int BN, int BK, bool WT>
+GGO_DEV void read_one(const Ctx& c, const uint16_t* __restrict__ buf, int g, int r, Frags<BN, BK, WT>& f) {
+    using G = Geo<BN, BK, WT>;
+    constexpr int ROW16 = 16 * G::CA * 16;   // bytes of 16 rows of A (or of W^T)
+    constexpr int NW = (WT ? 1 : 2) * G::WJ;
+    const char* base = reinterpret_cast<const char*>(buf);
+    if (r == 0 || r > NW) {
+        const int i = r == 0 ? 0 : r - NW;
+        f.a[i] = *reinterpret_cast<const bf16x8*>(base + c.ra[g] + i * ROW16);
+    } else if (WT) {   // W^T: 8 consecutive k of column n are one 16-byte chunk, as for A
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(base + c.rw[g] + (r - 1) * ROW16);
+        const i16x4* h = reinterpret_cast<const i16x4*>(&w);
+        f.wl[r - 1] = h[0];
+        f.wh[r - 1] = h[1];
+    } else {
+        // lanes 4t'+q of each 16-lane group read k-row g*32 + 8*lg + t' (and +4), columns 4q..4q+3
+        const int j = (r - 1) >> 1;
+        const char* w = base + c.rw[j] + g * 32 * G::CB * 16 + ((r - 1) & 1) * 4 * G::CB * 16;
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w));
+        if ((r - 1) & 1) f.wh[j] = v;
+        else f.wl[j] = v;
+    }
+}
+
+// MFMA q of a group (block i = q / WJ, j = q % WJ): W's fragment first, so the
+// instruction computes the transposed block. One instruction whose
+// accumulator operand is tied to its result: the accumulators stay in place
+// in the AGPRs for the whole k-loop, and the volatile statement keeps its
+// place among the LDS reads and loads around it, which fixes the interleaving.
+// Each accumulator gets exactly one instruction per group, so the order of q
+// inside a group is free; groups stay in ascending k.
+template <int BN, int BK, bool WT>
+GGO_DEV void mfma_one(const Frags<BN, BK, WT>& f, f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ], int q) {
+    constexpr int WJ = Geo<BN, BK, WT>::WJ;
+    const int i = q / WJ, j = q % WJ;
+    const bf16x8 w = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.wl[j], f.wh[j], 0, 1, 2, 3, 4, 5, 6, 7));
+    __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(w), "v"(f.a[i]));
+}
+
+// Direct-to-LDS load l of this thread's share of the tile whose panels are pn, to dst (load_dst); loads
+// below a_loads are A's. (The descriptors are built here from plain values; the compiler shares them
+// between the loads of a tile.)
+GGO_DEV void load_l(const Ctx& c, const Panels& pn, int l, int a_loads, lds_t* dst) {
+    const bool is_a = l < a_loads;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(is_a ? pn.a : pn.b, 0, is_a ? pn.na : pn.nb, BUF_DWORD3), dst, 16,
+        is_a ? c.aoff[l] : c.boff[l - a_loads], 0, 0, 0);
+}
+
+// One k-tile, software pipelined on the fragment registers. On entry F[par]
+// holds (or is receiving) group 0 of tile kt; groups alternate between F[0]
+// and F[1]. Each group's MFMAs run while the next group's fragments are read,
+// one read after each MFMA: those of group g+1 of this tile, or, in the
+// tile's last group, those of group 0 of tile kt+1 -- after the barrier that
+// lands tile kt+1, placed halfway through the group. The matrix pipe never
+// waits for an LDS round trip and the barrier overlaps the MFMAs in flight.
+//
+// The loads of tile kt+NST refill this tile's buffer, free once every wave has
+// passed that barrier. They go out in two halves spread thinly over the MFMAs:
+// the first after the barrier, the second before the next tile's barrier
+// (which is why prv, the buffer of tile kt-1, receives the second half of
+// tile kt-1+NST's loads here). A burst of loads would fill the load queue and
+// stall the MFMA issue behind it. Either way NST-2 tiles of loads are in
+// flight at every barrier.
+//
+// (cur, nxt and prv never overlap; saying so lets the compiler keep the loads
+// into one buffer in flight while another is read.) Past the last tile the
+// same steps run on empty ranges: the loads write zeros and touch no memory.
+template <int BN, int BK, int NST, bool WT>
+GGO_DEV void tile(const Ctx& c, int kt, int par, uint16_t* __restrict__ cur, uint16_t* __restrict__ nxt,
+                  uint16_t* __restrict__ prv, Frags<BN, BK, WT> (&F)[2],
+                  f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ]) {
+    using G = Geo<BN, BK, WT>;
+    constexpr int NG = BK / 32, NQ = G::WI * G::WJ, HALF = NQ / 2, NR = reads_per_group<BN, BK, WT>();
+    constexpr int PRE = (NG - 1) * NQ + HALF, POST = NQ - HALF;   // MFMAs before and after the barrier
+    constexpr int LA = (G::LOADS + 1) / 2, LB = G::LOADS - LA;     // loads after the barrier, and before the next
+    constexpr int SA = POST / LA, SB = PRE / (LB > 0 ? LB : 1);    // MFMAs per load
+    static_assert(NST >= 3, "a second half of loads issued before the next barrier needs a tile of slack");
+    static_assert(NR <= POST && SA >= 1 && SB >= 1, "one read and one load per MFMA at most");
+    {
+        const Panels pp = panels<BN, BK, WT>(c, kt - 1 + NST);
 #pragma unroll
-    for (int g = 0; g < BK / 32; ++g) {   // ascending groups of 32 k
-        bf16x8 af[G::WI], wf[G::WJ];
+        for (int g = 0; g + 1 < NG; ++g) {
 #pragma unroll
-        for (int j = 0; j < G::WJ; ++j) {
-            if (WT) {   // W^T: 8 consecutive k of column n are one 16-byte chunk, as for A
-                wf[j] = *reinterpret_cast<const bf16x8*>(sb + G::t_phys(c.wn * (BN / 2) + j * 16 + c.lr, g * 4 + c.lg) * 8);
-                continue;
+            for (int q = 0; q < NQ; ++q) {
+                mfma_one<BN, BK, WT>(F[(par + g) & 1], acc, q);
+                if (q < NR) read_one<BN, BK, WT>(c, cur, g + 1, q, F[(par + g + 1) & 1]);
+                const int u = g * NQ + q;
+                if (u % SB == 0 && u / SB < LB) load_l(c, pp, LA + u / SB, G::A_LOADS, load_dst<BN, BK, WT>(c, prv, LA + u / SB));
             }
-            // lanes 4t'+q of each 16-lane group point at k-row g*32 + 8*lg + t' (and +4), columns 4q..4q+3
-            const int kr = g * 32 + 8 * c.lg + (c.lr >> 2);
-            const int ch = c.wn * (BN / 16) + 2 * j + ((c.lr & 3) >> 1), half = (c.lr & 1) * 4;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + G::b_phys(kr, ch) * 8 + half));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + G::b_phys(kr + 4, ch) * 8 + half));
-            const i16x4 v8[2] = {lo, hi};
-            wf[j] = *reinterpret_cast<const bf16x8*>(v8);
         }
 #pragma unroll
-        for (int i = 0; i < G::WI; ++i)
-            af[i] = *reinterpret_cast<const bf16x8*>(sa + G::a_phys(c.wm * 128 + i * 16 + c.lr, g * 4 + c.lg) * 8);
-#pragma unroll
-        for (int i = 0; i < G::WI; ++i)
-#pragma unroll
-            for (int j = 0; j < G::WJ; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
+        for (int q = 0; q < HALF; ++q) {
+            mfma_one<BN, BK, WT>(F[(par + NG - 1) & 1], acc, q);
+            const int u = (NG - 1) * NQ + q;
+            if (u % SB == 0 && u / SB < LB) load_l(c, pp, LA + u / SB, G::A_LOADS, load_dst<BN, BK, WT>(c, prv, LA + u / SB));
+        }
     }
+    land<BN, BK, NST, WT>(c, kt + 1, nxt);
+    const Panels pn = panels<BN, BK, WT>(c, kt + NST);
+#pragma unroll
+    for (int q = HALF; q < NQ; ++q) {
+        mfma_one<BN, BK, WT>(F[(par + NG - 1) & 1], acc, q);
+        const int u = q - HALF;
+        if (u < NR) read_one<BN, BK, WT>(c, nxt, 0, u, F[(par + NG) & 1]);
+        if (u % SA == 0 && u / SA < LA) load_l(c, pn, u / SA, G::A_LOADS, load_dst<BN, BK, WT>(c, cur, u / SA));
+    }
+}
+
+// The whole k-loop in one function whose stage buffers are distinct restrict
+// parameters: every LDS read and every direct-to-LDS load below then carries
+// alias scopes that tell the buffers apart, so the compiler never has to wait
+// for the loads into one buffer before reading another.
+template <int BN, int BK, int NST, bool WT>
+GGO_DEV void kloop(const Ctx& c, uint16_t* __restrict__ b0, uint16_t* __restrict__ b1, uint16_t* __restrict__ b2,
+                   uint16_t* __restrict__ b3, f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ]) {
+    uint16_t* const buf[4] = {b0, b1, b2, b3};
+#pragma unroll
+    for (int s = 0; s + 1 < NST; ++s) issue<BN, BK, WT>(c, s, buf[s]);
+    Frags<BN, BK, WT> F[2];
+    land<BN, BK, NST, WT>(c, 0, buf[0]);
+    {   // the first half of tile NST-1's loads; tile 0 issues the second half
+        using G = Geo<BN, BK, WT>;
+        const Panels pn = panels<BN, BK, WT>(c, NST - 1);
+#pragma unroll
+        for (int l = 0; l < (G::LOADS + 1) / 2; ++l) load_l(c, pn, l, G::A_LOADS, load_dst<BN, BK, WT>(c, buf[NST - 1], l));
+    }
+#pragma unroll
+    for (int r = 0; r < reads_per_group<BN, BK, WT>(); ++r) read_one<BN, BK, WT>(c, buf[0], 0, r, F[0]);
+    // Full rounds of NST tiles carry no branch between a tile's loads and the
+    // next tile's reads (a join there makes the compiler wait for every load
+    // in flight); the last nkt % NST tiles follow.
+    // Group parity: tile kt's group 0 is group kt*NG of the k-loop, held in F[(kt*NG) & 1].
+    constexpr int NG = BK / 32;
+    static_assert((NST * NG) % 2 == 0, "a round of NST tiles keeps the fragment parity");
+    int kt = 0;
+    for (; kt + NST <= c.nkt; kt += NST) {
+#pragma unroll
+        for (int s = 0; s < NST; ++s)
+            tile<BN, BK, NST, WT>(c, kt + s, (s * NG) & 1, buf[s], buf[(s + 1) % NST], buf[(s + NST - 1) % NST], F, acc);
+    }
+#pragma unroll
+    for (int s = 0; s + 1 < NST; ++s)
+        if (kt + s < c.nkt)
+            tile<BN, BK, NST, WT>(c, kt + s, (s * NG) & 1, buf[s], buf[(s + 1) % NST], buf[(s + NST - 1) % NST], F, acc);
+    // The compiler does not see the MFMAs above, so it cannot pad the hazard of
+    // a VALU read of their results: wait here, in front of every later use, for
+    // longer than the deepest matrix pipeline.
+    __asm__ volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" :::);
+#pragma unroll
+    for (int i = 0; i < Geo<BN, BK>::WI; ++i)
+#pragma unroll
+        for (int j = 0; j < Geo<BN, BK>::WJ; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
 }
 
 // NST stage buffers: while tile kt is multiplied, the next NST-1 tiles are in
@@ -364,11 +527,23 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
     c.m0 = tm * BM;
     c.n0 = tn * BN;
     c.t = threadIdx.x;
-    c.wave = c.t >> 6;
+    c.wave = __builtin_amdgcn_readfirstlane(c.t >> 6);   // wave-uniform: LDS addresses of the loads stay scalar
     c.wm = c.wave >> 1;
     c.wn = c.wave & 1;
     c.lr = c.t & 15;           // row (or column) of the lane inside a 16 x 16 block
     c.lg = (c.t & 63) >> 4;    // k-octet of the lane
+#pragma unroll
+    for (int g = 0; g < BK / 32; ++g) {
+        c.ra[g] = G::a_phys(c.wm * 128 + c.lr, g * 4 + c.lg) * 16;
+        if (WT) c.rw[g] = G::A_ELEMS * 2 + G::t_phys(c.wn * (BN / 2) + c.lr, g * 4 + c.lg) * 16;
+    }
+    if (!WT) {
+        // lane 4t'+q of a 16-lane group: k-row 8*lg + t', 16-byte chunk 2j + q/2 of the wave's columns, half q%2
+#pragma unroll
+        for (int j = 0; j < G::WJ; ++j)
+            c.rw[j] = G::A_ELEMS * 2 + G::b_phys(8 * c.lg + (c.lr >> 2), c.wn * (BN / 16) + 2 * j + ((c.lr & 3) >> 1)) * 16
+                    + (c.lr & 1) * 8;
+    }
     c.nkt = (p.K + BK - 1) / BK;
     c.rows_left = p.M - c.m0;
     // per-thread constant byte offsets of the chunks this thread loads
@@ -394,43 +569,47 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
     for (int i = 0; i < G::WI; ++i)
 #pragma unroll
         for (int j = 0; j < G::WJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // Put the zeros in the AGPRs here, well ahead of the first MFMA (which the
+    // compiler does not see, so it would not pad a VALU write just before it).
+#pragma unroll
+    for (int i = 0; i < G::WI; ++i)
+#pragma unroll
+        for (int j = 0; j < G::WJ; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+    __asm__ volatile("s_nop 4" :::);
 
-#pragma unroll
-    for (int s = 0; s + 1 < NST; ++s) issue<BN, BK, WT>(c, s, buf[s]);
-    int kt = 0;
-    for (; kt + NST - 1 < c.nkt; kt += NST) {
-#pragma unroll
-        for (int s = 0; s < NST; ++s) stage<BN, BK, NST, WT>(c, kt + s, buf[s], buf[(s + NST - 1) % NST], acc);
-    }
-#pragma unroll
-    for (int s = 0; s + 1 < NST; ++s)
-        if (kt + s < c.nkt) stage<BN, BK, NST, WT>(c, kt + s, buf[s], buf[(s + NST - 1) % NST], acc);
+    kloop<BN, BK, NST, WT>(c, lds_stage0, lds_stage1, lds_stage2, lds_stage3, acc);
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the trailing empty-range loads have landed before the workgroup ends
 
     // lane holds C[row][col .. col+3] of each block: row = lane % 16, col = 4 * (lane / 16)
     if (!epi_identity(p.ep)) {
-        // Fused epilogue. Each wave stages half of its 128 x (BN/2) results at a time in LDS (the operand
-        // ring is free now), then walks them row-major in a plain loop: coalesced bias / residual loads
-        // and stores, and the epilogue's code appears once instead of once per accumulator.
-        constexpr int RS = BN / 2 + 4;   // floats per staged row; +4 spreads 16 rows over the banks
-        static_assert(2 * 64 * RS * 4 <= G::STAGE * 2, "two wave regions per stage buffer");
-        __syncthreads();                 // every wave has finished reading the last stage
-        float* region = reinterpret_cast<float*>(c.wave < 2 ? buf[0] : buf[1]) + (c.wave & 1) * 64 * RS;
+        // Fused epilogue. Each wave stages 32 rows of its 128 x (BN/2) results at a time in a region of its
+        // own in LDS (the operand ring is free now), then walks them row-major in a plain loop: coalesced
+        // bias / residual loads and stores, and the epilogue's code appears once instead of once per
+        // accumulator.
+        constexpr int RS = BN / 2 + 4;              // floats per staged row; +4 spreads 16 rows over the banks
+        constexpr int PR = 32;                      // rows per pass
+        constexpr int WPB = (4 + NST - 1) / NST;    // wave regions per stage buffer
+        static_assert(WPB * PR * RS * 4 <= G::STAGE * 2, "the wave regions fit in the stage buffers");
+        __syncthreads();                            // every wave has finished reading the last stage
+        const int wb = c.wave % NST;                // selects, not an indexed load: the buffers are LDS objects
+        uint16_t* const rb = wb == 0 ? buf[0] : wb == 1 ? buf[1] : wb == 2 ? buf[2] : buf[3];
+        float* region = reinterpret_cast<float*>(rb) + (c.wave / NST) * PR * RS;
         const int lane = c.t & 63;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int pass = 0; pass < 128 / PR; ++pass) {
 #pragma unroll
-            for (int ii = 0; ii < G::WI / 2; ++ii)
+            for (int ii = 0; ii < PR / 16; ++ii)
 #pragma unroll
-                for (int j = 0; j < G::WJ; ++j)
+                for (int j = 0; j < G::WJ; ++j) {
+                    const f32x4 v = acc[pass * (PR / 16) + ii][j];
                     *reinterpret_cast<float4*>(region + (ii * 16 + c.lr) * RS + j * 16 + 4 * c.lg) =
-                        make_float4(acc[half * (G::WI / 2) + ii][j][0], acc[half * (G::WI / 2) + ii][j][1],
-                                    acc[half * (G::WI / 2) + ii][j][2], acc[half * (G::WI / 2) + ii][j][3]);
+                        make_float4(v[0], v[1], v[2], v[3]);
+                }
             __syncthreads();
 #pragma unroll 1
-            for (int e = lane; e < 64 * (BN / 8); e += 64) {
+            for (int e = lane; e < PR * (BN / 8); e += 64) {
                 const int rl = e / (BN / 8), c4 = e % (BN / 8);
-                const int row = c.m0 + c.wm * 128 + half * 64 + rl;
+                const int row = c.m0 + c.wm * 128 + pass * PR + rl;
                 const int col = c.n0 + c.wn * (BN / 2) + 4 * c4;
                 if (row >= p.M || col >= p.N) continue;
                 const float4 y = *reinterpret_cast<const float4*>(region + rl * RS + 4 * c4);
@@ -441,7 +620,7 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
                     for (int r = 0; r < 4 && col + r < p.N; ++r) epi_store(p.ep, p.C, p.ldc, row, col + r, yv[r]);
                 }
             }
-            __syncthreads();             // before the next half overwrites the region
+            __syncthreads();                        // before the next pass overwrites the region
         }
         return;
     }
