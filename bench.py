@@ -376,7 +376,7 @@ def traffic_summary(fetch_dir, write_dir):
         rec["hbm_over_algorithmic"] = rec["hbm_bytes"] / rec["algorithmic_bytes"]
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
-    lines = ["# k_gemv_tree — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
+    lines = ["# k_gemv_tree_p — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
              "Commands (from the repository root, on one MI355X):", "",
              "    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/traffic_fetch -o run -- python3 $REPO/bench.py --counters",
              "    cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/traffic_write -o run -- python3 $REPO/bench.py --counters",
@@ -558,7 +558,7 @@ def main():
                    "graph": run is not None, "parity": parity},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(ms),
-                     "kernel": "k_gemv_tree", "avg_launch_us": round(avg_launch_us, 3),
+                     "kernel": "k_gemv_tree_p", "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch": step_bytes / len(ms)},
         "cpu_baseline": cpu,
         "per_M": per_m,

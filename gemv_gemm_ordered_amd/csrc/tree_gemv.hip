@@ -30,6 +30,9 @@
 // and 16-byte aligned operands (then no load straddles the end of a row); the narrow instances load
 // 2 bytes per element and take any operands. The result of each output goes through the fused
 // epilogue (epilogue.hpp) on its way out.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -213,6 +216,150 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree(TreeArgs a) {
     }
 }
 
+// The same arithmetic in persistent form, for 16-byte operands with K <= S * 2048 (S steps per
+// chain) and M <= 8. A lane's x tiles are the same for every output n (chain p always takes the
+// tiles p, p + 256, ...), so they are loaded once, widened to binary32 and kept in registers. The
+// workgroup then walks groups of R outputs, g = blockIdx.x, blockIdx.x + gridDim.x, ..., with the
+// weight rows of the next NB - 1 groups in flight while a group is folded: the weight stream and the
+// FMAs overlap, and the x tiles are not fetched again for every R rows. (In the form above a
+// workgroup owns one group: all of its loads, then all of its FMAs, in step with the other
+// workgroups on its CU.) Every output's chains, their order and the tree are those of k_gemv_tree,
+// so the bits are too.
+template <int MT, int R, int S>
+GGO_DEV void load_group(const TreeArgs& a, int g, int off, uint32_t (&w)[S][R][4]) {
+    const int kbytes = a.K * 2;
+    rsrc_t wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = static_cast<int64_t>(g) * R + r;
+        wr[r] = row_rsrc(a.WT + n * a.ldwt, n < a.N ? kbytes : 0);   // past N (or past the last group): empty
+    }
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+#pragma unroll
+        for (int r = 0; r < R; ++r) load_tile<true, AUX_STREAM>(wr[r], off + j * STEP_BYTES, w[j][r]);
+}
+
+template <int MT, int R, bool EPI>
+GGO_DEV void reduce_store(const TreeArgs& a, int64_t n0, float (&acc)[R][MT], float (&red)[WAVES][R * MT], int lane,
+                          int wave) {
+    constexpr int V = R * MT;
+    static_assert(V <= 64 && (V & (V - 1)) == 0, "one wave total per lane at most, a power of two");
+    float v[V];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) v[r * MT + m] = acc[r][m];
+    wave_tree_scatter<V, 1>(v, lane);
+    if (lane < V) red[wave][scatter_index<V>(lane)] = v[0];
+    __syncthreads();
+    for (int i = threadIdx.x; i < V; i += THREADS) {
+        const int r = i / MT, m = i % MT;
+        if (m < a.M && n0 + r < a.N) {
+            const float y = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
+            if constexpr (EPI) epi_store(a.ep, a.y, a.ldy, m, n0 + r, y);
+            else static_cast<float*>(a.y)[m * a.ldy + n0 + r] = y;
+        }
+    }
+}
+
+// fold_tile with the x tile already widened to binary32.
+template <int MT, int R, int S>
+GGO_DEV void fold_group(float (&acc)[R][MT], const uint32_t (&w)[S][R][4], const float (&xf)[S][MT][TILE]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < S; ++j)          // the chain's tiles in ascending order, k ascending in each
+#pragma unroll
+        for (int e = 0; e < TILE; ++e) {
+            float wf[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) wf[r] = elem(w[j][r], e);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[r][m] = __builtin_fmaf(xf[j][m][e], wf[r], acc[r][m]);
+        }
+}
+
+template <int MT, int R, int S, int NB, bool EPI>
+__global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = wave * 64 + lane;
+    const int off = p * TILE * 2;
+    const int groups = static_cast<int>((a.N + R - 1) / R);
+    const int kbytes = a.K * 2;
+
+    float x[S][MT][TILE];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const rsrc_t xr = row_rsrc(a.x + m * a.ldx, m < a.M ? kbytes : 0);
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            uint32_t d[4];
+            load_tile<true>(xr, off + j * STEP_BYTES, d);
+#pragma unroll
+            for (int e = 0; e < TILE; ++e) x[j][m][e] = elem(d, e);
+        }
+    }
+    // NB weight buffers in rotation, and as many reduction buffers: a group's LDS totals are read
+    // after its barrier and not written again before NB - 1 more barriers.
+    __shared__ float red[NB][WAVES][R * MT];
+    uint32_t w[NB][S][R][4];
+    float acc[R][MT];
+    const int stride = gridDim.x;
+    int g = blockIdx.x;                       // < groups: the grid is never larger
+#pragma unroll
+    for (int b = 0; b + 1 < NB; ++b) load_group<MT, R, S>(a, g + b * stride, off, w[b]);
+    for (;;) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int gb = g + b * stride;
+            load_group<MT, R, S>(a, gb + (NB - 1) * stride, off, w[(b + NB - 1) % NB]);
+            __builtin_amdgcn_sched_barrier(0);    // the requests stay ahead of this fold
+            fold_group<MT, R, S>(acc, w[b], x);
+            reduce_store<MT, R, EPI>(a, static_cast<int64_t>(gb) * R, acc, red[b], lane, wave);
+            if (gb + stride >= groups) goto done;
+        }
+        g += NB * stride;
+    }
+done:
+    // the loads of the groups past the end (empty ranges) return zeros to registers nobody reads;
+    // they have landed before the wave ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+}
+
+// Compute units of the current device (the persistent grid is a few workgroups per CU).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Persistent launch: R outputs per group, NB groups in rotation, two workgroups per CU (8 waves).
+// Measured on the decode shape (N = K = 4096): smaller groups keep more workgroups streaming at
+// M = 4 and 8, where the fold per group is largest; deeper rotation (NB = 3, 4) spreads the requests
+// in flight over more of the matrix and reads slower.
+template <int MT, int S>
+hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
+    constexpr int R = MT >= 4 ? 2 : 4, NB = 2, PER_CU = 2;
+    const int64_t groups = (a.N + R - 1) / R;
+    const int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
+    if (epi_identity(a.ep))
+        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, false>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, true>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int MT, bool WIDE>
 hipError_t launch_mt(const TreeArgs& a, hipStream_t stream) {
     // Rows per workgroup: 4 keeps more workgroups (and loads) in flight; at MT = 8 the x tiles,
@@ -224,6 +371,14 @@ hipError_t launch_mt(const TreeArgs& a, hipStream_t stream) {
     else
         hipLaunchKernelGGL((k_gemv_tree<MT, R, WIDE, true>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_any(const TreeArgs& a, hipStream_t stream) {
+    const int steps = (a.K + TILE * CHAINS - 1) / (TILE * CHAINS);
+    if (a.wide && steps <= 1) return launch_persistent<MT, 1>(a, stream);
+    if (a.wide && steps == 2) return launch_persistent<MT, 2>(a, stream);
+    return a.wide ? launch_mt<MT, true>(a, stream) : launch_mt<MT, false>(a, stream);
 }
 
 template <bool WIDE>
@@ -240,5 +395,9 @@ hipError_t launch_w(const TreeArgs& a, hipStream_t stream) {
 int gemv_tree_max_k() { return (1 << 29) - 3 * TILE * CHAINS; }
 
 hipError_t launch_gemv_tree(const TreeArgs& a, hipStream_t stream) {
+    if (a.M <= 1) return launch_any<1>(a, stream);
+    if (a.M <= 2) return launch_any<2>(a, stream);
+    if (a.M <= 4) return launch_any<4>(a, stream);
+    if (a.M <= 8) return launch_any<8>(a, stream);
     return a.wide ? launch_w<true>(a, stream) : launch_w<false>(a, stream);
 }

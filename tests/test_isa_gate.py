@@ -72,9 +72,12 @@ def test_tree_kernels_use_single_fma_and_add(code):
     The epilogue instances add the epilogue's own operations after the fold; they are checked for no
     packed, dot or matrix instruction."""
     ks = [k for k in code["tree_gemv.hip"] if "k_gemv_tree" in k]
-    assert len(ks) == 20, ks   # M tiers 1, 2, 4, 8, 16 x 16-byte / 2-byte loads x with / without epilogue
+    # one-group form: M tiers 1, 2, 4, 8, 16 x 16-byte / 2-byte loads x with / without epilogue;
+    # persistent form: M tiers 1, 2, 4, 8 x 1 or 2 steps per chain x with / without epilogue
+    assert len([k for k in ks if "k_gemv_treeI" in k]) == 20, ks
+    assert len([k for k in ks if "k_gemv_tree_pI" in k]) == 16, ks
     plain = [k for k in ks if k.endswith("Lb0EEEv8TreeArgs")]
-    assert len(plain) == 10, plain
+    assert len(plain) == 18, plain
     for k in ks:
         text = "\n".join(code["tree_gemv.hip"][k])
         assert not MFMA.search(text) and not re.search(r"\bv_dot|\bv_pk_(?:fma|mul|add)_f32", text), k
