@@ -213,12 +213,17 @@ template <int BN, int BK, bool WT = false> struct Geo {
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static_assert(A_LOADS <= 8 && B_LOADS <= 8, "Ctx holds at most 8 offsets per operand");
     // LDS position (in 16-byte chunks) of A chunk (row r, k-chunk c) and of W
-    // chunk (k-row k, n-chunk c); the XOR keeps the 8 lanes that one 16-byte
-    // read serves in one cycle (and the 16 lanes of one transposing read) on
-    // distinct groups of 4 banks.
+    // chunk (k-row k, n-chunk c). The XOR on A keeps the lanes that one 16-byte
+    // read serves per cycle on distinct banks. On W, a transposing read's
+    // 16-lane group takes two chunks of four consecutive k-rows: k mod 4 moves
+    // each row to its own pair of chunks, and k bit 3 swaps the row's 128-byte
+    // halves, because the two groups served in one pass read rows 8 apart
+    // (without it the two groups hit the same banks, two conflict cycles per read).
+    static_assert(WT || CB >= 16, "the W swizzle needs rows of at least 16 chunks");
     static GGO_DEV int swz_a(int r) { return CA == 8 ? (r & 7) : ((r >> 1) & 3); }
+    static GGO_DEV int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
     static GGO_DEV int a_phys(int r, int c) { return r * CA + (c ^ swz_a(r)); }
-    static GGO_DEV int b_phys(int k, int c) { return k * CB + (c ^ ((k & 3) << 1)); }   // W, k-major
+    static GGO_DEV int b_phys(int k, int c) { return k * CB + (c ^ swz_b(k)); }   // W, k-major
     static GGO_DEV int t_phys(int n, int c) { return n * CA + (c ^ swz_a(n)); }         // W^T, like A
 };
 
@@ -559,7 +564,7 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
             const int r = ph / G::CA, ch = (ph % G::CA) ^ G::swz_a(r);
             c.boff[j] = (r * static_cast<int>(p.ldw) + 8 * ch) * 2;
         } else {
-            const int k = ph / G::CB, ch = (ph % G::CB) ^ ((k & 3) << 1);
+            const int k = ph / G::CB, ch = (ph % G::CB) ^ G::swz_b(k);
             c.boff[j] = (k * static_cast<int>(p.ldw) + 8 * ch) * 2;
         }
     }
