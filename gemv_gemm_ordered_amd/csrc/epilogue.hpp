@@ -97,13 +97,12 @@ GGO_DEV void epi_store(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n,
     else static_cast<float*>(C)[m * ldc + n] = v;
 }
 
-// Four consecutive results of row m, columns n .. n+3, with 16-byte bias / residual loads and one
-// 16-byte (binary32) or 8-byte (bfloat16) store. The caller guarantees the alignment.
-GGO_DEV void epi_store4(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n, float y0, float y1, float y2,
-                        float y3) {
-    float v[4] = {y0, y1, y2, y3};
+// Four consecutive results of row m, columns n .. n+3, given the bias b[n .. n+3] and the residual
+// r[m, n .. n+3] already loaded (ignored when the epilogue has none), with one 16-byte (binary32) or
+// 8-byte (bfloat16) store. The caller guarantees the alignment.
+GGO_DEV void epi_finish4(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n, float4 y, float4 b, float4 r) {
+    float v[4] = {y.x, y.y, y.z, y.w};
     if (e.bias) {
-        const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
         v[0] = v[0] + b.x;
         v[1] = v[1] + b.y;
         v[2] = v[2] + b.z;
@@ -112,7 +111,6 @@ GGO_DEV void epi_store4(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = epi_act(v[i], e.act);
     if (e.res) {
-        const float4 r = *reinterpret_cast<const float4*>(e.res + m * e.ldr + n);
         v[0] = v[0] + r.x;
         v[1] = v[1] + r.y;
         v[2] = v[2] + r.z;
@@ -125,4 +123,18 @@ GGO_DEV void epi_store4(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n
     } else {
         *reinterpret_cast<float4*>(static_cast<float*>(C) + m * ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
     }
+}
+
+GGO_DEV float4 epi_bias4(const Epi& e, int64_t n) {
+    return e.bias ? *reinterpret_cast<const float4*>(e.bias + n) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+GGO_DEV float4 epi_res4(const Epi& e, int64_t m, int64_t n) {
+    return e.res ? *reinterpret_cast<const float4*>(e.res + m * e.ldr + n) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+// Four consecutive results with 16-byte bias / residual loads: epi_finish4 after its loads.
+GGO_DEV void epi_store4(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n, float y0, float y1, float y2,
+                        float y3) {
+    epi_finish4(e, C, ldc, m, n, make_float4(y0, y1, y2, y3), epi_bias4(e, n), epi_res4(e, m, n));
 }

@@ -509,6 +509,19 @@ GGO_DEV void kloop(const Ctx& c, uint16_t* __restrict__ b0, uint16_t* __restrict
         for (int j = 0; j < Geo<BN, BK>::WJ; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
 }
 
+// Write block rows P * NI .. P * NI + NI - 1 of this wave's accumulators into its LDS region (RS floats
+// per row); lane (lr, lg) holds columns 4 lg .. 4 lg + 3 of row lr of each 16 x 16 block.
+template <int BN, int BK, bool WT, int P, int NI>
+GGO_DEV void stage_rows(const f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ], float* region, int RS, const Ctx& c) {
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+        for (int j = 0; j < Geo<BN, BK, WT>::WJ; ++j) {
+            const f32x4 v = acc[P * NI + ii][j];
+            *reinterpret_cast<float4*>(region + (ii * 16 + c.lr) * RS + j * 16 + 4 * c.lg) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+}
+
 // NST stage buffers: while tile kt is multiplied, the next NST-1 tiles are in
 // flight. The buffers are separate LDS objects and the k-loop is unrolled by
 // NST, so every load and read names its buffer statically: the compiler can
@@ -600,22 +613,44 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
         uint16_t* const rb = wb == 0 ? buf[0] : wb == 1 ? buf[1] : wb == 2 ? buf[2] : buf[3];
         float* region = reinterpret_cast<float*>(rb) + (c.wave / NST) * PR * RS;
         const int lane = c.t & 63;
-#pragma unroll
+        // The pass loop is not unrolled (its body is large); the accumulators are only ever indexed with
+        // constants, through the switch, so they stay in registers.
+#pragma unroll 1
         for (int pass = 0; pass < 128 / PR; ++pass) {
-#pragma unroll
-            for (int ii = 0; ii < PR / 16; ++ii)
-#pragma unroll
-                for (int j = 0; j < G::WJ; ++j) {
-                    const f32x4 v = acc[pass * (PR / 16) + ii][j];
-                    *reinterpret_cast<float4*>(region + (ii * 16 + c.lr) * RS + j * 16 + 4 * c.lg) =
-                        make_float4(v[0], v[1], v[2], v[3]);
-                }
+            static_assert(128 / PR == 4, "four passes of 32 rows");
+            switch (pass) {
+            case 0: stage_rows<BN, BK, WT, 0, PR / 16>(acc, region, RS, c); break;
+            case 1: stage_rows<BN, BK, WT, 1, PR / 16>(acc, region, RS, c); break;
+            case 2: stage_rows<BN, BK, WT, 2, PR / 16>(acc, region, RS, c); break;
+            default: stage_rows<BN, BK, WT, 3, PR / 16>(acc, region, RS, c); break;
+            }
             __syncthreads();
+            const int row0 = c.m0 + c.wm * 128 + pass * PR, col0 = c.n0 + c.wn * (BN / 2);
+            if ((p.vec & VEC_EP) && row0 + PR <= p.M && col0 + BN / 2 <= p.N) {
+                // Whole pass in range: every bias / residual load of the pass goes out first, so the
+                // pass waits for memory once instead of once per 4 results.
+                constexpr int IT = PR * (BN / 8) / 64;
+                float4 bv[IT], rv[IT];
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const int e = lane + 64 * i, rl = e / (BN / 8), c4 = e % (BN / 8);
+                    bv[i] = epi_bias4(p.ep, col0 + 4 * c4);
+                    rv[i] = epi_res4(p.ep, row0 + rl, col0 + 4 * c4);
+                }
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const int e = lane + 64 * i, rl = e / (BN / 8), c4 = e % (BN / 8);
+                    const float4 y = *reinterpret_cast<const float4*>(region + rl * RS + 4 * c4);
+                    epi_finish4(p.ep, p.C, p.ldc, row0 + rl, col0 + 4 * c4, y, bv[i], rv[i]);
+                }
+                __syncthreads();                    // before the next pass overwrites the region
+                continue;
+            }
 #pragma unroll 1
             for (int e = lane; e < PR * (BN / 8); e += 64) {
                 const int rl = e / (BN / 8), c4 = e % (BN / 8);
-                const int row = c.m0 + c.wm * 128 + pass * PR + rl;
-                const int col = c.n0 + c.wn * (BN / 2) + 4 * c4;
+                const int row = row0 + rl;
+                const int col = col0 + 4 * c4;
                 if (row >= p.M || col >= p.N) continue;
                 const float4 y = *reinterpret_cast<const float4*>(region + rl * RS + 4 * c4);
                 if (col + 4 <= p.N && (p.vec & VEC_EP)) {

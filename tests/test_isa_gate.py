@@ -107,3 +107,17 @@ def test_no_atomics_anywhere(code):
         for k, lines in ks.items():
             for line in lines:
                 assert not ATOMIC.search(line), (src, k, line)
+
+
+def test_hot_kernels_use_no_scratch(code):
+    """The matrix-core and tree GEMV kernels keep all their state in registers and LDS. A scratch
+    (private memory) access in them means an array the compiler could not keep in registers -- for
+    example an accumulator array indexed with a runtime value -- and it turns every matrix
+    instruction into a memory round trip while the results stay correct."""
+    scratch = re.compile(r"\b(scratch_\w+|buffer_(?:load|store)_\w+ [^;]*\boff, s\[0:3\])")
+    for src, tag in (("mfma_invariant.hip", "k_gemm_mfma"), ("tree_gemv.hip", "k_gemv_tree")):
+        ks = [k for k in code[src] if tag in k]
+        assert ks, src
+        for k in ks:
+            hits = [line for line in code[src][k] if scratch.search(line)]
+            assert not hits, (k, hits[:3])
