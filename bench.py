@@ -107,9 +107,34 @@ def cpu_baseline(x, WT, ms, seconds):
         if dt >= seconds:
             break
     gbs = steps * sum(gemv_bytes(M) for M in ms) / dt / 1e9
+    # the same oracle over all host threads (rows split across threads; same bits), for half the time
+    threads = max(1, min(16, os.cpu_count() or 1))
+    steps_all, t0 = 0, time.perf_counter()
+    while True:
+        for M in ms:
+            oracle.gemv_tree(x[:M], WT, threads=threads)
+        steps_all += 1
+        dt_all = time.perf_counter() - t0
+        if dt_all >= seconds / 2:
+            break
+    gbs_all = steps_all * sum(gemv_bytes(M) for M in ms) / dt_all / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} full decode steps (M={','.join(map(str, ms))}, K=N=4096) of the tree-order "
-                      f"oracle, plain C, single-threaded, {dt:.1f} s"}
+                      f"oracle, plain C, single-threaded, {dt:.1f} s",
+            "all_cores": {"value": round(gbs_all, 4), "cores": threads,
+                          "sample": f"{steps_all} steps, rows split over {threads} threads, {dt_all:.1f} s"},
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def certificate(g, x, W, r, ys, ms):
@@ -155,8 +180,9 @@ def paths(g, reps):
             return torch.mm(A, W)
 
     # MLP up-projection and 7B projections: ordered VALU, MFMA invariant, hipBLASLt
+    # (7b_up_shard8: one GPU's share of the up-projection's W split 8 ways along N)
     shapes = [("mlp_up", 256, 4096, 1024), ("mlp_up", 2048, 4096, 1024),
-              ("7b_qkvo", 4096, 4096, 4096), ("7b_up", 4096, 11008, 4096)]
+              ("7b_qkvo", 4096, 4096, 4096), ("7b_up", 4096, 11008, 4096), ("7b_up_shard8", 4096, 1376, 4096)]
     for name, M, N, K in shapes:
         A = randn_bf16((M, K), 1.0)
         W = randn_bf16((K, N), 0.02)
@@ -175,6 +201,21 @@ def paths(g, reps):
         rec["mfma_vs_hipblaslt"] = round(tb / t, 3)
         out[f"{name}_M{M}_N{N}_K{K}"] = rec
         del A, W, C
+    # invariance control on the MLP shape: row 0's bits at each M against M = 2048, for the MFMA path and
+    # for hipBLASLt (the control: if its rows never moved, the invariance shown here would be trivial)
+    A = randn_bf16((2048, 1024), 1.0)
+    W = randn_bf16((1024, 4096), 0.02)
+    ref_m = g.gemm_mfma_invariant(A, W)[0].view(torch.int32).clone()
+    ref_b = mm_blaslt(A, W)[0].float().view(torch.int32).clone()
+    moved_m, moved_b = [], []
+    for M in (1, 2, 8, 64, 128, 256, 512, 1024):
+        if not torch.equal(g.gemm_mfma_invariant(A[:M], W)[0].view(torch.int32), ref_m):
+            moved_m.append(M)
+        if not torch.equal(mm_blaslt(A[:M], W)[0].float().view(torch.int32), ref_b):
+            moved_b.append(M)
+    out["invariance_control_mlp_up_N4096_K1024"] = {
+        "row0_bits_differ_from_M2048_at_M": {"gemm_mfma_invariant": moved_m, "hipblaslt": moved_b}}
+    del A, W
     # fused epilogue (bias, activation, residual, bf16 output) against the same steps as separate kernels
     F = torch.nn.functional
     N = K = 4096

@@ -211,3 +211,21 @@ def test_full_size_sampled_rows_equal_cpu_model(g, name, M, n):
     assert np.array_equal(got, ref)
     got_wt = host_bits(g.gemm_mfma_invariant_wt(dA, _wt(dW)))[rows]
     assert np.array_equal(got_wt, ref)
+
+
+def test_hipblaslt_control_rows_move_with_M(g):
+    """The control of the invariance tests: the vendor GEMM (hipBLASLt through torch.mm, binary32 out)
+    on the same data gives row 0 different bits at some M, while gemm_mfma_invariant gives the same
+    bits at every M. Without the control the invariance checks would not show anything."""
+    import torch
+    A = dev_bf16(synth.normal_bf16(41, "ctl.A", (2048, 1024)))
+    W = dev_bf16(synth.normal_bf16(41, "ctl.W", (1024, 4096), 0.02))
+    say("hipBLASLt control, MLP shape")
+    ref_m = g.gemm_mfma_invariant(A, W)[0].view(torch.int32).clone()
+    ref_b = torch.mm(A, W, out_dtype=torch.float32)[0].view(torch.int32).clone()
+    moved_b = []
+    for M in (1, 2, 8, 64, 128, 256, 512, 1024):
+        assert torch.equal(g.gemm_mfma_invariant(A[:M], W)[0].view(torch.int32), ref_m), M
+        if not torch.equal(torch.mm(A[:M], W, out_dtype=torch.float32)[0].view(torch.int32), ref_b):
+            moved_b.append(M)
+    assert moved_b, "hipBLASLt gave row 0 the same bits at every M: the control shows nothing here"
