@@ -26,6 +26,7 @@
 #include <vector>
 
 #include "../../include/ggo.h"
+#include "kernels.hpp"
 
 namespace {
 
@@ -75,7 +76,7 @@ struct ggo_cert {
 namespace {
 
 void worker_loop(ggo_cert* c) {
-    std::vector<double> out(4);
+    std::vector<double> out(4 * FREIVALDS_MAX_T);
     for (;;) {
         int id;
         {
@@ -93,12 +94,16 @@ void worker_loop(ggo_cert* c) {
         double worst = 0.0;
         const auto t0 = std::chrono::steady_clock::now();
         if (copy_ok) {
-            for (int v = 0; v < m.nr; ++v) {
-                const int rc = freivalds_check(m.s.data() + v * m.K, m.q.data(), m.a.data(), m.r.data() + v * m.N,
-                                               m.K, m.N, sl.x, sl.y, c->c_f, out.data());
+            // all sign vectors in one pass over the row (up to FREIVALDS_MAX_T at a time)
+            for (int v0 = 0; v0 < m.nr; v0 += FREIVALDS_MAX_T) {
+                const int t = std::min(FREIVALDS_MAX_T, m.nr - v0);
+                const int rc = freivalds_check_multi(t, m.s.data() + static_cast<int64_t>(v0) * m.K, m.q.data(), m.a.data(),
+                                                     m.r.data() + static_cast<int64_t>(v0) * m.N, m.K, m.N, sl.x, sl.y,
+                                                     c->c_f, out.data());
                 if (rc < 0) copy_ok = false;
                 if (rc != 1) pass = false;
-                if (out[1] > 0.0) worst = std::max(worst, out[0] / out[1]);
+                for (int v = 0; v < t; ++v)
+                    if (out[4 * v + 1] > 0.0) worst = std::max(worst, out[4 * v] / out[4 * v + 1]);
             }
         }
         const double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
@@ -191,7 +196,8 @@ static int create(int64_t max_K, int64_t max_N, int64_t nslots, int nworkers, do
                    hipHostMalloc(reinterpret_cast<void**>(&s.y), static_cast<size_t>(max_N) * 4) != hipSuccess ||
                    hipHostGetDevicePointer(reinterpret_cast<void**>(&s.x_dev), s.x, 0) != hipSuccess ||
                    hipHostGetDevicePointer(reinterpret_cast<void**>(&s.y_dev), s.y, 0) != hipSuccess ||
-                   hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess) {
+                   // blocking sync: a worker waiting for its slot's copy sleeps instead of spinning
+                   hipEventCreateWithFlags(&s.done, hipEventDisableTiming | hipEventBlockingSync) != hipSuccess) {
             rc = GGO_ELAUNCH;
         }
         c->free_slots.push_back(static_cast<int>(i));

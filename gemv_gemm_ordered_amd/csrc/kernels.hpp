@@ -52,6 +52,12 @@ struct TreeArgs {
 hipError_t launch_gemv_tree(const TreeArgs& a, hipStream_t stream);
 int gemv_tree_max_k();   // byte offsets along a row are 32-bit
 
+// Float Freivalds check of one row against t <= FREIVALDS_MAX_T sign vectors in one pass (freivalds.cpp);
+// the same values and verdicts as t calls of freivalds_check.
+constexpr int FREIVALDS_MAX_T = 16;
+int freivalds_check_multi(int t, const double* s, const double* q, const double* a, const int8_t* r, int64_t K,
+                          int64_t N, const uint16_t* x, const float* y, double c_f, double* out);
+
 struct MfmaArgs {
     const uint16_t* A;
     const uint16_t* W;
