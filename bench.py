@@ -271,10 +271,11 @@ def cert_loop(g, tokens=48):
     res = {"matrices": len(shapes), "tokens": tokens, "rows_per_token": len(shapes)}
 
     def run(eng, mids):
-        keep = []
+        keep, stamps = [], []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for tok in range(tokens):
+            stamps.append(time.perf_counter())
             rows = []
             for i in range(len(shapes)):
                 x = xs[i][tok % 4]
@@ -287,21 +288,28 @@ def cert_loop(g, tokens=48):
         t1 = time.perf_counter()
         st = eng.drain() if eng is not None else None
         t2 = time.perf_counter()
-        return (t1 - t0) / tokens, t2 - t1, st
+        # host time of each token's launches and submit (the device runs behind; the mean includes
+        # the final synchronisation)
+        per = np.diff(np.array(stamps + [t1]))
+        return (t1 - t0) / tokens, t2 - t1, st, float(np.median(per)), float(per.max())
 
     run(None, None)
-    base, _, _ = run(None, None)
+    base, _, _, base_med, _ = run(None, None)
     res["no_certificate_us_per_token"] = round(1e6 * base, 1)
+    res["no_certificate_median_us_per_token"] = round(1e6 * base_med, 1)
     Wh = [w.view(torch.int16).cpu().numpy().view(np.uint16) for w in WTs]
     for t in (1, 4):
         eng = g.CertEngine(11008, 11008, slots=64, workers=4)
         rng = np.random.default_rng(t)
         mids = [eng.add_matrix(w, rng.choice(np.int8([-1, 1]), size=(t, w.shape[0])), transposed=True) for w in Wh]
-        per_tok, drain, st = run(eng, mids)
-        res[f"t{t}"] = {"us_per_token": round(1e6 * per_tok, 1), "drain_after_gpu_ms": round(1e3 * drain, 2),
+        per_tok, drain, st, med, worst = run(eng, mids)
+        res[f"t{t}"] = {"us_per_token": round(1e6 * per_tok, 1), "median_us_per_token": round(1e6 * med, 1),
+                        "slowest_token_us": round(1e6 * worst, 1), "drain_after_gpu_ms": round(1e3 * drain, 2),
                         "rows_checked": st["checked"], "failed": st["failed"],
                         "max_honest_ratio": round(st["max_honest_ratio"], 5),
                         "host_check_us_per_row": round(1e6 * st["check_seconds"] / max(1, st["checked"]), 1),
+                        "copy_wait_us_per_row": round(1e6 * st["wait_seconds"] / max(1, st["checked"]), 1),
+                        "submit_wait_us_per_token": round(1e6 * st["submit_wait_seconds"] / tokens, 1),
                         "escape_probability_of_a_cancelling_fault": 2.0 ** -t}
         eng.close()
     return res

@@ -12,6 +12,12 @@
 // copy, run freivalds_check once per sign vector (the check fails if any vector rejects) and return
 // the slot. When every slot is in use, submit waits for a worker (back pressure), so the ring bounds
 // both host memory and how far the checks may trail the GPU.
+//
+// A worker learns that its slot's copy has landed from the slot's flag: a word of pinned host memory
+// that a small kernel on the engine's stream sets to the slot's sequence number after the copy. The
+// worker polls that word (no runtime call on the way, so the workers never contend with the thread
+// that launches the decode kernels) and falls back to the slot's event, which also reports a failed
+// copy, only when the flag is late.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,6 +50,9 @@ struct Slot {
     uint16_t* x_dev = nullptr; // the same memory as the GPU addresses it
     float* y_dev = nullptr;
     hipEvent_t done = nullptr; // the copies into this slot have landed
+    uint32_t* flag = nullptr;  // pinned; set to seq on the engine's stream once the copy has landed
+    uint32_t* flag_dev = nullptr;
+    uint32_t seq = 0;          // sequence number of the submit that filled the slot
     int matrix = -1;
     int64_t token = 0;
     bool device = true;        // false: filled from host memory by ggo_cert_submit_host
@@ -58,6 +67,8 @@ struct ggo_cert {
     std::mutex submit_mu;              // one submit at a time uses ready_evt
     hipStream_t copy_stream = nullptr;
     hipEvent_t ready_evt = nullptr;    // recorded on the caller's stream, waited on by copy_stream
+    uint32_t* flags = nullptr;         // pinned, one 64-byte line per slot (Slot::flag)
+    uint32_t next_seq = 0;             // under submit_mu
     std::vector<Matrix> mats;
     std::vector<Slot> slots;
     std::mutex mu;
@@ -68,12 +79,29 @@ struct ggo_cert {
     std::vector<std::thread> workers;
     // statistics (under mu)
     int64_t submitted = 0, checked = 0, failed = 0;
-    double max_ratio = 0.0, check_seconds = 0.0;
+    double max_ratio = 0.0, check_seconds = 0.0, wait_seconds = 0.0, submit_wait_seconds = 0.0;
     std::vector<std::pair<int64_t, int>> failures;   // (token, matrix), oldest first
     int copy_error = 0;
 };
 
 namespace {
+
+using Clock = std::chrono::steady_clock;
+
+// Wait until the copy into slot s has landed. Poll the slot's flag, yielding the core between looks,
+// for up to POLL; past that (a copy stuck behind a long kernel, or one that failed) block on the
+// slot's event, which returns the copy's error if there is one.
+bool wait_copy(Slot& s) {
+    constexpr auto POLL = std::chrono::milliseconds(2);
+    const auto t0 = Clock::now();
+    for (;;) {
+        if (__atomic_load_n(s.flag, __ATOMIC_ACQUIRE) == s.seq) return true;
+        if (Clock::now() - t0 > POLL) break;
+        std::this_thread::yield();
+    }
+    if (hipEventSynchronize(s.done) != hipSuccess) return false;
+    return __atomic_load_n(s.flag, __ATOMIC_ACQUIRE) == s.seq;
+}
 
 void worker_loop(ggo_cert* c) {
     std::vector<double> out(4 * FREIVALDS_MAX_T);
@@ -88,11 +116,13 @@ void worker_loop(ggo_cert* c) {
         }
         Slot& sl = c->slots[id];
         bool copy_ok = true;
-        if (sl.device) copy_ok = hipEventSynchronize(sl.done) == hipSuccess;
+        const auto tw = Clock::now();
+        if (sl.device) copy_ok = wait_copy(sl);
         const Matrix& m = c->mats[sl.matrix];
         bool pass = true;
         double worst = 0.0;
-        const auto t0 = std::chrono::steady_clock::now();
+        const auto t0 = Clock::now();
+        const double waited = std::chrono::duration<double>(t0 - tw).count();
         if (copy_ok) {
             // all sign vectors in one pass over the row (up to FREIVALDS_MAX_T at a time)
             for (int v0 = 0; v0 < m.nr; v0 += FREIVALDS_MAX_T) {
@@ -106,11 +136,12 @@ void worker_loop(ggo_cert* c) {
                     if (out[4 * v + 1] > 0.0) worst = std::max(worst, out[4 * v] / out[4 * v + 1]);
             }
         }
-        const double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+        const double dt = std::chrono::duration<double>(Clock::now() - t0).count();
         {
             std::lock_guard<std::mutex> lk(c->mu);
             c->checked += 1;
             c->check_seconds += dt;
+            c->wait_seconds += waited;
             if (!copy_ok) c->copy_error = 1;
             if (!pass || !copy_ok) {
                 c->failed += 1;
@@ -129,7 +160,11 @@ void worker_loop(ggo_cert* c) {
 // Take a free slot, waiting for a worker to return one if the ring is full.
 int take_slot(ggo_cert* c) {
     std::unique_lock<std::mutex> lk(c->mu);
-    c->cv_free.wait(lk, [&] { return !c->free_slots.empty(); });
+    if (c->free_slots.empty()) {
+        const auto t0 = Clock::now();
+        c->cv_free.wait(lk, [&] { return !c->free_slots.empty(); });
+        c->submit_wait_seconds += std::chrono::duration<double>(Clock::now() - t0).count();
+    }
     const int id = c->free_slots.front();
     c->free_slots.pop_front();
     c->in_flight += 1;
@@ -162,6 +197,34 @@ __global__ void k_cert_gather(GatherArgs a) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < s.count;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
         s.dst[i] = s.src[i];
+    __threadfence_system();   // this thread's writes reach host memory before the kernel ends
+}
+
+// Runs after the copies of a batch on the engine's stream: sets each slot's flag to its sequence
+// number (a release store to host memory, read by the workers with an acquire load).
+struct FlagArgs {
+    uint32_t* flag[MAX_BATCH];
+    uint32_t seq[MAX_BATCH];
+    int n;
+};
+
+__global__ void k_cert_flags(FlagArgs a) {
+    const int i = threadIdx.x;
+    if (i < a.n) __hip_atomic_store(a.flag[i], a.seq[i], __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Queue the flag kernel for slots sid[0 .. n) on the engine's stream, then each slot's event.
+hipError_t mark_landed(ggo_cert* c, const int* sid, int64_t n) {
+    FlagArgs fa{};
+    fa.n = static_cast<int>(n);
+    for (int64_t i = 0; i < n; ++i) {
+        fa.flag[i] = c->slots[sid[i]].flag_dev;
+        fa.seq[i] = c->slots[sid[i]].seq;
+    }
+    hipLaunchKernelGGL(k_cert_flags, dim3(1), dim3(64), 0, c->copy_stream, fa);
+    hipError_t e = hipGetLastError();
+    for (int64_t i = 0; i < n && e == hipSuccess; ++i) e = hipEventRecord(c->slots[sid[i]].done, c->copy_stream);
+    return e;
 }
 
 inline double widen(uint16_t b) {
@@ -187,6 +250,20 @@ static int create(int64_t max_K, int64_t max_N, int64_t nslots, int nworkers, do
     c->host_only = host_only;
     c->slots.resize(static_cast<size_t>(nslots));
     int rc = GGO_OK;
+    uint32_t* flags_dev = nullptr;
+    if (!host_only) {
+        constexpr size_t LINE = 64 / sizeof(uint32_t);   // one flag per 64-byte line
+        if (hipHostMalloc(reinterpret_cast<void**>(&c->flags), static_cast<size_t>(nslots) * 64) != hipSuccess ||
+            hipHostGetDevicePointer(reinterpret_cast<void**>(&flags_dev), c->flags, 0) != hipSuccess) {
+            rc = GGO_ELAUNCH;
+        } else {
+            std::memset(c->flags, 0, static_cast<size_t>(nslots) * 64);
+            for (int64_t i = 0; i < nslots; ++i) {
+                c->slots[i].flag = c->flags + i * LINE;
+                c->slots[i].flag_dev = flags_dev + i * LINE;
+            }
+        }
+    }
     for (int64_t i = 0; i < nslots && rc == GGO_OK; ++i) {
         Slot& s = c->slots[i];
         if (host_only) {
@@ -265,12 +342,13 @@ int ggo_cert_submit(ggo_cert* c, int id, const uint16_t* x_dev, const float* y_d
     s.matrix = id;
     s.token = token;
     s.device = true;
+    s.seq = ++c->next_seq;
     hipStream_t caller = static_cast<hipStream_t>(stream);
     hipError_t e = hipEventRecord(c->ready_evt, caller);
     if (e == hipSuccess) e = hipStreamWaitEvent(c->copy_stream, c->ready_evt, 0);
     if (e == hipSuccess) e = hipMemcpyAsync(s.x, x_dev, static_cast<size_t>(m.K) * 2, hipMemcpyDeviceToHost, c->copy_stream);
     if (e == hipSuccess) e = hipMemcpyAsync(s.y, y_dev, static_cast<size_t>(m.N) * 4, hipMemcpyDeviceToHost, c->copy_stream);
-    if (e == hipSuccess) e = hipEventRecord(s.done, c->copy_stream);
+    if (e == hipSuccess) e = mark_landed(c, &sid, 1);
     if (e != hipSuccess) {
         std::lock_guard<std::mutex> lk(c->mu);
         c->free_slots.push_back(sid);
@@ -299,6 +377,7 @@ int ggo_cert_submit_rows(ggo_cert* c, int64_t n, const int* ids, const uint16_t*
         s.matrix = ids[i];
         s.token = token;
         s.device = true;
+        s.seq = ++c->next_seq;
         ga.seg[2 * i] = GatherSeg{x_dev[i], s.x_dev, m.K};
         ga.seg[2 * i + 1] = GatherSeg{reinterpret_cast<const uint16_t*>(y_dev[i]), reinterpret_cast<uint16_t*>(s.y_dev),
                                       2 * m.N};
@@ -313,7 +392,7 @@ int ggo_cert_submit_rows(ggo_cert* c, int64_t n, const int* ids, const uint16_t*
         hipLaunchKernelGGL(k_cert_gather, dim3(bx, static_cast<unsigned>(2 * n)), dim3(256), 0, c->copy_stream, ga);
         e = hipGetLastError();
     }
-    for (int64_t i = 0; i < n && e == hipSuccess; ++i) e = hipEventRecord(c->slots[sid[i]].done, c->copy_stream);
+    if (e == hipSuccess) e = mark_landed(c, sid, n);
     if (e != hipSuccess) {
         std::lock_guard<std::mutex> lk(c->mu);
         for (int64_t i = 0; i < n; ++i) {
@@ -353,6 +432,8 @@ int ggo_cert_drain(ggo_cert* c, ggo_cert_stats* out) {
         out->max_honest_ratio = c->max_ratio;
         out->check_seconds = c->check_seconds;
         out->copy_error = c->copy_error;
+        out->wait_seconds = c->wait_seconds;
+        out->submit_wait_seconds = c->submit_wait_seconds;
     }
     return GGO_OK;
 }
@@ -387,6 +468,7 @@ void ggo_cert_destroy(ggo_cert* c) {
         if (s.y) hipHostFree(s.y);
         if (s.done) hipEventDestroy(s.done);
     }
+    if (c->flags) hipHostFree(c->flags);
     if (c->ready_evt) hipEventDestroy(c->ready_evt);
     if (c->copy_stream) hipStreamDestroy(c->copy_stream);
     delete c;

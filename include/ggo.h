@@ -328,7 +328,10 @@ const char *ggo_last_error(void);
  *   after all work already queued on `stream`; the caller's stream does not
  *   wait for the copy. The buffers must stay unchanged until that work and
  *   the copy have run. Blocks only while every slot is in use. One submit at
- *   a time (calls are serialised inside).
+ *   a time (calls are serialised inside). After the copy, a one-block kernel
+ *   on the engine's stream writes the slot's sequence number into a flag in
+ *   pinned host memory; the worker that checks the row polls that flag and
+ *   blocks on the slot's event only if the flag is more than 2 ms late.
  * ggo_cert_submit_rows: ggo_cert_submit for n <= 16 rows at once (ids[i],
  *   x_dev[i], y_dev[i]): one kernel on the engine's stream writes all of them
  *   into their pinned slots, so a token's rows cost one launch instead of two
@@ -348,6 +351,8 @@ typedef struct ggo_cert_stats {
     double max_honest_ratio;   /* largest rho / sigma over the rows that passed */
     double check_seconds;      /* host time spent in the checks */
     int copy_error;
+    double wait_seconds;        /* worker time spent waiting for the rows' copies to land */
+    double submit_wait_seconds; /* submit time spent waiting for a free slot (back pressure) */
 } ggo_cert_stats;
 
 int ggo_cert_create(int64_t max_K, int64_t max_N, int64_t slots, int workers, double c_f, ggo_cert **out);
