@@ -663,6 +663,7 @@ def main():
     for M in ms:
         rec = {}
         for name, fn in (("tree", lambda i: g.gemv_tree(dx[:M], dWTs[i % copies], y=ys[M])),
+                         ("mfma", lambda i: g.gemv_mfma_invariant(dx[:M], dWTs[i % copies], y=ys[M])),
                          ("ordered", lambda i: g.gemv_ordered(dx[:M], dWs[i % copies], y=ys[M])),
                          ("hipblaslt", lambda i: torch.mm(dx[:M], dWTs[i % copies].t(), out_dtype=torch.float32))):
             try:

@@ -71,6 +71,8 @@ def _load():
     lib.gemm_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.ggo_test_gemm_mfma_tile128.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant_wt.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemv_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemv_mfma_invariant_ep.argtypes = [P, I64, P, I64, ct.POINTER(Epilogue), P, I64, I64, I64, I64, P]
     lib.freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     PP = ct.POINTER(ct.c_void_p)
@@ -92,7 +94,7 @@ def _load():
     lib.ggo_last_error.restype = ct.c_char_p
     for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
               "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
-              "ggo_test_gemm_mfma_tile128", "gemm_mfma_invariant_wt", "freivalds_prepare", "freivalds_check"):
+              "ggo_test_gemm_mfma_tile128", "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep", "freivalds_prepare", "freivalds_check"):
         getattr(lib, f).restype = I
     return lib
 
@@ -101,7 +103,7 @@ lib = _load()
 
 EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
            "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
-           "gemm_mfma_invariant_wt",
+           "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep",
            "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error",
            "ggo_cert_create", "ggo_cert_create_host", "ggo_cert_add_matrix", "ggo_cert_submit", "ggo_cert_submit_rows",
            "ggo_cert_submit_host",
@@ -227,6 +229,37 @@ def gemv_tree(x, WT, y=None, stream=None):
     ldy = _rowmajor(y, "y") if M and N else N
     _raise(lib.gemv_tree(x.data_ptr(), ldx, WT.data_ptr(), ldwt, y.data_ptr(), ldy, M, N, K, _stream(stream)),
            "gemv_tree")
+    return y
+
+
+def gemv_mfma_invariant(x, WT, y=None, stream=None):
+    """y = x W for x bf16 [M <= 16, K] and the weight given transposed, WT bf16 [N, K], on the matrix cores:
+    the bits of gemm_mfma_invariant(x, W) for every row and every M. Needs 16-byte aligned operands with
+    row strides and K multiples of 8."""
+    ldx, ldwt = _rowmajor(x, "x"), _rowmajor(WT, "WT")
+    M, K = x.shape
+    if not (_is_bf16(x) and _is_bf16(WT)) or WT.shape[1] != K:
+        raise ValueError("x and WT must be bf16, WT [N, K]")
+    N = WT.shape[0]
+    y = _out(y, M, N, x)
+    ldy = _rowmajor(y, "y") if M and N else N
+    _raise(lib.gemv_mfma_invariant(x.data_ptr(), ldx, WT.data_ptr(), ldwt, y.data_ptr(), ldy, M, N, K,
+                                   _stream(stream)), "gemv_mfma_invariant")
+    return y
+
+
+def gemv_mfma_invariant_ep(x, WT, bias=None, act="none", residual=None, out="f32", y=None, stream=None):
+    """gemv_mfma_invariant followed, in the same kernel, by y = act(y + bias) + residual (fixed order), stored
+    as float32 or bfloat16 (out='bf16')."""
+    ldx, ldwt = _rowmajor(x, "x"), _rowmajor(WT, "WT")
+    M, K = x.shape
+    if not (_is_bf16(x) and _is_bf16(WT)) or WT.shape[1] != K:
+        raise ValueError("x and WT must be bf16, WT [N, K]")
+    N = WT.shape[0]
+    e, y, keep = _epilogue(M, N, x, bias, act, residual, out, y)
+    ldy = _rowmajor(y, "y") if M and N else N
+    _raise(lib.gemv_mfma_invariant_ep(x.data_ptr(), ldx, WT.data_ptr(), ldwt, ct.byref(e), y.data_ptr(), ldy, M, N,
+                                      K, _stream(stream)), "gemv_mfma_invariant_ep")
     return y
 
 

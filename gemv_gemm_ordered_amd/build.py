@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libggo.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["ordered_gemm.hip", "ordered_gemv.hip", "tree_gemv.hip", "mfma_invariant.hip", "capi.cpp", "freivalds.cpp", "cert_runtime.cpp"]
+SOURCES = ["ordered_gemm.hip", "ordered_gemv.hip", "tree_gemv.hip", "mfma_invariant.hip", "mfma_gemv.hip", "capi.cpp", "freivalds.cpp", "cert_runtime.cpp"]
 HEADERS = ["common.hpp", "kernels.hpp", "epilogue.hpp", os.path.join("..", "..", "include", "ggo.h")]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -367,6 +367,50 @@ int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, i
     return launched(fn, launch_gemm_mfma_invariant_wt(a, s));
 }
 
+static int run_gemv_mfma(const char* fn, const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, void* y,
+                         int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s, const Epi& ep) {
+    int rc = check_mnk(fn, M, N, K);
+    if (rc) return rc;
+    if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d", fn, (long long)M, GGO_GEMV_MAX_M);
+    if (M == 0 || N == 0) return ok();
+    if (!y || (K && (!x || !WT))) return fail(GGO_EINVAL, "%s: null pointer", fn);
+    if (ldx < K || ldwt < K || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
+    if (K == 0) return launched(fn, epi_zero(y, ldy, M, N, ep, s));
+    // 16-byte chunks through range-checked row descriptors: no chunk may straddle the end of a row
+    if (!aligned(x, 16) || ldx % 8 || !aligned(WT, 16) || ldwt % 8 || K % 8)
+        return fail(GGO_EUNSUPPORTED,
+                    "%s: x and W^T must be 16-byte aligned with row strides and K multiples of 8 "
+                    "(gemm_mfma_invariant takes any operands and gives the same bits)", fn);
+    if (K > gemv_mfma_max_k())
+        return fail(GGO_EUNSUPPORTED, "%s: K=%lld too large for 32-bit byte offsets along a row", fn, (long long)K);
+    GemvMfmaArgs a;
+    a.x = x;
+    a.WT = WT;
+    a.y = y;
+    a.ldx = ldx;
+    a.ldwt = ldwt;
+    a.ldy = ldy;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.ep = ep;
+    return launched(fn, launch_gemv_mfma(a, s));
+}
+
+int gemv_mfma_invariant(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy,
+                        int64_t M, int64_t N, int64_t K, void* stream) {
+    return run_gemv_mfma("gemv_mfma_invariant", x, ldx, WT, ldwt, y, ldy, M, N, K, static_cast<hipStream_t>(stream),
+                         no_epi());
+}
+
+int gemv_mfma_invariant_ep(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, const ggo_epilogue* ep,
+                           void* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+    Epi e;
+    int rc = make_epi("gemv_mfma_invariant_ep", ep, N, &e);
+    if (rc) return rc;
+    return run_gemv_mfma("gemv_mfma_invariant_ep", x, ldx, WT, ldwt, y, ldy, M, N, K, static_cast<hipStream_t>(stream), e);
+}
+
 int ggo_test_gemm_mfma_tile128(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                                int64_t M, int64_t N, int64_t K, void* stream) {
     return run_mfma("ggo_test_gemm_mfma_tile128", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), true, no_epi());

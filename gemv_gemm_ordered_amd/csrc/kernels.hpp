@@ -73,3 +73,14 @@ void mfma_tile_shape_t128(int* bm, int* bn);   // 128x128 instance (any operands
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_t128(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream);   // W given as W^T [N, K]
+
+struct GemvMfmaArgs {
+    const uint16_t* x;
+    const uint16_t* WT;
+    void* y;          // binary32, or bfloat16 when ep.out_bf16
+    int64_t ldx, ldwt, ldy;
+    int32_t M, N, K;
+    Epi ep;
+};
+hipError_t launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t stream);   // 16-byte operands, K % 8 == 0
+int gemv_mfma_max_k();   // byte offsets along a row are 32-bit

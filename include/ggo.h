@@ -252,6 +252,46 @@ int gemm_mfma_invariant_wt(const uint16_t *A, int64_t lda,
                            int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * gemv_mfma_invariant -- decode GEMV on the matrix cores with the bits of
+ * gemm_mfma_invariant: y = x W for M <= GGO_GEMV_MAX_M rows, the weight given
+ * transposed as for gemv_tree (WT [N, K], k contiguous).
+ * Source: "Taming Bitwise Behavior in GPU Kernels with Tensor Core", sections
+ * 3.2.1 and 3.2.2: on a matrix-instruction path an output's bits are fixed by
+ * the opcode, the way the accumulator is carried between instructions and the
+ * placement of the last short group of K, not by the tile. This entry keeps
+ * gemm_mfma_invariant's three (one v_mfma_f32_16x16x32_bf16 per 32 k in
+ * ascending order from k = 0, the binary32 accumulator carried through the
+ * instruction from +0, k >= K fed as zeros), so
+ *     gemv_mfma_invariant(x, W^T) == gemm_mfma_invariant(x, W)
+ * bit for bit, for every row and every M: a decode step gives the bits a
+ * prefill of the same rows gives. One workgroup owns 16 consecutive outputs
+ * and runs their whole k chain; no split of K, no workspace, no atomics.
+ *   x   device, [M, K] bfloat16 bits, row stride ldx >= K
+ *   WT  device, [N, K] bfloat16 bits, row stride ldwt >= K
+ *   y   device, [M, N] binary32, row stride ldy >= N; written, never read
+ *   x and WT 16-byte aligned, ldx % 8 == 0, ldwt % 8 == 0, K % 8 == 0 (no
+ *   16-byte chunk may straddle the end of a row), K <= 2^29 - 2560; else
+ *   GGO_EUNSUPPORTED (gemm_mfma_invariant takes any operands, same bits).
+ *   0 <= M <= GGO_GEMV_MAX_M (M = 0 or N = 0: no-op; K = 0: y = +0).
+ * Asynchronous on `stream`.
+ */
+int gemv_mfma_invariant(const uint16_t *x, int64_t ldx,
+                        const uint16_t *WT, int64_t ldwt,
+                        float *y, int64_t ldy,
+                        int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * gemv_mfma_invariant_ep -- gemv_mfma_invariant with the fused epilogue `ep`
+ * (NULL = none); y is binary32 or bfloat16 as ep->out_dtype says. The fold's
+ * bits are gemv_mfma_invariant's (and gemm_mfma_invariant_ep's with the same
+ * epilogue).
+ */
+int gemv_mfma_invariant_ep(const uint16_t *x, int64_t ldx,
+                           const uint16_t *WT, int64_t ldwt,
+                           const ggo_epilogue *ep, void *y, int64_t ldy,
+                           int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * ggo_test_gemm_mfma_tile128 -- test hook, not a production entry point: the
  * gemm_mfma_invariant descriptor executed by its second tile instance
  * (128x128 outputs per workgroup instead of 256x128), for any operands. The
