@@ -12,16 +12,21 @@
 // Shape. One instruction covers 16 outputs n (its A rows: weight rows) by 16 rows m of x (its B
 // columns), so a workgroup owns one block of 16 consecutive n and runs the whole k chain of that
 // block in one wave; with no split of K there are N / 16 chains, one workgroup each (256 for a
-// 4096-wide weight, one per CU). Eight more waves exist to keep the weight stream in flight: the
-// block's 16 weight rows (and the MT staged rows of x) move HBM -> LDS with direct-to-LDS 16-byte
-// loads, one 1 KiB contiguous run of one row per load instruction, through a ring of NST stages of
-// 512 k. Per stage every producer waits for its own loads, the workgroup meets at one barrier, the
-// stage NST - 1 ahead is requested into the buffer freed by the previous stage, and wave 0, which
-// issues no loads, folds
-// the stage's 16 groups: a chain of 16 dependent MFMAs (one wave issues them back to back at the
-// instruction's full rate, about 7.6 ns each), with the fragment reads running a few groups ahead.
-// Measured with loads only, this shape streams a 32 MiB weight in about
-// 6.6 us with 8 waves (7.0 us with 4).
+// 4096-wide weight, one per CU). Eight producer waves keep the weight stream in flight: the block's
+// 16 weight rows (and the MT staged rows of x) move HBM -> LDS with direct-to-LDS 16-byte loads, one
+// 1 KiB contiguous run of one row per load instruction, through a ring of NST stages of 512 k. Per
+// stage every producer waits for its own loads, the workgroup meets at one barrier, the stage
+// NST - 1 ahead is requested into the buffer freed by the previous stage, and wave 0 folds the
+// stage: its 32 fragment reads, then a chain of 16 dependent MFMAs (one wave issues them back to
+// back at the instruction's full rate, about 7.6 ns each).
+//
+// Wave 0 issues no loads of its own. The compiler puts a wait for every outstanding load before
+// each LDS read that might alias a direct-to-LDS load still in flight; a wave that also loaded would
+// wait there for the stages requested ahead, which drained the pipeline every stage (1 us per call).
+//
+// Measured on the 4096 x 4096 decode weight: loads and barriers alone take 7.3 us per call, the fold
+// alone 2.3 us, a launch with barriers only 2.3 us, the whole kernel 7.8 - 8.0 us at M = 1 ... 8.
+// Four producers or a ring of 3 or 6 stages were slower.
 //
 // LDS layout: a row's 64 chunks of 16 bytes are stored with chunk c at slot c xor (row mod 16),
 // by letting the lane that fills slot l fetch chunk l xor (row mod 16); the fragment reads (lane l
@@ -107,33 +112,27 @@ GGO_DEV void wait_stage(int p) {
     else wait_vm<RW * (NST - 2)>();
 }
 
-// Wave 0's fold of one stage: the stage's chain of 16 MFMAs, groups in ascending k, with the fragment
-// reads running AHEAD groups in front of it (each MFMA is followed by the reads of group g + AHEAD, which
-// land while the chain runs). xrow is this lane's row of x in the stage, or a row of zeros for lanes
-// whose row is not staged (l mod 16 >= MT). TAIL: the last stage, whose groups from gmax on lie wholly
-// past K and are skipped.
-constexpr int AHEAD = 4;
-
+// Wave 0's fold of one stage: every fragment read of the stage first, then its chain of 16 MFMAs,
+// groups in ascending k (the chain waits for each group's reads as they land; reading a few groups ahead
+// of each MFMA instead measured 0.1 us slower per call). xrow is this lane's row of x in the stage, or a
+// row of zeros for lanes whose row is not staged (l mod 16 >= MT). TAIL: the last stage, whose groups
+// from gmax on lie wholly past K and are skipped.
 template <bool TAIL>
 GGO_DEV void fold_stage(const uint16_t* __restrict__ wrow, const uint16_t* __restrict__ xrow, int c, int gmax,
                         f32x4& acc) {
     bf16x8 wf[GROUPS], xf[GROUPS];
     // chunk 4g + l/16 of a row sits at slot (4g + l/16) xor (l mod 16) = 4g xor c, c = (l/16) xor (l mod 16)
-    auto read = [&](int g) {
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) {
         if (!TAIL || g < gmax) {
             wf[g] = *reinterpret_cast<const bf16x8*>(wrow + ((4 * g) ^ c) * 8);
             xf[g] = *reinterpret_cast<const bf16x8*>(xrow + ((4 * g) ^ c) * 8);
         }
-    };
-#pragma unroll
-    for (int g = 0; g < AHEAD; ++g) read(g);
-#pragma unroll
-    for (int g = 0; g < GROUPS; ++g) {
-        if (g + AHEAD < GROUPS) read(g + AHEAD);
-        __builtin_amdgcn_sched_barrier(0);   // keep this order: reads of g + AHEAD, then MFMA g
-        if (!TAIL || g < gmax) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[g], xf[g], acc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the chain
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g)
+        if (!TAIL || g < gmax) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[g], xf[g], acc, 0, 0, 0);
 }
 
 template <int MT, bool EPI>

@@ -52,7 +52,8 @@ def code():
     if not os.path.isdir(BUILD):
         pytest.skip("library not built")
     return {src: disassemble(os.path.join(BUILD, src + ".o"))
-            for src in ("ordered_gemm.hip", "ordered_gemv.hip", "tree_gemv.hip", "mfma_invariant.hip", "capi.cpp")}
+            for src in ("ordered_gemm.hip", "ordered_gemv.hip", "tree_gemv.hip", "mfma_invariant.hip", "mfma_gemv.hip",
+                        "capi.cpp")}
 
 
 def test_ordered_kernels_have_no_contraction(code):
@@ -100,6 +101,12 @@ def test_mfma_kernels_use_one_opcode(code):
     for k in ks:
         ops = {m.group(1) for line in code["mfma_invariant.hip"][k] for m in [MFMA.search(line)] if m}
         assert ops == {"v_mfma_f32_16x16x32_bf16"}, (k, ops)
+    # the matrix-core GEMV: staged x rows 1, 2, 4, 8, 16 x with / without the epilogue
+    ks = [k for k in code["mfma_gemv.hip"] if "k_gemv_mfma" in k]
+    assert len(ks) == 10, ks
+    for k in ks:
+        ops = {m.group(1) for line in code["mfma_gemv.hip"][k] for m in [MFMA.search(line)] if m}
+        assert ops == {"v_mfma_f32_16x16x32_bf16"}, (k, ops)
 
 
 def test_no_atomics_anywhere(code):
@@ -115,7 +122,8 @@ def test_hot_kernels_use_no_scratch(code):
     example an accumulator array indexed with a runtime value -- and it turns every matrix
     instruction into a memory round trip while the results stay correct."""
     scratch = re.compile(r"\b(scratch_\w+|buffer_(?:load|store)_\w+ [^;]*\boff, s\[0:3\])")
-    for src, tag in (("mfma_invariant.hip", "k_gemm_mfma"), ("tree_gemv.hip", "k_gemv_tree")):
+    for src, tag in (("mfma_invariant.hip", "k_gemm_mfma"), ("tree_gemv.hip", "k_gemv_tree"),
+                     ("mfma_gemv.hip", "k_gemv_mfma")):
         ks = [k for k in code[src] if tag in k]
         assert ks, src
         for k in ks:
