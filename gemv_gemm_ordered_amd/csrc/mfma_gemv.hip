@@ -24,17 +24,15 @@
 // each LDS read that might alias a direct-to-LDS load still in flight; a wave that also loaded would
 // wait there for the stages requested ahead, which drained the pipeline every stage (1 us per call).
 //
-// Measured on the 4096 x 4096 decode weight: loads and barriers alone take 7.3 us per call, the fold
-// alone 2.3 us, a launch with barriers only 2.3 us, the whole kernel 7.8 - 8.0 us at M = 1 ... 8.
-// Four producers or a ring of 3 or 6 stages were slower.
+// Measured on the 4096 x 4096 decode weight: loads and barriers alone take 7.3 us per call, the whole
+// kernel 7.8 - 8.0 us at M = 1 ... 8. Four producers or a ring of 3 or 6 stages were slower.
 //
 // LDS layout: a row's 64 chunks of 16 bytes are stored with chunk c at slot c xor (row mod 16),
 // by letting the lane that fills slot l fetch chunk l xor (row mod 16); the fragment reads (lane l
 // reads chunk 4g + l / 16 of row l mod 16) then fall on 16 distinct bank groups.
 //
 // Range: one raw buffer descriptor per row whose range is exactly K elements (empty for rows past
-// M or N), so loads past K -- including whole stages past the end -- write zeros without touching
-// memory. Operands must be 16-byte aligned with row strides and K multiples of 8, so no 16-byte
+// M or N), so loads past K write zeros without touching memory; no stage past the last is requested. Operands must be 16-byte aligned with row strides and K multiples of 8, so no 16-byte
 // chunk straddles the end of a row.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -101,15 +99,24 @@ GGO_DEV void issue_stage(const GemvMfmaArgs& a, int64_t n0, int p, int lane, int
     }
 }
 
-// Wait until producer p's loads of the current stage have landed, the stages requested after it
-// (NST - 2 of them) may stay in flight. Loads per stage differ between producers (rows of x), so the
-// count is chosen per producer; the branch is uniform within a wave.
-template <int MT>
-GGO_DEV void wait_stage(int p) {
+// Wait until producer p's loads of the current stage have landed; the `ahead` stages requested after
+// it (NST - 2 in the steady state, fewer near the end, where nothing past the last stage is requested)
+// may stay in flight. Loads per stage differ between producers (rows of x), so the count is chosen per
+// producer; the branches are uniform within a wave.
+template <int MT, int AHEAD>
+GGO_DEV void wait_ahead(int p) {
     using R = Ring<MT>;
     constexpr int LX = (MT < PRODUCERS ? 1 : R::XROWS_PER_WAVE);
-    if (p < MT) wait_vm<(RW + LX) * (NST - 2)>();
-    else wait_vm<RW * (NST - 2)>();
+    if (p < MT) wait_vm<(RW + LX) * AHEAD>();
+    else wait_vm<RW * AHEAD>();
+}
+
+template <int MT>
+GGO_DEV void wait_stage(int p, int ahead) {
+    static_assert(NST == 4, "the cases below cover up to NST - 2 = 2 stages ahead");
+    if (ahead >= 2) wait_ahead<MT, 2>(p);
+    else if (ahead == 1) wait_ahead<MT, 1>(p);
+    else wait_ahead<MT, 0>(p);
 }
 
 // Wave 0's fold of one stage: every fragment read of the stage first, then its chain of 16 MFMAs,
@@ -149,7 +156,8 @@ __global__ __launch_bounds__(THREADS) void k_gemv_mfma(const GemvMfmaArgs a) {
     const int p = wave - 1;   // producer index (wave 0 is the consumer)
     if (wave > 0) {
 #pragma unroll
-        for (int s = 0; s < NST - 1; ++s) issue_stage<MT>(a, n0, p, lane, s, ring + s * R::STAGE);
+        for (int s = 0; s < NST - 1; ++s)
+            if (s < stages) issue_stage<MT>(a, n0, p, lane, s, ring + s * R::STAGE);
     }
 
     if (MT < 16)   // read by wave 0 only after the first barrier below
@@ -157,14 +165,15 @@ __global__ __launch_bounds__(THREADS) void k_gemv_mfma(const GemvMfmaArgs a) {
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const int lr = lane & 15, lq = lane >> 4, c = lq ^ lr;
     for (int s = 0; s < stages; ++s) {
-        if (wave > 0) wait_stage<MT>(p);
+        if (wave > 0) wait_stage<MT>(p, min(NST - 2, stages - 1 - s));
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): wave 0's reads of the previous stage are done
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
         if (wave > 0) {
-            // the buffer of stage s - 1 is free: request stage s + NST - 1 into it (past the end: zeros)
-            issue_stage<MT>(a, n0, p, lane, s + NST - 1, ring + ((s + NST - 1) % NST) * R::STAGE);
+            // the buffer of stage s - 1 is free: request stage s + NST - 1 into it
+            if (s + NST - 1 < stages)
+                issue_stage<MT>(a, n0, p, lane, s + NST - 1, ring + ((s + NST - 1) % NST) * R::STAGE);
         } else {
             // wave 0 has no loads of its own in flight, so the wait for outstanding loads that the
             // compiler puts before these LDS reads (it cannot tell the direct-to-LDS loads of later
@@ -176,8 +185,6 @@ __global__ __launch_bounds__(THREADS) void k_gemv_mfma(const GemvMfmaArgs a) {
             else fold_stage<true>(wrow, xrow, c, groups - s * GROUPS, acc);
         }
     }
-    // the loads of the stages past the end (empty ranges) have landed before the wave ends
-    if (wave > 0) wait_vm<0>();
     if (wave == 0) {
         // lane l holds D[4 (l / 16) + r][l mod 16]: outputs n0 + 4 (l / 16) + r of row m = l mod 16
         const int m = lr;
