@@ -426,10 +426,10 @@ def traffic_summary(fetch_dir, write_dir):
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
     lines = ["# k_gemv_tree_p — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
-             "Commands (from the repository root, on one MI355X):", "",
-             "    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/traffic_fetch -o run -- python3 $REPO/bench.py --counters",
-             "    cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/traffic_write -o run -- python3 $REPO/bench.py --counters",
-             "    python3 bench.py --traffic-summary gpurun_out/traffic_fetch gpurun_out/traffic_write", "",
+             "Commands (from the repository root $REPO, on one MI355X; $OUT is any directory for the profiler's output):", "",
+             "    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic_fetch -o run -- python3 $REPO/bench.py --counters",
+             "    cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/traffic_write -o run -- python3 $REPO/bench.py --counters",
+             "    python3 bench.py --traffic-summary $OUT/traffic_fetch $OUT/traffic_write", "",
              f"Calibration: a plain elementwise copy of {COPY_BYTES >> 20} MiB (reads and writes {COPY_BYTES} "
              f"bytes) reads FETCH_SIZE = {out['FETCH_SIZE']['copy_counter_kib']:.0f} KiB and WRITE_SIZE = "
              f"{out['WRITE_SIZE']['copy_counter_kib']:.0f} KiB, so one counted KiB is "
@@ -467,7 +467,7 @@ def traffic_per_launch(ms):
 
 
 
-# Utilisation counters of the three kinds of kernel (the spec evidence for the design choices):
+# Utilisation counters of the three kinds of kernel (the counter evidence for their design choices):
 # the MFMA GEMM at 4096^3, the ordered GEMM at the MLP up-projection (M = 2048), the tree GEMV at M = 8.
 # `--counters-kernels` runs KERNEL_REPS launches of each; two rocprofv3 passes collect the counters:
 #   rocprofv3 --pmc MfmaUtil SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_LDS_BANK_CONFLICT ...
@@ -524,11 +524,11 @@ def kernel_counter_summary(dir1, dir2):
                     dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
                     rec.setdefault("_dur", []).append(dur)
     lines = ["# Utilisation counters of the MFMA GEMM, the ordered GEMM and the tree GEMV", "",
-             "Commands (from the repository root, on one MI355X):", ""]
+             "Commands (from the repository root $REPO, on one MI355X; $OUT is any directory for the profiler's output):", ""]
     for i, p in enumerate(KERNEL_PASSES, 1):
-        lines.append(f"    cd /tmp && rocprofv3 --pmc {' '.join(p)} --output-format csv -d $REPO/gpurun_out/kcount{i} -o run "
+        lines.append(f"    cd /tmp && rocprofv3 --pmc {' '.join(p)} --output-format csv -d $OUT/kcount{i} -o run "
                      "-- python3 $REPO/bench.py --counters-kernels")
-    lines += ["    python3 bench.py --kernel-counter-summary gpurun_out/kcount1 gpurun_out/kcount2", "",
+    lines += ["    python3 bench.py --kernel-counter-summary $OUT/kcount1 $OUT/kcount2", "",
               f"Medians over {KERNEL_REPS} launches of each kernel. `MfmaUtil` and `VALUBusy` are rocprofv3's "
               "derived metrics (matrix-pipe busy cycles over all SIMDs, and VALU-active cycles per CU, as a "
               "percentage of the GPU-active cycles). Binary32 VALU rate: (mul + add + fma wave instructions) x 64 "
