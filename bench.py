@@ -247,8 +247,8 @@ def paths(g, reps):
         "mfma_alone_us": round(1e3 * plain, 1), "hipblaslt_then_torch_epilogue_us": round(1e3 * blas, 1)}
     del A, W, r2
     out["certificate_decode_loop_7b_layer"] = cert_loop(g)
-    # attention value product, 32 heads, head_dim 128
-    for L in (256, 1024):
+    # attention value product, 32 heads, head_dim 128 (L = 5000: P is 3.2 GB, 204.8 GFLOP)
+    for L in (256, 1024, 5000):
         P = torch.softmax(torch.randn((32, L, L), device="cuda"), dim=-1)
         V = randn_bf16((32, L, 128), 1.0)
         O = torch.empty((32, L, 128), device="cuda")
