@@ -195,9 +195,24 @@ def paths(g, reps):
         except TypeError:
             return torch.mm(A, W)
 
+    # GPT-2-small projection, A[M,768] x W[768,768]: launch- and latency-bound, reported as time per call.
+    # gemv_ordered (M <= 16) gives gemm_ordered's bits with a decode-shaped kernel.
+    W = randn_bf16((768, 768), 0.02)
+    for M in (1, 8, 64):
+        A = randn_bf16((M, 768), 1.0)
+        rec = {}
+        fns = [("ordered", lambda i: g.gemm_ordered(A, W)), ("mfma", lambda i: g.gemm_mfma_invariant(A, W)),
+               ("hipblaslt", lambda i: mm_blaslt(A, W))]
+        if M <= 16:
+            fns.insert(1, ("gemv_ordered", lambda i: g.gemv_ordered(A, W)))
+        for name, fn in fns:
+            rec[f"{name}_us"] = round(1e3 * graph_time(fn, 32), 2)
+        out[f"gpt2_proj_M{M}_N768_K768"] = rec
+    del W, A
+
     # MLP up-projection and 7B projections: ordered VALU, MFMA invariant, hipBLASLt
     # (7b_up_shard8: one GPU's share of the up-projection's W split 8 ways along N)
-    shapes = [("mlp_up", 256, 4096, 1024), ("mlp_up", 2048, 4096, 1024),
+    shapes = [("mlp_up", m, 4096, 1024) for m in (64, 128, 256, 512, 1024, 2048)] + [
               ("7b_qkvo", 4096, 4096, 4096), ("7b_up", 4096, 11008, 4096), ("7b_up_shard8", 4096, 1376, 4096)]
     for name, M, N, K in shapes:
         A = randn_bf16((M, K), 1.0)
