@@ -278,6 +278,21 @@ def paths(g, reps):
         "mfma_alone_us": round(1e3 * plain, 1), "hipblaslt_then_torch_epilogue_us": round(1e3 * blas, 1)}
     del A, W, r2
     out["certificate_decode_loop_7b_layer"] = cert_loop(g)
+    # decode GEMVs at the other projection shapes of a 7B layer (weight as W^T [N, K], 8 rotated copies so
+    # that each launch streams its weight from HBM): tree order, the matrix-core GEMV, hipBLASLt
+    for N, K in ((11008, 4096), (4096, 11008)):
+        WTs = [randn_bf16((N, K), 0.02) for _ in range(8)]
+        for M in (1, 8):
+            x = randn_bf16((M, K), 1.0)
+            rec = {}
+            for name, fn in (("tree", lambda i: g.gemv_tree(x, WTs[i % 8])),
+                             ("mfma", lambda i: g.gemv_mfma_invariant(x, WTs[i % 8])),
+                             ("hipblaslt", lambda i: mm_blaslt(x, WTs[i % 8].t()))):
+                t = graph_time(fn, 32)
+                rec[f"{name}_us"] = round(1e3 * t, 2)
+                rec[f"{name}_GBps"] = round(gemv_bytes(M, K, N) / t / 1e6, 1)
+            out[f"decode_gemv_M{M}_N{N}_K{K}"] = rec
+        del WTs
     # attention value product, 32 heads, head_dim 128 (L = 5000: P is 3.2 GB, 204.8 GFLOP)
     for L in (256, 1024, 5000):
         P = torch.softmax(torch.randn((32, L, L), device="cuda"), dim=-1)
