@@ -73,3 +73,28 @@ def test_batched_rows_catch_exactly_the_planted_faults(g):
     assert st["submitted"] == st["checked"] == 90 and not st["copy_error"]
     assert set(eng.failures()) == planted
     eng.close()
+
+
+def test_late_copy_takes_the_event_path(g):
+    """A row whose copy waits behind a long kernel on the caller's stream (an ordered 4096^3 GEMM, a few
+    ms) arrives after the workers' 2 ms of polling: the worker then blocks on the slot's event and
+    still checks the row."""
+    import torch
+    K = N = 4096
+    WT = synth.normal_bf16(3, "certl.WT", (N, K), 0.02)
+    eng = g.CertEngine(K, N, slots=4, workers=1)
+    mid = eng.add_matrix(WT, synth.rademacher(5, "certl.r", N)[None, :], transposed=True)
+    x = dev_bf16(synth.normal_bf16(4, "certl.x", (1, K)))
+    y = g.gemv_tree(x, dev_bf16(WT))
+    A = dev_bf16(synth.normal_bf16(6, "certl.A", (4096, 4096)))
+    B = dev_bf16(synth.normal_bf16(7, "certl.B", (4096, 4096), 0.02))
+    torch.cuda.synchronize()
+    say("cert late copy: a long GEMM ahead of the submit")
+    C = g.gemm_ordered(A, B)                 # queued ahead of the copy on the same stream
+    eng.submit(mid, x[0], y[0], token=0)
+    st = eng.drain()
+    torch.cuda.synchronize()
+    assert st["checked"] == 1 and st["failed"] == 0 and not st["copy_error"]
+    assert st["wait_seconds"] > 0.002, st
+    eng.close()
+    del C
