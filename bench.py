@@ -381,6 +381,19 @@ COPY_REPS = 3
 COUNTER_REPS = 4
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemv_tree_traffic.json")
 GEMV_SOURCE = os.path.join(ROOT, "gemv_gemm_ordered_amd", "csrc", "tree_gemv.hip")
+# the counted GEMV kernels: --gemv tree (the headline kernel) or mfma (the matrix-core GEMV)
+COUNTED = {
+    "tree": {"kernel": "k_gemv_tree_p", "source": "tree_gemv.hip", "json": "gemv_tree_traffic.json",
+             "md": "gemv_tree_decode_4096x4096_traffic.md"},
+    "mfma": {"kernel": "k_gemv_mfma", "source": "mfma_gemv.hip", "json": "gemv_mfma_traffic.json",
+             "md": "gemv_mfma_decode_4096x4096_traffic.md"},
+}
+
+
+def source_sha256(name: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "gemv_gemm_ordered_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def gemv_source_sha256() -> str:
@@ -389,7 +402,7 @@ def gemv_source_sha256() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def run_counters():
+def run_counters(which="tree"):
     import numpy as np
     import torch
 
@@ -418,9 +431,10 @@ def run_counters():
         torch.add(small, 0.0, out=small_dst)
     torch.cuda.synchronize()
     i = 0
+    gemv = g.gemv_tree if which == "tree" else g.gemv_mfma_invariant
     for M in (1, 4, 8):
         for _ in range(COUNTER_REPS):
-            g.gemv_tree(dx[:M], dWs[i % 4], y=ys[M])
+            gemv(dx[:M], dWs[i % 4], y=ys[M])
             i += 1
         torch.cuda.synchronize()
     print("counters sequence done", flush=True)
@@ -444,9 +458,11 @@ def _counter_values(directory, counter):
     return [per[d] for d in sorted(per)]
 
 
-def traffic_summary(fetch_dir, write_dir):
+def traffic_summary(fetch_dir, write_dir, which="tree"):
     import statistics
-    out = {"source_sha256": gemv_source_sha256(), "copy_bytes": COPY_BYTES, "units": "bytes per launch"}
+    info = COUNTED[which]
+    out = {"source_sha256": source_sha256(info["source"]), "copy_bytes": COPY_BYTES, "units": "bytes per launch",
+           "kernel": info["kernel"]}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         seq = _counter_values(directory, counter)
         # the last 3 * COPY_REPS dispatches before the GEMVs are the calibration copies:
@@ -469,13 +485,14 @@ def traffic_summary(fetch_dir, write_dir):
         rec["algorithmic_bytes"] = gemv_bytes(int(M))
         rec["hbm_bytes"] = rec["FETCH_SIZE"]["bytes"] + rec["WRITE_SIZE"]["bytes"]
         rec["hbm_over_algorithmic"] = rec["hbm_bytes"] / rec["algorithmic_bytes"]
-    with open(TRAFFIC_JSON, "w") as f:
+    with open(os.path.join(ROOT, "profiles", info["json"]), "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
-    lines = ["# k_gemv_tree_p — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
+    flag = f" --gemv {which}"
+    lines = [f"# {info['kernel']} — HBM traffic per launch (decode GEMV, K = N = 4096)", "",
              "Commands (from the repository root $REPO, on one MI355X; $OUT is any directory for the profiler's output):", "",
-             "    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic_fetch -o run -- python3 $REPO/bench.py --counters",
-             "    cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/traffic_write -o run -- python3 $REPO/bench.py --counters",
-             "    python3 bench.py --traffic-summary $OUT/traffic_fetch $OUT/traffic_write", "",
+             f"    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic_fetch -o run -- python3 $REPO/bench.py --counters{flag}",
+             f"    cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/traffic_write -o run -- python3 $REPO/bench.py --counters{flag}",
+             f"    python3 bench.py --traffic-summary $OUT/traffic_fetch $OUT/traffic_write{flag}", "",
              f"Calibration: a plain elementwise copy of {COPY_BYTES >> 20} MiB (reads and writes {COPY_BYTES} "
              f"bytes) reads FETCH_SIZE = {out['FETCH_SIZE']['copy_counter_kib']:.0f} KiB and WRITE_SIZE = "
              f"{out['WRITE_SIZE']['copy_counter_kib']:.0f} KiB, so one counted KiB is "
@@ -490,9 +507,9 @@ def traffic_summary(fetch_dir, write_dir):
     for M, rec in sorted(out["per_M"].items(), key=lambda kv: int(kv[0])):
         lines.append(f"| {M} | {rec['FETCH_SIZE']['counter_kib']:.0f} | {rec['WRITE_SIZE']['counter_kib']:.0f} | "
                      f"{rec['hbm_bytes']:.0f} | {rec['algorithmic_bytes']} | {rec['hbm_over_algorithmic']:.3f} |")
-    lines += ["", f"Kernel source (tree_gemv.hip) SHA-256: `{out['source_sha256']}` (the bench reports `traffic` only "
-                  "for this source)."]
-    with open(os.path.join(ROOT, "profiles", "gemv_tree_decode_4096x4096_traffic.md"), "w") as f:
+    lines += ["", f"Kernel source ({info['source']}) SHA-256: `{out['source_sha256']}`"
+                  + (" (the bench reports `traffic` only for this source)." if which == "tree" else ".")]
+    with open(os.path.join(ROOT, "profiles", info["md"]), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -609,6 +626,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-paths", action="store_true", help="skip the other paths' throughput")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of one graph replay")
+    ap.add_argument("--gemv", choices=sorted(COUNTED), default="tree",
+                    help="which decode GEMV --counters launches and --traffic-summary summarises")
     ap.add_argument("--counters", action="store_true",
                     help="run the fixed launch sequence for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -625,10 +644,10 @@ def main():
         run_kernel_counters()
         return
     if args.traffic_summary:
-        traffic_summary(*args.traffic_summary)
+        traffic_summary(*args.traffic_summary, which=args.gemv)
         return
     if args.counters:
-        run_counters()
+        run_counters(args.gemv)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library's path has no cross-GPU step, and this "
