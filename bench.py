@@ -730,6 +730,7 @@ def main():
         for name, fn in (("tree", lambda i: g.gemv_tree(dx[:M], dWTs[i % copies], y=ys[M])),
                          ("mfma", lambda i: g.gemv_mfma_invariant(dx[:M], dWTs[i % copies], y=ys[M])),
                          ("ordered", lambda i: g.gemv_ordered(dx[:M], dWs[i % copies], y=ys[M])),
+                         ("ordered_wt", lambda i: g.gemv_ordered_wt(dx[:M], dWTs[i % copies], y=ys[M])),
                          ("hipblaslt", lambda i: torch.mm(dx[:M], dWTs[i % copies].t(), out_dtype=torch.float32))):
             try:
                 t = graph_time(fn, 64)

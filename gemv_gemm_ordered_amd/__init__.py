@@ -65,6 +65,7 @@ def _load():
     lib.gemm_ordered.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemm_ordered_grouped.argtypes = [ct.POINTER(Problem), I64, I, P]
     lib.gemv_ordered.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.gemv_ordered_wt.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemv_tree.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemv_tree_ep.argtypes = [P, I64, P, I64, ct.POINTER(Epilogue), P, I64, I64, I64, I64, P]
     lib.gemm_mfma_invariant_ep.argtypes = [P, I64, P, I64, ct.POINTER(Epilogue), P, I64, I64, I64, I64, P]
@@ -92,7 +93,7 @@ def _load():
         getattr(lib, f).restype = I
     lib.ggo_build_info.restype = ct.c_char_p
     lib.ggo_last_error.restype = ct.c_char_p
-    for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
+    for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered_wt", "gemv_tree", "gemv_tree_ep",
               "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
               "ggo_test_gemm_mfma_tile128", "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep", "freivalds_prepare", "freivalds_check"):
         getattr(lib, f).restype = I
@@ -101,7 +102,7 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemv_tree_ep",
+EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered_wt", "gemv_tree", "gemv_tree_ep",
            "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
            "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep",
            "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error",
@@ -214,6 +215,21 @@ def gemv_ordered(x, W, y=None, stream=None):
     ldy = _rowmajor(y, "y") if M and N else N
     _raise(lib.gemv_ordered(x.data_ptr(), ldx, W.data_ptr(), ldw, y.data_ptr(), ldy, M, N, K, _stream(stream)),
            "gemv_ordered")
+    return y
+
+
+def gemv_ordered_wt(x, WT, y=None, stream=None):
+    """gemv_ordered with the weight given transposed, WT bf16 [N, K] (k contiguous): the same order contract
+    and bits. Needs 8-byte aligned operands with row strides and K multiples of 4."""
+    ldx, ldwt = _rowmajor(x, "x"), _rowmajor(WT, "WT")
+    M, K = x.shape
+    if not (_is_bf16(x) and _is_bf16(WT)) or WT.shape[1] != K:
+        raise ValueError("x and WT must be bf16, WT [N, K]")
+    N = WT.shape[0]
+    y = _out(y, M, N, x)
+    ldy = _rowmajor(y, "y") if M and N else N
+    _raise(lib.gemv_ordered_wt(x.data_ptr(), ldx, WT.data_ptr(), ldwt, y.data_ptr(), ldy, M, N, K, _stream(stream)),
+           "gemv_ordered_wt")
     return y
 
 

@@ -269,10 +269,44 @@ int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
     a.N = (int32_t)N;
     a.K = (int32_t)K;
     a.vec = 0;
+    a.wt = 0;
     // wide loads: W as 4-byte column pairs at even n, x as 8-byte runs of 4 k
     // (same arithmetic and bits either way; only the load width differs)
     if (aligned(W, 4) && ldw % 2 == 0 && N % 2 == 0 && aligned(x, 8) && ldx % 4 == 0 && K % 4 == 0)
         a.vec |= VEC_W | VEC_A;
+    return launched(fn, launch_gemv_ordered(a, s));
+}
+
+int gemv_ordered_wt(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy, int64_t M,
+                    int64_t N, int64_t K, void* stream) {
+    const char* fn = "gemv_ordered_wt";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = check_mnk(fn, M, N, K);
+    if (rc) return rc;
+    if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d (gemm_ordered gives the same bits)", fn, (long long)M, GGO_GEMV_MAX_M);
+    if (M == 0 || N == 0) return ok();
+    if (!y || (K && (!x || !WT))) return fail(GGO_EINVAL, "%s: null pointer", fn);
+    if (ldx < K || ldwt < K || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
+    if (K == 0) return launched(fn, fill_zero(y, ldy, M, N, s));
+    // 8-byte loads of 4 k from rows of x and W^T: no load may straddle the end of a row
+    if (!aligned(x, 8) || ldx % 4 || !aligned(WT, 8) || ldwt % 4 || K % 4)
+        return fail(GGO_EUNSUPPORTED,
+                    "%s: x and W^T must be 8-byte aligned with row strides and K multiples of 4 "
+                    "(gemv_ordered on W [K, N] takes any operands and gives the same bits)", fn);
+    if (ldwt > gemv_ordered_wt_max_ldw())
+        return fail(GGO_EUNSUPPORTED, "%s: ldwt=%lld too large for 32-bit buffer offsets", fn, (long long)ldwt);
+    GemvArgs a;
+    a.x = x;
+    a.W = WT;
+    a.y = y;
+    a.ldx = ldx;
+    a.ldw = ldwt;
+    a.ldy = ldy;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.vec = VEC_W | VEC_A;
+    a.wt = 1;
     return launched(fn, launch_gemv_ordered(a, s));
 }
 

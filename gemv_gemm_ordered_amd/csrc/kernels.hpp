@@ -31,14 +31,16 @@ hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, hi
 
 struct GemvArgs {
     const uint16_t* x;
-    const uint16_t* W;
+    const uint16_t* W;   // W [K, N]; or, with wt set, W^T [N, K] (row stride ldw)
     float* y;
     int64_t ldx, ldw, ldy;
     int32_t M, N, K;
     uint32_t vec;
+    int32_t wt;
 };
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream);
 int gemv_ordered_max_ldw();   // buffer offsets of the GEMV kernel are 32-bit
+int gemv_ordered_wt_max_ldw();   // the same for W^T: a 16-row slab of W^T in one 32-bit range
 
 struct TreeArgs {
     const uint16_t* x;

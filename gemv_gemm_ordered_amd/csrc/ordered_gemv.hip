@@ -35,6 +35,17 @@
 // Columns past N only feed chains that are never stored. The grid is
 // ceil(N/16) x ceil(M/8) workgroups, and each workgroup's column slice is
 // mapped XCD-contiguously so that slices sharing an L2 line run under one L2.
+//
+// W^T form (WT): the weight arrives as W^T [N, K], k contiguous, as a linear
+// layer stores it. A producer lane then loads 4 consecutive k of each of its
+// two weight rows with one 8-byte load per row, so a workgroup's 16 rows are
+// read in 128-byte runs per stage instead of the 32-byte column slices of
+// W [K, N]. One descriptor covers the workgroup's slab of rows; a load for a
+// row past N or a k past K gets an offset beyond that range and returns 0.
+// The products, their order and the consumers are those of the W [K, N] form,
+// and so are the bits.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -76,13 +87,27 @@ template <> struct Fetch<false> {
     uint16_t x[4][4];
 };
 
+// W^T form: rows n and n+1 of W^T at the lane's 4 k, one 8-byte load each, and x as in Fetch<true>.
+struct FetchT {
+    uint2 w[2];
+    uint2 x[4];
+};
+
 // Per-lane constants: byte offsets of the lane's W elements inside a stage,
 // the lane's byte offset into a row of x, and the descriptors of its x rows.
+// W^T form: the slab descriptor, the byte offsets of the lane's two rows at
+// k = 4 kq (relative to the slab), the lane's first k, and which rows are live.
 struct Lane {
     int wof[4][2];
     int xof;
     __amdgpu_buffer_rsrc_t xr[4];
+    __amdgpu_buffer_rsrc_t wt;
+    int tof[2];
+    int k4;
+    bool tlive[2];
 };
+
+constexpr int OUT_OF_RANGE = 0x7ffffff0;   // a buffer offset past every slab range: the load returns 0
 
 // W descriptor of one stage: it starts at row stage*KC and ends right after
 // the last element of W the caller owns (row K-1, column N-1), so rows past K
@@ -121,6 +146,39 @@ GGO_DEV void fetch(const GemvArgs& a, const Lane& L, int stage, Fetch<false>& f)
         for (int i = 0; i < 4; ++i) f.x[j][i] = __builtin_amdgcn_raw_buffer_load_b16(L.xr[j], xo + 2 * i, 0, 0);
 }
 
+GGO_DEV void fetch(const GemvArgs& a, const Lane& L, int stage, FetchT& f) {
+    const bool kin = stage * KC + L.k4 < a.K;   // K % 4 == 0: the lane's 4 k lie wholly inside or past K
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int off = (kin && L.tlive[j]) ? L.tof[j] + stage * KC * 2 : OUT_OF_RANGE;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(L.wt, off, 0, 0);
+        f.w[j] = make_uint2(v[0], v[1]);
+    }
+    const int xo = L.xof + stage * KC * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(L.xr[j], xo, 0, 0);
+        f.x[j] = make_uint2(v[0], v[1]);
+    }
+}
+
+GGO_DEV void unpack_w(const FetchT& f, float (&w0)[4], float (&w1)[4]) {
+    w0[0] = bf16_lo(f.w[0].x);
+    w0[1] = bf16_hi(f.w[0].x);
+    w0[2] = bf16_lo(f.w[0].y);
+    w0[3] = bf16_hi(f.w[0].y);
+    w1[0] = bf16_lo(f.w[1].x);
+    w1[1] = bf16_hi(f.w[1].x);
+    w1[2] = bf16_lo(f.w[1].y);
+    w1[3] = bf16_hi(f.w[1].y);
+}
+GGO_DEV void unpack_x(const FetchT& f, int j, float (&xv)[4]) {
+    xv[0] = bf16_lo(f.x[j].x);
+    xv[1] = bf16_hi(f.x[j].x);
+    xv[2] = bf16_lo(f.x[j].y);
+    xv[3] = bf16_hi(f.x[j].y);
+}
+
 GGO_DEV void unpack_w(const Fetch<true>& f, float (&w0)[4], float (&w1)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -148,8 +206,8 @@ GGO_DEV void unpack_x(const Fetch<false>& f, int j, float (&xv)[4]) {
 
 // Products of one 4(k) x 2(n) block for the lane's live rows, written as
 // 16-byte runs of 4 ascending k.
-template <bool WIDE>
-GGO_DEV void produce(const Fetch<WIDE>& f, float* ps, int kq, int np, int r0, int rows) {
+template <typename F>
+GGO_DEV void produce(const F& f, float* ps, int kq, int np, int r0, int rows) {
     float w0[4], w1[4];
     unpack_w(f, w0, w1);
 #pragma unroll
@@ -166,8 +224,10 @@ GGO_DEV void produce(const Fetch<WIDE>& f, float* ps, int kq, int np, int r0, in
     }
 }
 
-template <bool WIDE>
+template <bool WIDE, bool WT = false>
 __global__ __launch_bounds__(THREADS) void k_gemv_ordered(const GemvArgs a) {
+    static_assert(!WT || WIDE, "the W^T form loads 8 bytes per row");
+    using F = typename std::conditional<WT, FetchT, Fetch<WIDE>>::type;
     // prefetch distance of W and x in stages (the wide ring keeps 64 loads in
     // flight, the element ring 48), and an unroll that makes every ring index static
     constexpr int DEPTH = WIDE ? 8 : 2;
@@ -207,10 +267,22 @@ __global__ __launch_bounds__(THREADS) void k_gemv_ordered(const GemvArgs a) {
         const int task = q % TASKS;
         const int kq = task >> 3, np = task & 7, n = n0 + 2 * np;
         Lane L;
+        if (WT) {
+            const int slab_rows = a.N - n0 < NS ? a.N - n0 : NS;
+            L.wt = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.W) + static_cast<int64_t>(n0) * a.ldw, 0,
+                                                     ((slab_rows - 1) * static_cast<int>(a.ldw) + a.K) * 2, BUF_DWORD3);
+            L.k4 = 4 * kq;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 2; ++j) {
+                L.tof[j] = ((2 * np + j) * static_cast<int>(a.ldw) + 4 * kq) * 2;
+                L.tlive[j] = n + j < a.N;
+            }
+        } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) L.wof[i][j] = ((4 * kq + i) * static_cast<int>(a.ldw) + n + j) * 2;
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) L.wof[i][j] = ((4 * kq + i) * static_cast<int>(a.ldw) + n + j) * 2;
+        }
         L.xof = 8 * kq;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -220,7 +292,7 @@ __global__ __launch_bounds__(THREADS) void k_gemv_ordered(const GemvArgs a) {
                 const_cast<uint16_t*>(a.x) + (live ? static_cast<int64_t>(m0 + r) * a.ldx : 0), 0,
                 live ? a.K * 2 : 0, BUF_DWORD3);
         }
-        Fetch<WIDE> f[DEPTH];
+        F f[DEPTH];
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) fetch(a, L, d, f[d]);
         __syncthreads();
@@ -228,7 +300,7 @@ __global__ __launch_bounds__(THREADS) void k_gemv_ordered(const GemvArgs a) {
 #pragma unroll
             for (int d = 0; d < UNROLL; ++d) {
                 const int s = s0 + d;
-                if (s < nst) produce<WIDE>(f[d % DEPTH], ps[d % NBUF], kq, np, first_row, rows);   // uniform
+                if (s < nst) produce(f[d % DEPTH], ps[d % NBUF], kq, np, first_row, rows);   // uniform
                 fetch(a, L, s + DEPTH, f[d % DEPTH]);   // empty range past the end: zeros, no memory access
                 __syncthreads();
             }
@@ -269,7 +341,9 @@ __global__ __launch_bounds__(THREADS) void k_gemv_ordered(const GemvArgs a) {
 
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
     const dim3 grid((a.N + NS - 1) / NS, (a.M + RG - 1) / RG);
-    if (a.vec & VEC_W)
+    if (a.wt)
+        hipLaunchKernelGGL((k_gemv_ordered<true, true>), grid, dim3(THREADS), 0, stream, a);
+    else if (a.vec & VEC_W)
         hipLaunchKernelGGL(k_gemv_ordered<true>, grid, dim3(THREADS), 0, stream, a);
     else
         hipLaunchKernelGGL(k_gemv_ordered<false>, grid, dim3(THREADS), 0, stream, a);
@@ -277,3 +351,6 @@ hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
 }
 
 int gemv_ordered_max_ldw() { return ((1 << 30) - (1 << 16)) / (KC + 1); }
+
+// The W^T slab range, (NS - 1) * ldw + K elements of 2 bytes, stays below OUT_OF_RANGE.
+int gemv_ordered_wt_max_ldw() { return ((1 << 30) - (1 << 16)) / NS; }

@@ -110,6 +110,25 @@ int gemv_ordered(const uint16_t *x, int64_t ldx,
                  int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * gemv_ordered_wt -- gemv_ordered with the weight supplied transposed, WT
+ * [N, K] (k contiguous: a linear layer's weight layout), row stride ldwt >= K.
+ * The order contract and the bits are gemv_ordered's (and gemm_ordered's):
+ * gemv_ordered_wt(x, W^T) == gemv_ordered(x, W) bit for bit. With k
+ * contiguous, a workgroup reads its 16 weight rows in 128-byte runs instead
+ * of 32-byte column slices.
+ *   x   device, [M, K] bfloat16 bits, 8-byte aligned, ldx % 4 == 0
+ *   WT  device, [N, K] bfloat16 bits, 8-byte aligned, ldwt % 4 == 0,
+ *       ldwt <= (2^30 - 2^16) / 16
+ *   y   device, [M, N] binary32
+ *   K % 4 == 0; 0 <= M <= GGO_GEMV_MAX_M. Operands that break these rules
+ *   give GGO_EUNSUPPORTED.
+ */
+int gemv_ordered_wt(const uint16_t *x, int64_t ldx,
+                    const uint16_t *WT, int64_t ldwt,
+                    float *y, int64_t ldy,
+                    int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * gemv_tree -- tree-ordered GEMV for decode shapes, batch invariant, with the
  * weight supplied transposed (WT [N, K], k contiguous: a linear layer's
  * weight layout), so that every output streams one contiguous row.

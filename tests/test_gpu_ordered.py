@@ -147,6 +147,54 @@ def test_gemv_ragged(g, M, K, N):
     assert np.array_equal(host_bits(g.gemv_ordered(dxa[:, :K], dWa[:, :N])), ref)
 
 
+def test_gemv_wt_decode_every_M(g):
+    """The W^T form at the decode size: every M from 1 to 16 against the oracle, and equal to gemv_ordered
+    on W [K, N]."""
+    say("gemv_ordered_wt decode x[16,4096] W^T[4096,4096]")
+    x, W, _ = synth.decode_gemv(0, 16)
+    ref = f32_bits(oracle.gemm_ordered(x, W, threads=16))
+    dx, dW, dWT = dev_bf16(x), dev_bf16(W), dev_bf16(np.ascontiguousarray(W.T))
+    for M in range(1, 17):
+        y = host_bits(g.gemv_ordered_wt(dx[:M], dWT))
+        assert np.array_equal(y, ref[:M]), M
+    assert np.array_equal(host_bits(g.gemv_ordered(dx[:8], dW)), ref[:8])
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4, 1), (3, 100, 17), (5, 1028, 33), (16, 4096, 4095), (2, 16392, 600),
+                                   (9, 4100, 13), (8, 64, 16), (7, 772, 1000), (1, 11008, 40)])
+def test_gemv_wt_ragged_and_strided(g, M, K, N):
+    import torch
+    say(f"gemv_ordered_wt ragged M={M} K={K} N={N}")
+    x = synth.normal_bf16(M * 7 + K, "gvt.x", (M, K))
+    W = synth.normal_bf16(N + K, "gvt.W", (K, N), 0.02)
+    ref = f32_bits(oracle.gemm_ordered(x, W))
+    WT = np.ascontiguousarray(W.T)
+    assert np.array_equal(host_bits(g.gemv_ordered_wt(dev_bf16(x), dev_bf16(WT))), ref)
+    # row strides past K (multiples of 4), padding filled with NaN: it must never be read
+    nan = np.uint16(0x7fc1)
+    xp = np.full((M, K + 12), nan, dtype=np.uint16)
+    xp[:, :K] = x
+    wp = np.full((N, K + 4), nan, dtype=np.uint16)
+    wp[:, :K] = WT
+    yb = torch.full((M, N + 5), -3.0, device="cuda")
+    g.gemv_ordered_wt(dev_bf16(xp)[:, :K], dev_bf16(wp)[:, :K], y=yb[:, :N])
+    got = host_bits(yb)
+    assert np.array_equal(got[:, :N], ref)
+    assert (got[:, N:] == np.float32(-3.0).view(np.uint32)).all()
+
+
+def test_gemv_wt_rejects_what_it_cannot_take(g):
+    import torch
+    x = torch.zeros((2, 72), dtype=torch.bfloat16, device="cuda")
+    WT = torch.zeros((16, 72), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(g.GGOError):
+        g.gemv_ordered_wt(x[:, :70], WT[:, :70])          # K % 4 != 0
+    with pytest.raises(g.GGOError):
+        g.gemv_ordered_wt(x[:, 2:66], WT[:, :64])         # x not 8-byte aligned
+    with pytest.raises(g.GGOError):
+        g.gemv_ordered_wt(torch.zeros((17, 64), dtype=torch.bfloat16, device="cuda"), WT[:, :64])   # M > 16
+
+
 def _pv_problem(seq, L, heads=4):
     P, V = synth.pv_sequence(0, seq, L, heads=heads)
     return P, V
