@@ -66,6 +66,17 @@ def test_bad_arguments_are_rejected_without_touching_the_gpu(g):
     assert lib.gemv_tree(1, 8, 1, 8, 1, 4, 4, 8, 8, null) == -1            # ldy < N
     assert lib.gemv_tree(1, 1 << 30, 1, 1 << 30, 1, 8, 1, 8, 1 << 30, null) == -2   # K too large
     assert lib.gemm_mfma_invariant(1, 8, 1, 4, 1, 8, 4, 8, 8, null) == -1  # ldw < N
+    # matrix-core GEMV and the W^T ordered GEMV: M > 16, short strides, alignment, K multiples, null pointers
+    for f in (lib.gemv_mfma_invariant, lib.gemv_ordered_wt):
+        assert f(16, 8, 16, 8, 16, 8, 17, 8, 8, null) == -2                 # M > 16
+        assert f(16, 8, 16, 4, 16, 8, 4, 8, 8, null) == -1                 # ldwt < K
+        assert f(16, 8, 16, 8, 16, 4, 4, 8, 8, null) == -1                  # ldy < N
+        assert f(null, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1                # null x
+        assert f(18, 8, 16, 8, 16, 8, 4, 8, 8, null) == -2                  # x misaligned (2 bytes)
+        assert f(16, 8, 16, 8, 16, 8, 4, 8, 6, null) == -2                  # K % 4 != 0 (and % 8)
+    assert lib.gemv_mfma_invariant(16, 12, 16, 12, 16, 8, 4, 8, 12, null) == -2   # K % 8 != 0
+    assert lib.gemv_mfma_invariant(16, 1 << 29, 16, 1 << 29, 16, 8, 1, 8, 1 << 29, null) == -2   # K too large
+    assert b"too large" in lib.ggo_last_error()
     assert lib.gemm_ordered_grouped(null, 1, 0, null) == -1
     arr = (g.Problem * 1)()
     assert lib.gemm_ordered_grouped(arr, 17, 0, null) == -1
@@ -75,6 +86,8 @@ def test_bad_arguments_are_rejected_without_touching_the_gpu(g):
     assert lib.gemv_tree(null, 8, null, 8, null, 8, 0, 8, 8, null) == 0
     assert lib.gemv_tree(null, 8, null, 8, null, 8, 3, 0, 8, null) == 0
     assert lib.gemm_mfma_invariant(null, 8, null, 8, null, 8, 5, 0, 8, null) == 0
+    assert lib.gemv_mfma_invariant(null, 8, null, 8, null, 8, 0, 8, 8, null) == 0
+    assert lib.gemv_ordered_wt(null, 8, null, 8, null, 8, 3, 0, 8, null) == 0
     assert lib.ggo_last_error() == b""
 
 
