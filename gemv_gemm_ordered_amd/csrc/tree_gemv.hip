@@ -240,9 +240,10 @@ GGO_DEV void load_group(const TreeArgs& a, int g, int off, uint32_t (&w)[S][R][4
         for (int r = 0; r < R; ++r) load_tile<true, AUX_STREAM>(wr[r], off + j * STEP_BYTES, w[j][r]);
 }
 
-template <int MT, int R, bool EPI>
-GGO_DEV void reduce_store(const TreeArgs& a, int64_t n0, float (&acc)[R][MT], float (&red)[WAVES][R * MT], int lane,
-                          int wave) {
+// The wave levels of the tree for one group (levels 1-6, a reduce-scatter over the lanes), left in
+// LDS for the cross-wave levels: red[wave][i] is this wave's total of value i (i = r * MT + m).
+template <int MT, int R>
+GGO_DEV void wave_partials(float (&acc)[R][MT], float (&red)[WAVES][R * MT], int lane, int wave) {
     constexpr int V = R * MT;
     static_assert(V <= 64 && (V & (V - 1)) == 0, "one wave total per lane at most, a power of two");
     float v[V];
@@ -252,13 +253,21 @@ GGO_DEV void reduce_store(const TreeArgs& a, int64_t n0, float (&acc)[R][MT], fl
         for (int m = 0; m < MT; ++m) v[r * MT + m] = acc[r][m];
     wave_tree_scatter<V, 1>(v, lane);
     if (lane < V) red[wave][scatter_index<V>(lane)] = v[0];
-    __syncthreads();
-    for (int i = threadIdx.x; i < V; i += THREADS) {
-        const int r = i / MT, m = i % MT;
-        if (m < a.M && n0 + r < a.N) {
-            const float y = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
-            if constexpr (EPI) epi_store(a.ep, a.y, a.ldy, m, n0 + r, y);
-            else static_cast<float*>(a.y)[m * a.ldy + n0 + r] = y;
+}
+
+// Levels 7-8 of the tree, (w0 + w1) + (w2 + w3), for the cnt groups whose wave totals sit in red[0 .. cnt),
+// the groups of ordinals j0 .. j0 + cnt - 1 of this workgroup (group g = blockIdx.x + ordinal * gridDim.x),
+// and the store. Called by every thread after a barrier.
+template <int MT, int R, int RB, bool EPI>
+GGO_DEV void finish_groups(const TreeArgs& a, const float (&red)[RB][WAVES][R * MT], int j0, int cnt) {
+    constexpr int V = R * MT;
+    for (int i = threadIdx.x; i < cnt * V; i += THREADS) {
+        const int q = i / V, iv = i - q * V, r = iv / MT, m = iv % MT;
+        const int64_t n = (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j0 + q) * gridDim.x) * R + r;
+        if (m < a.M && n < a.N) {
+            const float y = (red[q][0][iv] + red[q][1][iv]) + (red[q][2][iv] + red[q][3][iv]);
+            if constexpr (EPI) epi_store(a.ep, a.y, a.ldy, m, n, y);
+            else static_cast<float*>(a.y)[m * a.ldy + n] = y;
         }
     }
 }
@@ -284,7 +293,7 @@ GGO_DEV void fold_group(float (&acc)[R][MT], const uint32_t (&w)[S][R][4], const
         }
 }
 
-template <int MT, int R, int S, int NB, bool EPI>
+template <int MT, int R, int S, int NB, bool EPI, int RB>
 __global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p = wave * 64 + lane;
@@ -304,13 +313,18 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a) {
             for (int e = 0; e < TILE; ++e) x[j][m][e] = elem(d, e);
         }
     }
-    // NB weight buffers in rotation, and as many reduction buffers: a group's LDS totals are read
-    // after its barrier and not written again before NB - 1 more barriers.
-    __shared__ float red[NB][WAVES][R * MT];
+    // NB weight buffers in rotation. The cross-wave levels of the tree wait for a batch of RB groups
+    // (RB = 1: a barrier per group):
+    // each wave leaves its totals of a group in the batch's LDS slot and goes on to the next group, and
+    // the workgroup meets once per batch (or at its last group) to add the four waves' totals of every
+    // group in the batch. Two batch buffers alternate, so the next batch's totals never overwrite a
+    // buffer that is still being read. The arithmetic is that of one barrier per group.
+    __shared__ float red[2][RB][WAVES][R * MT];
     uint32_t w[NB][S][R][4];
     float acc[R][MT];
     const int stride = gridDim.x;
     int g = blockIdx.x;                       // < groups: the grid is never larger
+    int j = 0;                                // ordinal of the current group in this workgroup
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) load_group<MT, R, S>(a, g + b * stride, off, w[b]);
     for (;;) {
@@ -320,8 +334,15 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a) {
             load_group<MT, R, S>(a, gb + (NB - 1) * stride, off, w[(b + NB - 1) % NB]);
             __builtin_amdgcn_sched_barrier(0);    // the requests stay ahead of this fold
             fold_group<MT, R, S>(acc, w[b], x);
-            reduce_store<MT, R, EPI>(a, static_cast<int64_t>(gb) * R, acc, red[b], lane, wave);
-            if (gb + stride >= groups) goto done;
+            const int h = (j / RB) & 1, q = j % RB;
+            wave_partials<MT, R>(acc, red[h][q], lane, wave);
+            const bool last = gb + stride >= groups;   // uniform across the workgroup
+            if (last || q == RB - 1) {
+                __syncthreads();
+                finish_groups<MT, R, RB, EPI>(a, red[h], j - q, q + 1);
+            }
+            ++j;
+            if (last) goto done;
         }
         g += NB * stride;
     }
@@ -350,13 +371,16 @@ int device_cus() {
 // in flight over more of the matrix and reads slower.
 template <int MT, int S>
 hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
-    constexpr int R = MT >= 4 ? 2 : 4, NB = 2, PER_CU = 2;
+    // RB: groups per cross-wave batch. At M = 8 a barrier per group kept the waves in step and the folds
+    // from overlapping the stream (9.6 us; batches of 4: 9.2 us); at M <= 4, with two to four groups per
+    // workgroup, deferring the last levels only lengthens the tail (7.7 -> 7.9 us at M = 4).
+    constexpr int R = MT >= 4 ? 2 : 4, NB = 2, PER_CU = 2, RB = MT >= 8 ? 4 : 1;
     const int64_t groups = (a.N + R - 1) / R;
     const int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
     if (epi_identity(a.ep))
-        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, false>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, false, RB>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, true>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, true, RB>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
