@@ -372,9 +372,10 @@ int device_cus() {
 template <int MT, int S>
 hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
     // RB: groups per cross-wave batch. At M = 8 a barrier per group kept the waves in step and the folds
-    // from overlapping the stream (9.6 us; batches of 4: 9.2 us); at M <= 4, with two to four groups per
-    // workgroup, deferring the last levels only lengthens the tail (7.7 -> 7.9 us at M = 4).
-    constexpr int R = MT >= 4 ? 2 : 4, NB = 2, PER_CU = 2, RB = MT >= 8 ? 4 : 1;
+    // from overlapping the stream (R = 2: 9.6 us; batches of 4: 9.2 us; one output per group in batches
+    // of 8: 8.9 us); at M <= 4, with two to four groups per workgroup, deferring the last levels only
+    // lengthens the tail (7.7 -> 7.9 us at M = 4).
+    constexpr int R = MT >= 8 ? 1 : MT >= 4 ? 2 : 4, NB = 2, PER_CU = 2, RB = MT >= 8 ? 8 : 1;
     const int64_t groups = (a.N + R - 1) / R;
     const int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
     if (epi_identity(a.ep))
