@@ -16,8 +16,8 @@
 // A worker learns that its slot's copy has landed from the slot's flag: a word of pinned host memory
 // that a small kernel on the engine's stream sets to the slot's sequence number after the copy. The
 // worker polls that word (no runtime call on the way, so the workers never contend with the thread
-// that launches the decode kernels) and falls back to the slot's event, which also reports a failed
-// copy, only when the flag is late.
+// that launches the decode kernels) and falls back to synchronising the copy stream, which also
+// reports a failed copy, only when the flag is late.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -49,7 +49,6 @@ struct Slot {
     float* y = nullptr;        // pinned, max_N
     uint16_t* x_dev = nullptr; // the same memory as the GPU addresses it
     float* y_dev = nullptr;
-    hipEvent_t done = nullptr; // the copies into this slot have landed
     uint32_t* flag = nullptr;  // pinned; set to seq on the engine's stream once the copy has landed
     uint32_t* flag_dev = nullptr;
     uint32_t seq = 0;          // sequence number of the submit that filled the slot
@@ -88,18 +87,25 @@ namespace {
 
 using Clock = std::chrono::steady_clock;
 
-// Wait until the copy into slot s has landed. Poll the slot's flag, yielding the core between looks,
-// for up to POLL; past that (a copy stuck behind a long kernel, or one that failed) block on the
-// slot's event, which returns the copy's error if there is one.
-bool wait_copy(Slot& s) {
+// Wait until the copy into slot s has landed. Poll the slot's flag: with pause instructions between
+// looks for the first SPIN, then yielding the core between looks, for up to POLL; past that (a copy stuck behind a long kernel, or one that failed) synchronise the
+// engine's copy stream, which finishes at or after this slot's copy and returns the error of a failed
+// one. (No per-slot event: recording one per row cost a runtime call per row on the launch path.)
+bool wait_copy(hipStream_t copy_stream, Slot& s) {
+    constexpr auto SPIN = std::chrono::microseconds(100);   // a copy normally lands within tens of us
     constexpr auto POLL = std::chrono::milliseconds(2);
     const auto t0 = Clock::now();
     for (;;) {
         if (__atomic_load_n(s.flag, __ATOMIC_ACQUIRE) == s.seq) return true;
-        if (Clock::now() - t0 > POLL) break;
-        std::this_thread::yield();
+        const auto waited = Clock::now() - t0;
+        if (waited > POLL) break;
+        if (waited < SPIN) {
+            for (int i = 0; i < 32; ++i) __builtin_ia32_pause();   // no system call while the copy is due
+        } else {
+            std::this_thread::yield();
+        }
     }
-    if (hipEventSynchronize(s.done) != hipSuccess) return false;
+    if (hipStreamSynchronize(copy_stream) != hipSuccess) return false;
     return __atomic_load_n(s.flag, __ATOMIC_ACQUIRE) == s.seq;
 }
 
@@ -117,7 +123,7 @@ void worker_loop(ggo_cert* c) {
         Slot& sl = c->slots[id];
         bool copy_ok = true;
         const auto tw = Clock::now();
-        if (sl.device) copy_ok = wait_copy(sl);
+        if (sl.device) copy_ok = wait_copy(c->copy_stream, sl);
         const Matrix& m = c->mats[sl.matrix];
         bool pass = true;
         double worst = 0.0;
@@ -180,6 +186,17 @@ void enqueue(ggo_cert* c, int id) {
     c->cv_work.notify_one();
 }
 
+// The rows of one submit in one step: one lock, one wake-up call for the workers (a wake-up per row
+// was a system call per row on the launching thread).
+void enqueue_batch(ggo_cert* c, const int* ids, int64_t n) {
+    {
+        std::lock_guard<std::mutex> lk(c->mu);
+        for (int64_t i = 0; i < n; ++i) c->queued.push_back(ids[i]);
+    }
+    if (n == 1) c->cv_work.notify_one();
+    else c->cv_work.notify_all();
+}
+
 // One launch copies every row of a batch into its pinned slot (host memory the GPU writes through its
 // mapping), instead of two runtime copies per row: 2 x rows segments, one per blockIdx.y.
 constexpr int MAX_BATCH = 16;
@@ -213,7 +230,7 @@ __global__ void k_cert_flags(FlagArgs a) {
     if (i < a.n) __hip_atomic_store(a.flag[i], a.seq[i], __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Queue the flag kernel for slots sid[0 .. n) on the engine's stream, then each slot's event.
+// Queue the flag kernel for slots sid[0 .. n) on the engine's stream.
 hipError_t mark_landed(ggo_cert* c, const int* sid, int64_t n) {
     FlagArgs fa{};
     fa.n = static_cast<int>(n);
@@ -222,9 +239,7 @@ hipError_t mark_landed(ggo_cert* c, const int* sid, int64_t n) {
         fa.seq[i] = c->slots[sid[i]].seq;
     }
     hipLaunchKernelGGL(k_cert_flags, dim3(1), dim3(64), 0, c->copy_stream, fa);
-    hipError_t e = hipGetLastError();
-    for (int64_t i = 0; i < n && e == hipSuccess; ++i) e = hipEventRecord(c->slots[sid[i]].done, c->copy_stream);
-    return e;
+    return hipGetLastError();
 }
 
 inline double widen(uint16_t b) {
@@ -272,9 +287,7 @@ static int create(int64_t max_K, int64_t max_N, int64_t nslots, int nworkers, do
         } else if (hipHostMalloc(reinterpret_cast<void**>(&s.x), static_cast<size_t>(max_K) * 2) != hipSuccess ||
                    hipHostMalloc(reinterpret_cast<void**>(&s.y), static_cast<size_t>(max_N) * 4) != hipSuccess ||
                    hipHostGetDevicePointer(reinterpret_cast<void**>(&s.x_dev), s.x, 0) != hipSuccess ||
-                   hipHostGetDevicePointer(reinterpret_cast<void**>(&s.y_dev), s.y, 0) != hipSuccess ||
-                   // blocking sync: a worker waiting for its slot's copy sleeps instead of spinning
-                   hipEventCreateWithFlags(&s.done, hipEventDisableTiming | hipEventBlockingSync) != hipSuccess) {
+                   hipHostGetDevicePointer(reinterpret_cast<void**>(&s.y_dev), s.y, 0) != hipSuccess) {
             rc = GGO_ELAUNCH;
         }
         c->free_slots.push_back(static_cast<int>(i));
@@ -283,6 +296,13 @@ static int create(int64_t max_K, int64_t max_N, int64_t nslots, int nworkers, do
         (hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess ||
          hipEventCreateWithFlags(&c->ready_evt, hipEventDisableTiming) != hipSuccess))
         rc = GGO_ELAUNCH;
+    if (rc == GGO_OK && !host_only) {
+        // The first launch of a kernel of this source loads its code object (tens of ms); pay that here,
+        // with a flag kernel that writes nothing, rather than on the first token of a decode loop.
+        FlagArgs none{};
+        hipLaunchKernelGGL(k_cert_flags, dim3(1), dim3(64), 0, c->copy_stream, none);
+        if (hipGetLastError() != hipSuccess || hipStreamSynchronize(c->copy_stream) != hipSuccess) rc = GGO_ELAUNCH;
+    }
     if (rc != GGO_OK) {
         ggo_cert_destroy(c);
         return rc;
@@ -403,7 +423,7 @@ int ggo_cert_submit_rows(ggo_cert* c, int64_t n, const int* ids, const uint16_t*
         c->copy_error = 1;
         return GGO_ELAUNCH;
     }
-    for (int64_t i = 0; i < n; ++i) enqueue(c, sid[i]);
+    enqueue_batch(c, sid, n);
     return GGO_OK;
 }
 
@@ -466,7 +486,6 @@ void ggo_cert_destroy(ggo_cert* c) {
         }
         if (s.x) hipHostFree(s.x);
         if (s.y) hipHostFree(s.y);
-        if (s.done) hipEventDestroy(s.done);
     }
     if (c->flags) hipHostFree(c->flags);
     if (c->ready_evt) hipEventDestroy(c->ready_evt);

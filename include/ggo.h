@@ -390,7 +390,7 @@ const char *ggo_last_error(void);
  *   a time (calls are serialised inside). After the copy, a one-block kernel
  *   on the engine's stream writes the slot's sequence number into a flag in
  *   pinned host memory; the worker that checks the row polls that flag and
- *   blocks on the slot's event only if the flag is more than 2 ms late.
+ *   synchronises the engine's stream only if the flag is more than 2 ms late.
  * ggo_cert_submit_rows: ggo_cert_submit for n <= 16 rows at once (ids[i],
  *   x_dev[i], y_dev[i]): one kernel on the engine's stream writes all of them
  *   into their pinned slots, so a token's rows cost one launch instead of two

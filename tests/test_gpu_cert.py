@@ -75,9 +75,9 @@ def test_batched_rows_catch_exactly_the_planted_faults(g):
     eng.close()
 
 
-def test_late_copy_takes_the_event_path(g):
+def test_late_copy_takes_the_stream_path(g):
     """A row whose copy waits behind a long kernel on the caller's stream (an ordered 4096^3 GEMM, a few
-    ms) arrives after the workers' 2 ms of polling: the worker then blocks on the slot's event and
+    ms) arrives after the workers' 2 ms of polling: the worker then synchronises the engine's stream and
     still checks the row."""
     import torch
     K = N = 4096
