@@ -110,13 +110,13 @@ struct Lane {
 constexpr int OUT_OF_RANGE = 0x7ffffff0;   // a buffer offset past every slab range: the load returns 0
 
 // W descriptor of one stage: it starts at row stage*KC and ends right after
-// the last element of W the caller owns (row K-1, column N-1), so rows past K
-// read as 0; stages wholly past K have an empty range.
+// column N-1 of the stage's last row, so nothing past the elements the caller
+// owns is read (lanes of columns past N in that row, and rows past K, read 0);
+// stages wholly past K have an empty range.
 GGO_DEV __amdgpu_buffer_rsrc_t w_rsrc(const GemvArgs& a, int stage) {
     const int rows_left = a.K - stage * KC;
-    const int nrec = rows_left <= 0 ? 0
-                   : rows_left >= KC ? KC * static_cast<int>(a.ldw) * 2
-                                     : ((rows_left - 1) * static_cast<int>(a.ldw) + a.N) * 2;
+    const int rows_in = rows_left < KC ? rows_left : KC;
+    const int nrec = rows_left <= 0 ? 0 : ((rows_in - 1) * static_cast<int>(a.ldw) + a.N) * 2;
     const int64_t row0 = rows_left <= 0 ? 0 : static_cast<int64_t>(stage) * KC;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.W) + row0 * a.ldw, 0, nrec, BUF_DWORD3);
 }
@@ -337,11 +337,202 @@ __global__ __launch_bounds__(THREADS) void k_gemv_ordered(const GemvArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// The same contract with 128-k stages, for M > 4 (16-byte-capable operands only). A producer lane
+// covers all eight rows of its 4(k) x 2(n) block, so each weight pair is loaded once for the eight
+// rows instead of once per half, and a stage is twice as long, so there are half as many barriers;
+// two product buffers suffice because the consumers read stage s-1 and fold it in the same
+// iteration. Products, their positions in each chain and the consumers' order are those of
+// k_gemv_ordered, so the bits are too (the tests compare every M against the oracle). Measured on
+// the 4096 x 4096 decode weight: M = 8 42 -> 35 us, M = 13 73 -> 62 us; at M <= 4 the 64-k form is
+// as fast or faster, so it stays there.
+constexpr int KC2 = 128, NBUF2 = 2, RUN2 = KC2, NQ2 = KC2 / 4, TASKS2 = (KC2 / 4) * (NS / 2);
+static_assert(TASKS2 == 256, "one 4(k) x 2(n) block per producer lane");
+
+// slot() for 128-k runs: both the producers' writes and the consumers' reads keep 8 distinct groups
+// of 4 banks per 8 lanes.
+GGO_DEV int slot2(int run, int k4) { return run * RUN2 + ((k4 ^ ((run + (run >> 3)) & 7)) << 2); }
+
+template <bool WT> struct Fetch2;
+template <> struct Fetch2<true> {    // W^T rows n, n+1 at the lane's 4 k; x rows 0 .. RG-1 at the same k
+    uint2 w[2];
+    uint2 x[RG];
+};
+template <> struct Fetch2<false> {   // W [K, N]: the pair (n, n+1) of each of the lane's 4 k-rows
+    uint32_t w[4];
+    uint2 x[RG];
+};
+
+struct Lane2 {
+    __amdgpu_buffer_rsrc_t wt;   // W^T: the workgroup's slab of rows
+    int tof[2];
+    bool tlive[2];
+    int wof[4][2];               // W [K, N]: offsets inside a stage
+    int k4;
+    int xof;
+    __amdgpu_buffer_rsrc_t xr[RG];
+};
+
+// W [K, N] descriptor of one 128-k stage (w_rsrc for KC2 rows; launched only for ldw small enough that the range fits 31 bits).
+GGO_DEV __amdgpu_buffer_rsrc_t w_rsrc2(const GemvArgs& a, int stage) {
+    const int rows_left = a.K - stage * KC2;
+    const int rows_in = rows_left < KC2 ? rows_left : KC2;
+    const int nrec = rows_left <= 0 ? 0 : ((rows_in - 1) * static_cast<int>(a.ldw) + a.N) * 2;
+    const int64_t row0 = rows_left <= 0 ? 0 : static_cast<int64_t>(stage) * KC2;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.W) + row0 * a.ldw, 0, nrec, BUF_DWORD3);
+}
+
+template <bool WT>
+GGO_DEV void fetch2(const GemvArgs& a, const Lane2& L, int stage, Fetch2<WT>& f) {
+    if constexpr (WT) {
+        const bool kin = stage * KC2 + L.k4 < a.K;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int off = (kin && L.tlive[j]) ? L.tof[j] + stage * KC2 * 2 : OUT_OF_RANGE;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(L.wt, off, 0, 0);
+            f.w[j] = make_uint2(v[0], v[1]);
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t wr = w_rsrc2(a, stage);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.w[i] = __builtin_amdgcn_raw_buffer_load_b32(wr, L.wof[i][0], 0, 0);
+    }
+    const int xo = L.xof + stage * KC2 * 2;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(L.xr[j], xo, 0, 0);
+        f.x[j] = make_uint2(v[0], v[1]);
+    }
+}
+
+GGO_DEV void unpack_w2(const Fetch2<true>& f, float (&w0)[4], float (&w1)[4]) {
+    w0[0] = bf16_lo(f.w[0].x); w0[1] = bf16_hi(f.w[0].x); w0[2] = bf16_lo(f.w[0].y); w0[3] = bf16_hi(f.w[0].y);
+    w1[0] = bf16_lo(f.w[1].x); w1[1] = bf16_hi(f.w[1].x); w1[2] = bf16_lo(f.w[1].y); w1[3] = bf16_hi(f.w[1].y);
+}
+GGO_DEV void unpack_w2(const Fetch2<false>& f, float (&w0)[4], float (&w1)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w0[i] = bf16_lo(f.w[i]);
+        w1[i] = bf16_hi(f.w[i]);
+    }
+}
+
+// Products of the lane's 4(k) x 2(n) block for every live row, as 16-byte runs of 4 ascending k.
+template <bool WT>
+GGO_DEV void produce2(const Fetch2<WT>& f, float* ps, int kq, int np, int rows) {
+    float w0[4], w1[4];
+    unpack_w2(f, w0, w1);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        if (r >= rows) break;   // uniform across the workgroup
+        const float xv[4] = {bf16_lo(f.x[r].x), bf16_hi(f.x[r].x), bf16_lo(f.x[r].y), bf16_hi(f.x[r].y)};
+        const float4 p0 = make_float4(xv[0] * w0[0], xv[1] * w0[1], xv[2] * w0[2], xv[3] * w0[3]);
+        const float4 p1 = make_float4(xv[0] * w1[0], xv[1] * w1[1], xv[2] * w1[2], xv[3] * w1[3]);
+        const int run = r * NS + 2 * np;
+        *reinterpret_cast<float4*>(ps + slot2(run, kq)) = p0;
+        *reinterpret_cast<float4*>(ps + slot2(run + 1, kq)) = p1;
+    }
+}
+
+template <bool WT>
+__global__ __launch_bounds__(THREADS) void k_gemv_ordered_k128(const GemvArgs a) {
+    constexpr int DEPTH = 2, UNROLL = 2;   // prefetch distance in 128-k stages (deeper measured slower)
+    static_assert(UNROLL % NBUF2 == 0 && UNROLL % DEPTH == 0, "");
+    __shared__ __attribute__((aligned(16))) float ps[NBUF2][RG * NS * RUN2];
+
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n0 = xcd_contiguous(blockIdx.x, gridDim.x) * NS;
+    const int m0 = blockIdx.y * RG;
+    const int rows = a.M - m0 < RG ? a.M - m0 : RG;
+    const int nst = (a.K + KC2 - 1) / KC2;
+    // Iteration s (one barrier each): the producers form stage s, the consumers read and fold stage
+    // s-1. Iterations past the data skip the products and the adds.
+    const int iters = (nst + 1 + UNROLL - 1) / UNROLL * UNROLL;
+
+    const bool consumer = wave < CONSUMERS;
+    if (consumer && 4 * wave >= rows) {   // no live row in this consumer wave
+        for (int s = 0; s < iters + 1; ++s) __syncthreads();
+    } else if (!consumer) {
+        const int q = t - 64 * CONSUMERS;
+        const int kq = q >> 3, np = q & 7, n = n0 + 2 * np;
+        Lane2 L;
+        if (WT) {
+            const int slab_rows = a.N - n0 < NS ? a.N - n0 : NS;
+            L.wt = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.W) + static_cast<int64_t>(n0) * a.ldw, 0,
+                                                     ((slab_rows - 1) * static_cast<int>(a.ldw) + a.K) * 2, BUF_DWORD3);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                L.tof[j] = ((2 * np + j) * static_cast<int>(a.ldw) + 4 * kq) * 2;
+                L.tlive[j] = n + j < a.N;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) L.wof[i][j] = ((4 * kq + i) * static_cast<int>(a.ldw) + n + j) * 2;
+        }
+        L.k4 = 4 * kq;
+        L.xof = 8 * kq;
+#pragma unroll
+        for (int j = 0; j < RG; ++j) {
+            const bool live = j < rows;
+            L.xr[j] = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(a.x) + (live ? static_cast<int64_t>(m0 + j) * a.ldx : 0), 0, live ? a.K * 2 : 0,
+                BUF_DWORD3);
+        }
+        Fetch2<WT> f[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) fetch2<WT>(a, L, d, f[d]);
+        __syncthreads();
+        for (int s0 = 0; s0 < iters; s0 += UNROLL) {
+#pragma unroll
+            for (int d = 0; d < UNROLL; ++d) {
+                const int s = s0 + d;
+                if (s < nst) produce2<WT>(f[d % DEPTH], ps[d % NBUF2], kq, np, rows);   // uniform
+                fetch2<WT>(a, L, s + DEPTH, f[d % DEPTH]);   // past the end: empty ranges, zeros
+                __syncthreads();
+            }
+        }
+    } else {
+        const int run = t;   // = (4 * wave + lane / 16) * NS + lane % 16
+        float acc = 0.0f;    // +0.0: the chain's start
+        __syncthreads();
+        for (int s0 = 0; s0 < iters; s0 += UNROLL) {
+#pragma unroll
+            for (int d = 0; d < UNROLL; ++d) {
+                const int s = s0 + d;
+                if (s >= 1 && s <= nst) {   // uniform: stage s - 1, formed in the previous iteration
+                    const float* src = ps[(d + NBUF2 - 1) % NBUF2];
+                    float4 cb[NQ2];
+#pragma unroll
+                    for (int j = 0; j < NQ2; ++j) cb[j] = *reinterpret_cast<const float4*>(src + slot2(run, j));
+#pragma unroll
+                    for (int j = 0; j < NQ2; ++j) {   // ascending k
+                        acc = acc + cb[j].x;
+                        acc = acc + cb[j].y;
+                        acc = acc + cb[j].z;
+                        acc = acc + cb[j].w;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        const int r = t >> 4, nn = n0 + (t & 15);
+        if (r < rows && nn < a.N) a.y[static_cast<int64_t>(m0 + r) * a.ldy + nn] = acc;
+    }
+}
 }  // namespace
 
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
     const dim3 grid((a.N + NS - 1) / NS, (a.M + RG - 1) / RG);
-    if (a.wt)
+    // M > 4 with 16-byte-capable operands: the 128-k form (same bits; see k_gemv_ordered_k128)
+    if (a.M > 4 && a.wt)
+        hipLaunchKernelGGL((k_gemv_ordered_k128<true>), grid, dim3(THREADS), 0, stream, a);
+    else if (a.M > 4 && (a.vec & VEC_W) && a.ldw <= ((1 << 30) - (1 << 16)) / (KC2 + 1))   // 32-bit stage ranges
+        hipLaunchKernelGGL((k_gemv_ordered_k128<false>), grid, dim3(THREADS), 0, stream, a);
+    else if (a.wt)
         hipLaunchKernelGGL((k_gemv_ordered<true, true>), grid, dim3(THREADS), 0, stream, a);
     else if (a.vec & VEC_W)
         hipLaunchKernelGGL(k_gemv_ordered<true>, grid, dim3(THREADS), 0, stream, a);

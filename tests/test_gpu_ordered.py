@@ -118,18 +118,21 @@ def test_subnormals_kept_and_no_negative_zero(g):
 
 
 def test_gemv_decode_matches_oracle_and_gemm(g):
-    say("gemv decode x[8,4096] W[4096,4096]")
-    x, W, _ = synth.decode_gemv(0, 8)
+    """Every M from 1 to 16 at the decode size (M <= 4 and M > 4 take differently staged kernels)."""
+    say("gemv decode x[16,4096] W[4096,4096]")
+    x, W, _ = synth.decode_gemv(0, 16)
     ref = f32_bits(oracle.gemm_ordered(x, W, threads=16))
     dx, dW = dev_bf16(x), dev_bf16(W)
-    for M in (1, 4, 8):
+    for M in range(1, 17):
         y = host_bits(g.gemv_ordered(dx[:M], dW))
         assert np.array_equal(y, ref[:M]), M
+    for M in (1, 4, 8):
         assert np.array_equal(host_bits(g.gemm_ordered(dx[:M], dW)), ref[:M])
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16])
-@pytest.mark.parametrize("K,N", [(777, 1000), (772, 1000), (64, 16), (4, 2), (1, 1), (1092, 30), (2048, 4097)])
+@pytest.mark.parametrize("K,N", [(777, 1000), (772, 1000), (64, 16), (4, 2), (1, 1), (1092, 30), (2048, 4097),
+                                 (128, 34), (256, 18), (132, 48), (384, 30)])
 def test_gemv_ragged(g, M, K, N):
     # K % 4 == 0 and even N take the wide loads (edges masked), the rest element loads
     say(f"gemv ragged M={M} K={K} N={N}")
@@ -161,7 +164,8 @@ def test_gemv_wt_decode_every_M(g):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4, 1), (3, 100, 17), (5, 1028, 33), (16, 4096, 4095), (2, 16392, 600),
-                                   (9, 4100, 13), (8, 64, 16), (7, 772, 1000), (1, 11008, 40)])
+                                   (9, 4100, 13), (8, 64, 16), (7, 772, 1000), (1, 11008, 40),
+                                   (6, 128, 18), (12, 256, 31), (16, 132, 48)])
 def test_gemv_wt_ragged_and_strided(g, M, K, N):
     import torch
     say(f"gemv_ordered_wt ragged M={M} K={K} N={N}")

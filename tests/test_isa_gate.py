@@ -119,13 +119,13 @@ def test_no_atomics_anywhere(code):
 
 
 def test_hot_kernels_use_no_scratch(code):
-    """The matrix-core and tree GEMV kernels keep all their state in registers and LDS. A scratch
+    """The matrix-core, tree and ordered GEMV kernels keep all their state in registers and LDS. A scratch
     (private memory) access in them means an array the compiler could not keep in registers -- for
     example an accumulator array indexed with a runtime value -- and it turns every matrix
     instruction into a memory round trip while the results stay correct."""
     scratch = re.compile(r"\b(scratch_\w+|buffer_(?:load|store)_\w+ [^;]*\boff, s\[0:3\])")
     for src, tag in (("mfma_invariant.hip", "k_gemm_mfma"), ("tree_gemv.hip", "k_gemv_tree"),
-                     ("mfma_gemv.hip", "k_gemv_mfma")):
+                     ("mfma_gemv.hip", "k_gemv_mfma"), ("ordered_gemv.hip", "k_gemv_ordered")):
         ks = [k for k in code[src] if tag in k]
         assert ks, src
         for k in ks:
