@@ -385,12 +385,15 @@ COPY_REPS = 3
 COUNTER_REPS = 4
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemv_tree_traffic.json")
 GEMV_SOURCE = os.path.join(ROOT, "gemv_gemm_ordered_amd", "csrc", "tree_gemv.hip")
-# the counted GEMV kernels: --gemv tree (the headline kernel) or mfma (the matrix-core GEMV)
+# the counted GEMV kernels: --gemv tree (the headline kernel), mfma (the matrix-core GEMV) or ordered
 COUNTED = {
     "tree": {"kernel": "k_gemv_tree_p", "source": "tree_gemv.hip", "json": "gemv_tree_traffic.json",
              "md": "gemv_tree_decode_4096x4096_traffic.md"},
     "mfma": {"kernel": "k_gemv_mfma", "source": "mfma_gemv.hip", "json": "gemv_mfma_traffic.json",
              "md": "gemv_mfma_decode_4096x4096_traffic.md"},
+    # gemv_ordered on W [K, N]: k_gemv_ordered at M <= 4, k_gemv_ordered_k128 at M = 8
+    "ordered": {"kernel": "k_gemv_ordered", "source": "ordered_gemv.hip", "json": "gemv_ordered_traffic.json",
+                "md": "gemv_ordered_decode_4096x4096_traffic.md"},
 }
 
 
@@ -418,7 +421,7 @@ def run_counters(which="tree"):
     small_dst = dst[:(32 << 20) // 4]
     x, W, _ = synth.decode_gemv(0, 8)
     dx = dev_bf16(x)
-    dWs = [dev_bf16(np.ascontiguousarray(W.T))] + [None] * 3
+    dWs = [dev_bf16(W if which == "ordered" else np.ascontiguousarray(W.T))] + [None] * 3
     for i in range(1, 4):
         dWs[i] = dWs[0].clone()
     ys = {M: torch.empty((M, 4096), device="cuda") for M in (1, 4, 8)}
@@ -435,7 +438,7 @@ def run_counters(which="tree"):
         torch.add(small, 0.0, out=small_dst)
     torch.cuda.synchronize()
     i = 0
-    gemv = g.gemv_tree if which == "tree" else g.gemv_mfma_invariant
+    gemv = {"tree": g.gemv_tree, "mfma": g.gemv_mfma_invariant, "ordered": g.gemv_ordered}[which]
     for M in (1, 4, 8):
         for _ in range(COUNTER_REPS):
             gemv(dx[:M], dWs[i % 4], y=ys[M])
