@@ -360,6 +360,7 @@ def cert_loop(g, tokens=48):
                         "host_check_us_per_row": round(1e6 * st["check_seconds"] / max(1, st["checked"]), 1),
                         "copy_wait_us_per_row": round(1e6 * st["wait_seconds"] / max(1, st["checked"]), 1),
                         "submit_wait_us_per_token": round(1e6 * st["submit_wait_seconds"] / tokens, 1),
+                        "submit_c_us_per_token": round(1e6 * st["submit_seconds"] / tokens, 1),
                         "escape_probability_of_a_cancelling_fault": 2.0 ** -t}
         eng.close()
     return res

@@ -42,7 +42,7 @@ class CertStats(ct.Structure):
     """Mirror of ``ggo_cert_stats``."""
     _fields_ = [("submitted", ct.c_int64), ("checked", ct.c_int64), ("failed", ct.c_int64),
                 ("max_honest_ratio", ct.c_double), ("check_seconds", ct.c_double), ("copy_error", ct.c_int),
-                ("wait_seconds", ct.c_double), ("submit_wait_seconds", ct.c_double)]
+                ("wait_seconds", ct.c_double), ("submit_wait_seconds", ct.c_double), ("submit_seconds", ct.c_double)]
 
 
 class Problem(ct.Structure):

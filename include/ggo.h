@@ -412,6 +412,7 @@ typedef struct ggo_cert_stats {
     int copy_error;
     double wait_seconds;        /* worker time spent waiting for the rows' copies to land */
     double submit_wait_seconds; /* submit time spent waiting for a free slot (back pressure) */
+    double submit_seconds;      /* launching thread's time inside ggo_cert_submit_rows, waits included */
 } ggo_cert_stats;
 
 int ggo_cert_create(int64_t max_K, int64_t max_N, int64_t slots, int workers, double c_f, ggo_cert **out);
