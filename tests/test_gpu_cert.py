@@ -75,6 +75,42 @@ def test_batched_rows_catch_exactly_the_planted_faults(g):
     eng.close()
 
 
+def test_batched_rows_at_unaligned_addresses(g):
+    """Rows that start off a 16-byte boundary (inside a padded buffer) take the gather's 2-byte copies; the
+    rest take 16-byte copies. Honest rows pass and a planted fault is caught either way."""
+    import torch
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008), (1000, 1004)]
+    WTs = [synth.normal_bf16(50 + i, "certu.WT", (n, k), 0.02) for i, (n, k) in enumerate(shapes)]
+    eng = g.CertEngine(11008, 11008, slots=16, workers=2)
+    mids = [eng.add_matrix(wt, synth.rademacher(60 + i, "certu.r", wt.shape[0])[None, :], transposed=True)
+            for i, wt in enumerate(WTs)]
+    dW = [dev_bf16(wt) for wt in WTs]
+    keep, planted = [], set()
+    say("cert batched rows at unaligned addresses: 6 tokens x 4 matrices")
+    for tok in range(6):
+        xs, ys = [], []
+        for i, (n, k) in enumerate(shapes):
+            shift = (tok + i) % 3                      # 0: aligned; 1, 2: x and y off 16-byte boundaries
+            xb = torch.zeros((1, k + 8), dtype=torch.bfloat16, device="cuda")
+            xb[0, shift:shift + k] = dev_bf16(synth.normal_bf16(200 + 7 * tok + i, "certu.x", (1, k)))[0]
+            x = xb[0, shift:shift + k]
+            yb = torch.zeros((n + 8,), device="cuda")
+            y = yb[shift:shift + n]
+            g.gemv_tree(x[None, :].contiguous(), dW[i], y=y[None, :])
+            if i == 1 and tok in (2, 4):                # shift 0 at token 2, shift 2 at token 4
+                y[(31 * tok) % n] += 0.05
+                planted.add((tok, mids[i]))
+            xs.append(x)
+            ys.append(y)
+        eng.submit_rows(mids, xs, ys, token=tok)
+        keep.append((xs, ys))
+    st = eng.drain()
+    torch.cuda.synchronize()
+    assert st["submitted"] == st["checked"] == 24 and not st["copy_error"]
+    assert set(eng.failures()) == planted and len(planted) == 2
+    eng.close()
+
+
 def test_late_copy_takes_the_stream_path(g):
     """A row whose copy waits behind a long kernel on the caller's stream (an ordered 4096^3 GEMM, a few
     ms) arrives after the workers' 2 ms of polling: the worker then synchronises the engine's stream and
