@@ -97,7 +97,7 @@ int make_epi(const char* fn, const ggo_epilogue* e, int64_t N, Epi* out) {
     return GGO_OK;
 }
 
-int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, OrdProblem& p, int64_t& tiles) {
+int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, int small, OrdProblem& p, int64_t& tiles) {
     int rc = check_mnk(fn, q.M, q.N, q.K);
     if (rc) return rc;
     if (q.batch < 0) return fail(GGO_EINVAL, "%s: negative batch", fn);
@@ -110,7 +110,7 @@ int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, OrdProblem& 
             return fail(GGO_EINVAL, "%s: negative batch stride", fn);
     }
     int bm, bn;
-    ordered_tile_shape(&bm, &bn);
+    ordered_tile_shape(small, &bm, &bn);
     p.A = q.A;
     p.W = q.W;
     p.C = q.C;
@@ -137,7 +137,13 @@ int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, OrdProblem& 
     return GGO_OK;
 }
 
-int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype, hipStream_t s) {
+// Tile of the ordered kernel: the 16 x 16 tile for gemm_ordered on a weight of at most 2^20 elements
+// (one output per lane, so small weights fill the chip at small M), else 64 x 64. The choice depends on
+// the entry point and the weight's shape, never on M; every output's chain, and so its bits, is the
+// same under either tile. Grouped launches (the value product) keep 64 x 64.
+constexpr int64_t ORDERED_SMALL_WEIGHT = int64_t(1) << 20;
+
+int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype, int small_ok, hipStream_t s) {
     if (a_dtype != GGO_BF16 && a_dtype != GGO_F32) return fail(GGO_EINVAL, "%s: a_dtype must be GGO_BF16 or GGO_F32", fn);
     if (!qs) return fail(GGO_EINVAL, "%s: null problem array", fn);
     if (count < 1 || count > GGO_MAX_PROBLEMS) return fail(GGO_EINVAL, "%s: count must be 1..%d", fn, GGO_MAX_PROBLEMS);
@@ -145,10 +151,11 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     std::memset(&g, 0, sizeof g);
     int64_t total = 0;
     int n = 0;
+    const int small = small_ok && count == 1 && qs[0].batch == 1 && qs[0].N * qs[0].K <= ORDERED_SMALL_WEIGHT;
     for (int64_t i = 0; i < count; ++i) {
         int64_t tiles = 0;
         OrdProblem p;
-        int rc = fill_problem(fn, qs[i], a_dtype, p, tiles);
+        int rc = fill_problem(fn, qs[i], a_dtype, small, p, tiles);
         if (rc) return rc;
         if (qs[i].K == 0 && qs[i].M && qs[i].N) {
             // empty folds: +0.0 for every output of every batch entry
@@ -168,7 +175,7 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     if (n == 0) return ok();
     g.count = n;
     g.tile_start[n] = (int32_t)total;
-    return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, s));
+    return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, small, s));
 }
 
 // The 256x128 instance needs 16-byte aligned operands with row strides that
@@ -237,11 +244,11 @@ int gemm_ordered(const void* A, int a_dtype, int64_t lda, const uint16_t* W, int
     q.M = M;
     q.N = N;
     q.K = K;
-    return run_group("gemm_ordered", &q, 1, a_dtype, static_cast<hipStream_t>(stream));
+    return run_group("gemm_ordered", &q, 1, a_dtype, 1, static_cast<hipStream_t>(stream));
 }
 
 int gemm_ordered_grouped(const ggo_problem* problems, int64_t count, int a_dtype, void* stream) {
-    return run_group("gemm_ordered_grouped", problems, count, a_dtype, static_cast<hipStream_t>(stream));
+    return run_group("gemm_ordered_grouped", problems, count, a_dtype, 0, static_cast<hipStream_t>(stream));
 }
 
 int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw, float* y, int64_t ldy, int64_t M,

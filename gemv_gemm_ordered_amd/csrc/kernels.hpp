@@ -26,8 +26,9 @@ struct OrdGroup {
     OrdProblem p[GGO_MAX_PROBLEMS];
 };
 
-void ordered_tile_shape(int* bm, int* bn);
-hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, hipStream_t stream);
+// small != 0: the 16 x 16 tile (one output per lane), for single-problem launches on small weights
+void ordered_tile_shape(int small, int* bm, int* bn);
+hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, hipStream_t stream);
 
 struct GemvArgs {
     const uint16_t* x;

@@ -11,7 +11,8 @@
 //
 // Design for gfx950: a 64x64 output tile per 256-lane workgroup; each lane holds
 // a 4x4 register micro-tile (16 independent chains, which keeps the VALU busy
-// while each chain stays sequential). A and W tiles are read from HBM with
+// while each chain stays sequential). Small weights take a 16x16 tile with one
+// output per lane instead (see Tile below). A and W tiles are read from HBM with
 // 16-byte loads, widened to binary32 once, and staged in LDS (A transposed so a
 // lane's four rows sit in one 16-byte LDS read). Tiles move through registers
 // one step ahead of the arithmetic (prefetch), which moves loads but no adds.
@@ -24,15 +25,29 @@
 
 namespace {
 
-constexpr int BM = 64, BN = 64, BK = 32, TM = 4, TN = 4, THREADS = 256;
-constexpr int APAD = 4;
+constexpr int THREADS = 256, APAD = 4;
 
-struct ATile { float v[8]; };
-struct WTile { float v[8]; };
+// Tile shapes. Both give every output the same chain, so the same bits; which one a launch uses
+// depends only on the weight's shape and the entry point, never on M.
+//   Big:   64 x 64 outputs, 32-k steps, a 4 x 4 micro-tile per lane (16 chains: the VALU stays busy).
+//   Small: 16 x 16 outputs, 128-k steps, one output per lane, for small weights (N K <= 2^20): at
+//          M <= 64 the big tile leaves most CUs idle (12 workgroups for a 768 x 768 weight) and each
+//          lane's 16 chains run one after another.
+// DEPTH: k-steps of A and W in flight in registers ahead of the one being folded.
+template <int BM_, int BN_, int BK_, int TM_, int TN_, int DEPTH_> struct Tile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, TM = TM_, TN = TN_, DEPTH = DEPTH_;
+    static constexpr int CA = BK / 8, CW = BN / 8;   // 8-element chunks per A row / per W k-row
+    static_assert(BM * CA == THREADS && BK * CW == THREADS, "each thread loads one chunk of A and one of W");
+    static_assert((BM / TM) * (BN / TN) == THREADS, "one micro-tile per lane");
+};
+using BigTile = Tile<64, 64, 32, 4, 4, 1>;
+using SmallTile = Tile<16, 16, 128, 1, 1, 1>;   // four steps in flight measured no faster
 
-template <int AF32>
-GGO_DEV void load_a(const OrdProblem& P, const void* Abase, int m0, int k0, int t, ATile& out) {
-    const int r = t >> 2, kc = (t & 3) * 8;
+struct Chunk { float v[8]; };
+
+template <class T, int AF32>
+GGO_DEV void load_a(const OrdProblem& P, const void* Abase, int m0, int k0, int t, Chunk& out) {
+    const int r = t / T::CA, kc = (t % T::CA) * 8;
     const int row = m0 + r, k = k0 + kc;
     const bool rowok = row < P.M;
     if (AF32) {
@@ -59,8 +74,9 @@ GGO_DEV void load_a(const OrdProblem& P, const void* Abase, int m0, int k0, int 
     }
 }
 
-GGO_DEV void load_w(const OrdProblem& P, const uint16_t* Wb, int n0, int k0, int t, WTile& out) {
-    const int kr = t >> 3, nc = (t & 7) * 8;
+template <class T>
+GGO_DEV void load_w(const OrdProblem& P, const uint16_t* Wb, int n0, int k0, int t, Chunk& out) {
+    const int kr = t / T::CW, nc = (t % T::CW) * 8;
     const int k = k0 + kr, n = n0 + nc;
     const uint16_t* W = Wb + static_cast<int64_t>(k) * P.ldw + n;
     if (k < P.K && n + 8 <= P.N && (P.vec & VEC_W)) {
@@ -73,33 +89,47 @@ GGO_DEV void load_w(const OrdProblem& P, const uint16_t* Wb, int n0, int k0, int
     }
 }
 
-GGO_DEV void store_tiles(float (*As)[BM + APAD], float (*Ws)[BN], int t, const ATile& a, const WTile& w) {
-    const int r = t >> 2, kc = (t & 3) * 8;
+template <class T>
+GGO_DEV void store_tiles(float (*As)[T::BM + APAD], float (*Ws)[T::BN], int t, const Chunk& a, const Chunk& w) {
+    const int r = t / T::CA, kc = (t % T::CA) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) As[kc + i][r] = a.v[i];
-    const int kr = t >> 3, nc = (t & 7) * 8;
+    const int kr = t / T::CW, nc = (t % T::CW) * 8;
     *reinterpret_cast<float4*>(&Ws[kr][nc]) = make_float4(w.v[0], w.v[1], w.v[2], w.v[3]);
     *reinterpret_cast<float4*>(&Ws[kr][nc + 4]) = make_float4(w.v[4], w.v[5], w.v[6], w.v[7]);
 }
 
 // One step of every chain the lane owns: acc[i][j] = acc[i][j] + (a[i] * w[j]).
-GGO_DEV void fold_step(float (&acc)[TM][TN], const float (*As)[BM + APAD], const float (*Ws)[BN],
+template <class T>
+GGO_DEV void fold_step(float (&acc)[T::TM][T::TN], const float (*As)[T::BM + APAD], const float (*Ws)[T::BN],
                        int kk, int ty, int tx) {
-    const float4 a4 = *reinterpret_cast<const float4*>(&As[kk][ty * TM]);
-    const float4 w4 = *reinterpret_cast<const float4*>(&Ws[kk][tx * TN]);
-    const float a[TM] = {a4.x, a4.y, a4.z, a4.w};
-    const float w[TN] = {w4.x, w4.y, w4.z, w4.w};
+    float a[T::TM], w[T::TN];
+    if constexpr (T::TM == 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
+        a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < T::TM; ++i) a[i] = As[kk][ty * T::TM + i];
+    }
+    if constexpr (T::TN == 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&Ws[kk][tx * 4]);
+        w[0] = w4.x; w[1] = w4.y; w[2] = w4.z; w[3] = w4.w;
+    } else {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < T::TN; ++j) w[j] = Ws[kk][tx * T::TN + j];
+    }
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
             const float p = a[i] * w[j];   // first rounding
             acc[i][j] = acc[i][j] + p;     // second rounding
         }
 }
 
-template <int AF32>
+template <class T, int AF32>
 __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
+    constexpr int BM = T::BM, BN = T::BN, BK = T::BK, TM = T::TM, TN = T::TN;
     __shared__ __attribute__((aligned(16))) float As[BK][BM + APAD];
     __shared__ __attribute__((aligned(16))) float Ws[BK][BN];
 
@@ -119,39 +149,51 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
     const uint16_t* Wb = P.W + b * P.sw;
     float* Cb = P.C + b * P.sc;
 
-    const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+    const int t = threadIdx.x, tx = t % (BN / TN), ty = t / (BN / TN);
     float acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;   // +0.0: the chain's start
 
+    // Register ring of DEPTH k-steps: step kt sits in slot kt % DEPTH until it is stored to LDS; the
+    // k loop is unrolled by DEPTH so every slot index is static. Loads move ahead; the adds do not.
+    constexpr int D = T::DEPTH;
     const int nkt = (P.K + BK - 1) / BK;
-    ATile ra;
-    WTile rw;
-    if (nkt > 0) {
-        load_a<AF32>(P, Ab, m0, 0, t, ra);
-        load_w(P, Wb, n0, 0, t, rw);
-        store_tiles(As, Ws, t, ra, rw);
-    }
+    Chunk ra[D], rw[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < nkt) {
+            load_a<T, AF32>(P, Ab, m0, d * BK, t, ra[d]);
+            load_w<T>(P, Wb, n0, d * BK, t, rw[d]);
+        }
+    if (nkt > 0) store_tiles<T>(As, Ws, t, ra[0], rw[0]);
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int k0 = kt * BK;
-        if (kt + 1 < nkt) {                       // next tile in flight while this one folds
-            load_a<AF32>(P, Ab, m0, k0 + BK, t, ra);
-            load_w(P, Wb, n0, k0 + BK, t, rw);
-        }
-        const int kb = P.K - k0 < BK ? P.K - k0 : BK;
-        if (kb == BK) {
-#pragma unroll 8
-            for (int kk = 0; kk < BK; ++kk) fold_step(acc, As, Ws, kk, ty, tx);
-        } else {
-            for (int kk = 0; kk < kb; ++kk) fold_step(acc, As, Ws, kk, ty, tx);
-        }
-        __syncthreads();
-        if (kt + 1 < nkt) {
-            store_tiles(As, Ws, t, ra, rw);
+    for (int kt0 = 0; kt0 < nkt; kt0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int kt = kt0 + d;
+            if (kt >= nkt) break;                 // uniform
+            const int k0 = kt * BK;
+            if (kt + D < nkt) {                   // slot d is free: step kt is in LDS
+                load_a<T, AF32>(P, Ab, m0, k0 + D * BK, t, ra[d]);
+                load_w<T>(P, Wb, n0, k0 + D * BK, t, rw[d]);
+            }
+            const int kb = P.K - k0 < BK ? P.K - k0 : BK;
+            if (kb == BK) {
+                // the one-output tile unrolls the whole step, so its LDS reads can run ahead of its
+                // chain of adds (one wave per SIMD has nothing else to hide their latency behind)
+                constexpr int UNR = T::TM * T::TN == 1 ? BK : 8;
+#pragma unroll UNR
+                for (int kk = 0; kk < BK; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
+            } else {
+                for (int kk = 0; kk < kb; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
+            }
             __syncthreads();
+            if (kt + 1 < nkt) {
+                store_tiles<T>(As, Ws, t, ra[(d + 1) % D], rw[(d + 1) % D]);
+                __syncthreads();
+            }
         }
     }
 
@@ -161,9 +203,14 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
         if (row >= P.M) break;
         const int col = n0 + tx * TN;
         float* c = Cb + static_cast<int64_t>(row) * P.ldc + col;
-        if (col + TN <= P.N && (P.vec & VEC_C)) {
-            *reinterpret_cast<float4*>(c) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-        } else {
+        bool done = false;
+        if constexpr (TN == 4) {
+            if (col + TN <= P.N && (P.vec & VEC_C)) {
+                *reinterpret_cast<float4*>(c) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+                done = true;
+            }
+        }
+        if (!done) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 if (col + j < P.N) c[j] = acc[i][j];
@@ -173,12 +220,19 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
 
 }  // namespace
 
-void ordered_tile_shape(int* bm, int* bn) { *bm = BM; *bn = BN; }
+void ordered_tile_shape(int small, int* bm, int* bn) {
+    *bm = small ? SmallTile::BM : BigTile::BM;
+    *bn = small ? SmallTile::BN : BigTile::BN;
+}
 
-hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, hipStream_t stream) {
-    if (a_f32)
-        hipLaunchKernelGGL(k_gemm_ordered<1>, dim3(total_tiles), dim3(THREADS), 0, stream, g);
-    else
-        hipLaunchKernelGGL(k_gemm_ordered<0>, dim3(total_tiles), dim3(THREADS), 0, stream, g);
+hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, hipStream_t stream) {
+    const dim3 grid(total_tiles), block(THREADS);
+    if (small) {
+        if (a_f32) hipLaunchKernelGGL((k_gemm_ordered<SmallTile, 1>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((k_gemm_ordered<SmallTile, 0>), grid, block, 0, stream, g);
+    } else {
+        if (a_f32) hipLaunchKernelGGL((k_gemm_ordered<BigTile, 1>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((k_gemm_ordered<BigTile, 0>), grid, block, 0, stream, g);
+    }
     return hipGetLastError();
 }
