@@ -152,6 +152,7 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     int64_t total = 0;
     int n = 0;
     const int small = small_ok && count == 1 && qs[0].batch == 1 && qs[0].N * qs[0].K <= ORDERED_SMALL_WEIGHT;
+    int wide = 1;   // the launch takes the wide loads only if every problem allows them
     for (int64_t i = 0; i < count; ++i) {
         int64_t tiles = 0;
         OrdProblem p;
@@ -166,6 +167,9 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
             continue;
         }
         if (tiles == 0) continue;
+        const int64_t max_ld = ordered_wide_max_ld(small, a_dtype == GGO_F32);
+        if (!((p.vec & VEC_A) && (p.vec & VEC_W) && p.K % 8 == 0 && p.N % 8 == 0 && p.lda <= max_ld && p.ldw <= max_ld))
+            wide = 0;
         g.p[n] = p;
         g.tile_start[n] = (int32_t)total;
         total += tiles;
@@ -175,7 +179,7 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     if (n == 0) return ok();
     g.count = n;
     g.tile_start[n] = (int32_t)total;
-    return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, small, s));
+    return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, small, wide, s));
 }
 
 // The 256x128 instance needs 16-byte aligned operands with row strides that

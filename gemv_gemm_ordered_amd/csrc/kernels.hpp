@@ -28,7 +28,10 @@ struct OrdGroup {
 
 // small != 0: the 16 x 16 tile (one output per lane), for single-problem launches on small weights
 void ordered_tile_shape(int small, int* bm, int* bn);
-hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, hipStream_t stream);
+// wide != 0: every problem has 16-byte aligned A, W, row strides (and batch strides) of whole 16-byte
+// chunks, K and N multiples of 8, and lda, ldw <= ordered_wide_max_ld(small, a_f32)
+hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, int wide, hipStream_t stream);
+int64_t ordered_wide_max_ld(int small, int a_f32);
 
 struct GemvArgs {
     const uint16_t* x;

@@ -43,7 +43,10 @@ template <int BM_, int BN_, int BK_, int TM_, int TN_, int DEPTH_> struct Tile {
 using BigTile = Tile<64, 64, 32, 4, 4, 1>;
 using SmallTile = Tile<16, 16, 128, 1, 1, 1>;   // four steps in flight measured no faster
 
-struct Chunk { float v[8]; };
+// One 8-element chunk as loaded: bf16 pairs in u[0..3] (element 2i in the low half of u[i]) or eight
+// binary32 in u[0..7]. It is widened only when stored to LDS, so the loads of the next k-step stay in
+// flight while the current one is folded (widening at load time made every load wait at once).
+struct Chunk { uint32_t u[8]; };
 
 template <class T, int AF32>
 GGO_DEV void load_a(const OrdProblem& P, const void* Abase, int m0, int k0, int t, Chunk& out) {
@@ -53,23 +56,26 @@ GGO_DEV void load_a(const OrdProblem& P, const void* Abase, int m0, int k0, int 
     if (AF32) {
         const float* A = static_cast<const float*>(Abase) + static_cast<int64_t>(row) * P.lda + k;
         if (rowok && k + 8 <= P.K && (P.vec & VEC_A)) {
-            const float4 a0 = reinterpret_cast<const float4*>(A)[0];
-            const float4 a1 = reinterpret_cast<const float4*>(A)[1];
-            out.v[0] = a0.x; out.v[1] = a0.y; out.v[2] = a0.z; out.v[3] = a0.w;
-            out.v[4] = a1.x; out.v[5] = a1.y; out.v[6] = a1.z; out.v[7] = a1.w;
+            const uint4 a0 = reinterpret_cast<const uint4*>(A)[0];
+            const uint4 a1 = reinterpret_cast<const uint4*>(A)[1];
+            out.u[0] = a0.x; out.u[1] = a0.y; out.u[2] = a0.z; out.u[3] = a0.w;
+            out.u[4] = a1.x; out.u[5] = a1.y; out.u[6] = a1.z; out.u[7] = a1.w;
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) out.v[i] = (rowok && k + i < P.K) ? A[i] : 0.0f;
+            for (int i = 0; i < 8; ++i) out.u[i] = (rowok && k + i < P.K) ? __float_as_uint(A[i]) : 0u;
         }
     } else {
         const uint16_t* A = static_cast<const uint16_t*>(Abase) + static_cast<int64_t>(row) * P.lda + k;
         if (rowok && k + 8 <= P.K && (P.vec & VEC_A)) {
             const uint4 q = *reinterpret_cast<const uint4*>(A);
-            out.v[0] = bf16_lo(q.x); out.v[1] = bf16_hi(q.x); out.v[2] = bf16_lo(q.y); out.v[3] = bf16_hi(q.y);
-            out.v[4] = bf16_lo(q.z); out.v[5] = bf16_hi(q.z); out.v[6] = bf16_lo(q.w); out.v[7] = bf16_hi(q.w);
+            out.u[0] = q.x; out.u[1] = q.y; out.u[2] = q.z; out.u[3] = q.w;
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) out.v[i] = (rowok && k + i < P.K) ? bf16_one(A[i]) : 0.0f;
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = (rowok && k + 2 * i < P.K) ? A[2 * i] : 0u;
+                const uint32_t hi = (rowok && k + 2 * i + 1 < P.K) ? A[2 * i + 1] : 0u;
+                out.u[i] = lo | (hi << 16);
+            }
         }
     }
 }
@@ -81,22 +87,69 @@ GGO_DEV void load_w(const OrdProblem& P, const uint16_t* Wb, int n0, int k0, int
     const uint16_t* W = Wb + static_cast<int64_t>(k) * P.ldw + n;
     if (k < P.K && n + 8 <= P.N && (P.vec & VEC_W)) {
         const uint4 q = *reinterpret_cast<const uint4*>(W);
-        out.v[0] = bf16_lo(q.x); out.v[1] = bf16_hi(q.x); out.v[2] = bf16_lo(q.y); out.v[3] = bf16_hi(q.y);
-        out.v[4] = bf16_lo(q.z); out.v[5] = bf16_hi(q.z); out.v[6] = bf16_lo(q.w); out.v[7] = bf16_hi(q.w);
+        out.u[0] = q.x; out.u[1] = q.y; out.u[2] = q.z; out.u[3] = q.w;
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out.v[i] = (k < P.K && n + i < P.N) ? bf16_one(W[i]) : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (k < P.K && n + 2 * i < P.N) ? W[2 * i] : 0u;
+            const uint32_t hi = (k < P.K && n + 2 * i + 1 < P.N) ? W[2 * i + 1] : 0u;
+            out.u[i] = lo | (hi << 16);
+        }
+    }
+}
+
+// Wide form: every operand 16-byte aligned with row strides, K and N multiples of 8, so no chunk
+// straddles the end of a row. Loads go through range-checked buffer descriptors: rows past M (A) or
+// past K (W) lie past the range and read 0, and chunks past K (A) or past N (W) inside a row get an
+// offset past every range. No per-lane branch surrounds a load, so nothing forces it to land before
+// the k-step that needs it.
+constexpr int BUF_DWORD3 = 0x00020000;   // buffer descriptor word 3: raw 32-bit data, range checked
+constexpr int OUT_OF_RANGE = 0x7ffffff0;
+
+template <class T, int AF32>
+GGO_DEV void load_a_wide(const OrdProblem& P, const void* Abase, int m0, int k0, int t, Chunk& out) {
+    constexpr int ESZ = AF32 ? 4 : 2;
+    const int r = t / T::CA, kc = (t % T::CA) * 8;
+    const int rows = P.M - m0 < T::BM ? P.M - m0 : T::BM;
+    const char* base = static_cast<const char*>(Abase) + static_cast<int64_t>(m0) * P.lda * ESZ;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base), 0, ((rows - 1) * static_cast<int>(P.lda) + P.K) * ESZ, BUF_DWORD3);
+    const int off = (r < rows && k0 + kc < P.K) ? (r * static_cast<int>(P.lda) + k0 + kc) * ESZ : OUT_OF_RANGE;
+    const auto q0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    out.u[0] = q0[0]; out.u[1] = q0[1]; out.u[2] = q0[2]; out.u[3] = q0[3];
+    if (AF32) {
+        const auto q1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OUT_OF_RANGE ? OUT_OF_RANGE : off + 16, 0, 0);
+        out.u[4] = q1[0]; out.u[5] = q1[1]; out.u[6] = q1[2]; out.u[7] = q1[3];
     }
 }
 
 template <class T>
+GGO_DEV void load_w_wide(const OrdProblem& P, const uint16_t* Wb, int n0, int k0, int t, Chunk& out) {
+    const int kr = t / T::CW, nc = (t % T::CW) * 8;
+    const int krows = P.K - k0 < T::BK ? P.K - k0 : T::BK;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Wb) + static_cast<int64_t>(k0) * P.ldw + n0, 0,
+        ((krows - 1) * static_cast<int>(P.ldw) + (P.N - n0)) * 2, BUF_DWORD3);
+    const int off = (kr < krows && n0 + nc < P.N) ? (kr * static_cast<int>(P.ldw) + nc) * 2 : OUT_OF_RANGE;
+    const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    out.u[0] = q[0]; out.u[1] = q[1]; out.u[2] = q[2]; out.u[3] = q[3];
+}
+
+// Element i of a chunk as binary32 (bf16 widening is exact).
+template <int F32>
+GGO_DEV float elem(const Chunk& c, int i) {
+    if (F32) return __uint_as_float(c.u[i]);
+    return (i & 1) ? bf16_hi(c.u[i >> 1]) : bf16_lo(c.u[i >> 1]);
+}
+
+template <class T, int AF32>
 GGO_DEV void store_tiles(float (*As)[T::BM + APAD], float (*Ws)[T::BN], int t, const Chunk& a, const Chunk& w) {
     const int r = t / T::CA, kc = (t % T::CA) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) As[kc + i][r] = a.v[i];
+    for (int i = 0; i < 8; ++i) As[kc + i][r] = elem<AF32>(a, i);
     const int kr = t / T::CW, nc = (t % T::CW) * 8;
-    *reinterpret_cast<float4*>(&Ws[kr][nc]) = make_float4(w.v[0], w.v[1], w.v[2], w.v[3]);
-    *reinterpret_cast<float4*>(&Ws[kr][nc + 4]) = make_float4(w.v[4], w.v[5], w.v[6], w.v[7]);
+    *reinterpret_cast<float4*>(&Ws[kr][nc]) = make_float4(elem<0>(w, 0), elem<0>(w, 1), elem<0>(w, 2), elem<0>(w, 3));
+    *reinterpret_cast<float4*>(&Ws[kr][nc + 4]) = make_float4(elem<0>(w, 4), elem<0>(w, 5), elem<0>(w, 6), elem<0>(w, 7));
 }
 
 // One step of every chain the lane owns: acc[i][j] = acc[i][j] + (a[i] * w[j]).
@@ -127,7 +180,7 @@ GGO_DEV void fold_step(float (&acc)[T::TM][T::TN], const float (*As)[T::BM + APA
         }
 }
 
-template <class T, int AF32>
+template <class T, int AF32, bool WIDE>
 __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK, TM = T::TM, TN = T::TN;
     __shared__ __attribute__((aligned(16))) float As[BK][BM + APAD];
@@ -164,10 +217,15 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
 #pragma unroll
     for (int d = 0; d < D; ++d)
         if (d < nkt) {
-            load_a<T, AF32>(P, Ab, m0, d * BK, t, ra[d]);
-            load_w<T>(P, Wb, n0, d * BK, t, rw[d]);
+            if constexpr (WIDE) {
+                load_a_wide<T, AF32>(P, Ab, m0, d * BK, t, ra[d]);
+                load_w_wide<T>(P, Wb, n0, d * BK, t, rw[d]);
+            } else {
+                load_a<T, AF32>(P, Ab, m0, d * BK, t, ra[d]);
+                load_w<T>(P, Wb, n0, d * BK, t, rw[d]);
+            }
         }
-    if (nkt > 0) store_tiles<T>(As, Ws, t, ra[0], rw[0]);
+    if (nkt > 0) store_tiles<T, AF32>(As, Ws, t, ra[0], rw[0]);
     __syncthreads();
     for (int kt0 = 0; kt0 < nkt; kt0 += D) {
 #pragma unroll
@@ -176,8 +234,13 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             if (kt >= nkt) break;                 // uniform
             const int k0 = kt * BK;
             if (kt + D < nkt) {                   // slot d is free: step kt is in LDS
-                load_a<T, AF32>(P, Ab, m0, k0 + D * BK, t, ra[d]);
-                load_w<T>(P, Wb, n0, k0 + D * BK, t, rw[d]);
+                if constexpr (WIDE) {
+                    load_a_wide<T, AF32>(P, Ab, m0, k0 + D * BK, t, ra[d]);
+                    load_w_wide<T>(P, Wb, n0, k0 + D * BK, t, rw[d]);
+                } else {
+                    load_a<T, AF32>(P, Ab, m0, k0 + D * BK, t, ra[d]);
+                    load_w<T>(P, Wb, n0, k0 + D * BK, t, rw[d]);
+                }
             }
             const int kb = P.K - k0 < BK ? P.K - k0 : BK;
             if (kb == BK) {
@@ -191,7 +254,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             }
             __syncthreads();
             if (kt + 1 < nkt) {
-                store_tiles<T>(As, Ws, t, ra[(d + 1) % D], rw[(d + 1) % D]);
+                store_tiles<T, AF32>(As, Ws, t, ra[(d + 1) % D], rw[(d + 1) % D]);
                 __syncthreads();
             }
         }
@@ -225,14 +288,23 @@ void ordered_tile_shape(int small, int* bm, int* bn) {
     *bn = small ? SmallTile::BN : BigTile::BN;
 }
 
-hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, hipStream_t stream) {
+hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, int wide, hipStream_t stream) {
     const dim3 grid(total_tiles), block(THREADS);
+#define GGO_ORDERED_LAUNCH(TILE, F32, W) hipLaunchKernelGGL((k_gemm_ordered<TILE, F32, W>), grid, block, 0, stream, g)
     if (small) {
-        if (a_f32) hipLaunchKernelGGL((k_gemm_ordered<SmallTile, 1>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((k_gemm_ordered<SmallTile, 0>), grid, block, 0, stream, g);
+        if (wide) { if (a_f32) GGO_ORDERED_LAUNCH(SmallTile, 1, true); else GGO_ORDERED_LAUNCH(SmallTile, 0, true); }
+        else { if (a_f32) GGO_ORDERED_LAUNCH(SmallTile, 1, false); else GGO_ORDERED_LAUNCH(SmallTile, 0, false); }
     } else {
-        if (a_f32) hipLaunchKernelGGL((k_gemm_ordered<BigTile, 1>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((k_gemm_ordered<BigTile, 0>), grid, block, 0, stream, g);
+        if (wide) { if (a_f32) GGO_ORDERED_LAUNCH(BigTile, 1, true); else GGO_ORDERED_LAUNCH(BigTile, 0, true); }
+        else { if (a_f32) GGO_ORDERED_LAUNCH(BigTile, 1, false); else GGO_ORDERED_LAUNCH(BigTile, 0, false); }
     }
+#undef GGO_ORDERED_LAUNCH
     return hipGetLastError();
+}
+
+// Largest row stride (elements) the wide form takes: its byte ranges and offsets stay below 2^30.
+int64_t ordered_wide_max_ld(int small, int a_f32) {
+    const int64_t rows = small ? (SmallTile::BK > SmallTile::BM ? SmallTile::BK : SmallTile::BM)
+                               : (BigTile::BK > BigTile::BM ? BigTile::BK : BigTile::BM);
+    return (int64_t(1) << 30) / ((rows + 1) * (a_f32 ? 4 : 2));
 }
