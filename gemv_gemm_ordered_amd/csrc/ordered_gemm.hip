@@ -41,7 +41,7 @@ template <int BM_, int BN_, int BK_, int TM_, int TN_, int DEPTH_> struct Tile {
     static_assert((BM / TM) * (BN / TN) == THREADS, "one micro-tile per lane");
 };
 using BigTile = Tile<64, 64, 32, 4, 4, 1>;
-using SmallTile = Tile<16, 16, 128, 1, 1, 1>;   // four steps in flight measured no faster
+using SmallTile = Tile<16, 16, 128, 1, 1, 1>;   // deeper rings measured no faster
 
 // One 8-element chunk as loaded: bf16 pairs in u[0..3] (element 2i in the low half of u[i]) or eight
 // binary32 in u[0..7]. It is widened only when stored to LDS, so the loads of the next k-step stay in
@@ -244,11 +244,36 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             }
             const int kb = P.K - k0 < BK ? P.K - k0 : BK;
             if (kb == BK) {
-                // the one-output tile unrolls the whole step, so its LDS reads can run ahead of its
-                // chain of adds (one wave per SIMD has nothing else to hide their latency behind)
-                constexpr int UNR = T::TM * T::TN == 1 ? BK : 8;
-#pragma unroll UNR
-                for (int kk = 0; kk < BK; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
+                if constexpr (T::TM * T::TN == 1) {
+                    // One output per lane and one wave per SIMD: nothing else hides the LDS latency, so
+                    // the reads of the next 8 k are issued before the adds of the current 8 (the
+                    // compiler's own schedule kept two steps ahead).
+                    constexpr int CH = 8, NCH = BK / CH;
+                    float av[2][CH], wv[2][CH];
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        av[0][j] = As[j][ty];
+                        wv[0][j] = Ws[j][tx];
+                    }
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) {
+                        if (c + 1 < NCH) {
+#pragma unroll
+                            for (int j = 0; j < CH; ++j) {
+                                av[(c + 1) & 1][j] = As[(c + 1) * CH + j][ty];
+                                wv[(c + 1) & 1][j] = Ws[(c + 1) * CH + j][tx];
+                            }
+                        }
+#pragma unroll
+                        for (int j = 0; j < CH; ++j) {   // ascending k
+                            const float p = av[c & 1][j] * wv[c & 1][j];
+                            acc[0][0] = acc[0][0] + p;
+                        }
+                    }
+                } else {
+#pragma unroll 8
+                    for (int kk = 0; kk < BK; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
+                }
             } else {
                 for (int kk = 0; kk < kb; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
             }
