@@ -271,8 +271,28 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
                         }
                     }
                 } else {
-#pragma unroll 8
-                    for (int kk = 0; kk < BK; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
+                    // 4 x 4 micro-tile: the next k's two 16-byte reads are issued before this k's 32
+                    // operations (the same reasoning at small M, where a CU holds one workgroup)
+                    static_assert(T::TM == 4 && T::TN == 4, "");
+                    float4 a4[2], w4[2];
+                    a4[0] = *reinterpret_cast<const float4*>(&As[0][ty * 4]);
+                    w4[0] = *reinterpret_cast<const float4*>(&Ws[0][tx * 4]);
+#pragma unroll
+                    for (int kk = 0; kk < BK; ++kk) {
+                        if (kk + 1 < BK) {
+                            a4[(kk + 1) & 1] = *reinterpret_cast<const float4*>(&As[kk + 1][ty * 4]);
+                            w4[(kk + 1) & 1] = *reinterpret_cast<const float4*>(&Ws[kk + 1][tx * 4]);
+                        }
+                        const float a[4] = {a4[kk & 1].x, a4[kk & 1].y, a4[kk & 1].z, a4[kk & 1].w};
+                        const float w[4] = {w4[kk & 1].x, w4[kk & 1].y, w4[kk & 1].z, w4[kk & 1].w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const float p = a[i] * w[j];   // first rounding
+                                acc[i][j] = acc[i][j] + p;     // second rounding
+                            }
+                    }
                 }
             } else {
                 for (int kk = 0; kk < kb; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
