@@ -138,12 +138,16 @@ def cpu_model():
 
 
 def certificate(g, x, W, r, ys, ms):
+    import ctypes as ct
     import numpy as np
     import torch
+
+    import synth
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    prep = g.freivalds_prepare(W, r)
+    f = g.freivalds_prepare(W, synth.stream_key(0, "gemv.r"))   # the signs of the workload's r stream
     t_prep = time.perf_counter() - t0
+    assert np.array_equal(f.signs(), r)
     y8 = ys[ms[-1]]
     t1 = time.perf_counter()
     yh = y8.cpu().numpy()
@@ -151,22 +155,20 @@ def certificate(g, x, W, r, ys, ms):
     checks, worst, t_check = 0, 0.0, 0.0
     for m in range(yh.shape[0]):
         t2 = time.perf_counter()
-        ok, rho, sigma, tau, bound = g.freivalds_check(prep, r, x[m], yh[m])
+        ok, rho, sigma, tau, bound = f.check(x[m], yh[m])
         t_check += time.perf_counter() - t2
         checks += ok
         worst = max(worst, rho / sigma)
     j = 1234
     yb = yh[0].copy()
     yb[j] += np.float32(0.005)
-    caught = not g.freivalds_check(prep, r, x[0], yb)[0]
-    # the library's check itself: the C entry point called directly on prepared host rows, 200 rows
-    s, q, a = prep
+    caught = not f.check(x[0], yb)[0]
+    # the library's check itself: the C entry point called directly on host rows, 200 rows
     out = np.empty(4, dtype=np.float64)
     xr = [np.ascontiguousarray(x[m]) for m in range(yh.shape[0])]
     yr = [np.ascontiguousarray(yh[m], dtype=np.float32) for m in range(yh.shape[0])]
-    K, N = W.shape
-    calls = [(s.ctypes.data, q.ctypes.data, a.ctypes.data, r.ctypes.data, K, N, xr[m].ctypes.data, yr[m].ctypes.data,
-              0.125, out.ctypes.data) for m in range(yh.shape[0])]
+    calls = [(f.h, xr[m].ctypes.data, yr[m].ctypes.data, ct.c_double(0.125), out.ctypes.data)
+             for m in range(yh.shape[0])]
     for c in calls:
         g.lib.freivalds_check(*c)
     reps = 200
@@ -174,6 +176,7 @@ def certificate(g, x, W, r, ys, ms):
     for i in range(reps):
         g.lib.freivalds_check(*calls[i % len(calls)])
     t_c = (time.perf_counter() - t3) / reps
+    f.close()
     return {"honest_pass": f"{checks}/{yh.shape[0]}", "max_honest_ratio": round(worst, 5), "c_f": 0.125,
             "planted_0.005_caught": caught, "us_per_check": round(1e6 * t_c, 2),
             "us_per_check_through_python_binding": round(1e6 * t_check / yh.shape[0], 2),

@@ -74,9 +74,15 @@ def _load():
     lib.gemm_mfma_invariant_wt.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemv_mfma_invariant.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.gemv_mfma_invariant_ep.argtypes = [P, I64, P, I64, ct.POINTER(Epilogue), P, I64, I64, I64, I64, P]
-    lib.freivalds_prepare.argtypes = [P, I64, I64, I64, P, P, P, P]
-    lib.freivalds_check.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     PP = ct.POINTER(ct.c_void_p)
+    lib.ggo_test_gemv_instance.argtypes = [I, I, I, P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.freivalds_prepare.argtypes = [P, I64, I64, I64, ct.c_uint64, PP]
+    lib.freivalds_check.argtypes = [P, P, P, ct.c_double, P]
+    lib.freivalds_signs.argtypes = [P, P]
+    lib.freivalds_free.argtypes = [P]
+    lib.freivalds_free.restype = None
+    lib.freivalds_prepare_signs.argtypes = [P, I64, I64, I64, P, P, P, P]
+    lib.freivalds_check_signs.argtypes = [P, P, P, P, I64, I64, P, P, ct.c_double, P]
     lib.ggo_cert_create.argtypes = [I64, I64, I64, I, ct.c_double, PP]
     lib.ggo_cert_create_host.argtypes = [I64, I64, I64, I, ct.c_double, PP]
     lib.ggo_cert_add_matrix.argtypes = [P, P, I64, I, I64, I64, P, I64, ct.POINTER(I)]
@@ -95,7 +101,9 @@ def _load():
     lib.ggo_last_error.restype = ct.c_char_p
     for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered_wt", "gemv_tree", "gemv_tree_ep",
               "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
-              "ggo_test_gemm_mfma_tile128", "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep", "freivalds_prepare", "freivalds_check"):
+              "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "gemm_mfma_invariant_wt", "gemv_mfma_invariant",
+              "gemv_mfma_invariant_ep", "freivalds_prepare", "freivalds_check", "freivalds_signs",
+              "freivalds_prepare_signs", "freivalds_check_signs"):
         getattr(lib, f).restype = I
     return lib
 
@@ -105,7 +113,9 @@ lib = _load()
 EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered_wt", "gemv_tree", "gemv_tree_ep",
            "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
            "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep",
-           "ggo_test_gemm_mfma_tile128", "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error",
+           "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "freivalds_prepare", "freivalds_check",
+           "freivalds_signs", "freivalds_free", "freivalds_prepare_signs", "freivalds_check_signs",
+           "ggo_build_info", "ggo_last_error",
            "ggo_cert_create", "ggo_cert_create_host", "ggo_cert_add_matrix", "ggo_cert_submit", "ggo_cert_submit_rows",
            "ggo_cert_submit_host",
            "ggo_cert_drain", "ggo_cert_failures", "ggo_cert_destroy")
@@ -373,6 +383,27 @@ def test_gemm_mfma_tile128(A, W, C=None, stream=None):
     return _mfma("ggo_test_gemm_mfma_tile128", A, W, C, stream)
 
 
+GEMV_KINDS = {"tree": 0, "ordered": 1, "ordered_wt": 2, "mfma": 3}
+
+
+def test_gemv_instance(kind, rows, form, x, W, y=None, stream=None):
+    """Test hook: the decode GEMV `kind` ('tree', 'ordered', 'ordered_wt', 'mfma') run by a chosen kernel
+    instance (rows of x staged per workgroup, and the form; see ggo_test_gemv_instance) instead of the one
+    its entry point picks from M. W is W [K, N] for 'ordered', else W^T [N, K]. Must give the entry
+    point's bits."""
+    ldx, ldw = _rowmajor(x, "x"), _rowmajor(W, "W")
+    M, K = x.shape
+    transposed = kind != "ordered"
+    if not (_is_bf16(x) and _is_bf16(W)) or (W.shape[1] if transposed else W.shape[0]) != K:
+        raise ValueError("x and W must be bf16 with matching K")
+    N = W.shape[0] if transposed else W.shape[1]
+    y = _out(y, M, N, x)
+    ldy = _rowmajor(y, "y") if M and N else N
+    _raise(lib.ggo_test_gemv_instance(GEMV_KINDS[kind], rows, form, x.data_ptr(), ldx, W.data_ptr(), ldw,
+                                      y.data_ptr(), ldy, M, N, K, _stream(stream)), "ggo_test_gemv_instance")
+    return y
+
+
 def _np(a, dtype):
     if hasattr(a, "detach"):
         a = a.detach().cpu()
@@ -383,27 +414,72 @@ def _np(a, dtype):
         else np.ascontiguousarray(a, dtype=dtype)
 
 
-def freivalds_prepare(W, r):
-    """Host precompute (s, q, a) for W [K, N] (bf16 bits, host) and signs r (N, +-1)."""
+class Freivalds:
+    """Handle of the float Freivalds certificate for one matrix (freivalds_prepare / freivalds_check /
+    freivalds_free): W [K, N] host bf16 bits; the N signs are drawn inside the library from `seed`."""
+
+    def __init__(self, W, seed: int):
+        W = np.ascontiguousarray(_np(W, np.uint16))
+        self.K, self.N = W.shape
+        h = ct.c_void_p()
+        _raise(lib.freivalds_prepare(W.ctypes.data, self.N, self.K, self.N, ct.c_uint64(seed & (2 ** 64 - 1)),
+                                     ct.byref(h)), "freivalds_prepare")
+        self.h = h
+
+    def check(self, x, y, c_f: float = 0.125):
+        """(accept, rho, sigma, tau, bound) for one host row x (bf16 bits, K) and y (float32, N)."""
+        x = np.ascontiguousarray(_np(x, np.uint16)).reshape(-1)
+        y = np.ascontiguousarray(_np(y, np.float32)).reshape(-1)
+        if x.size != self.K or y.size != self.N:
+            raise ValueError(f"x must hold {self.K} and y {self.N} elements")
+        out = np.empty(4, dtype=np.float64)
+        rc = lib.freivalds_check(self.h, x.ctypes.data, y.ctypes.data, float(c_f), out.ctypes.data)
+        _raise(rc, "freivalds_check")
+        return bool(rc), float(out[0]), float(out[1]), float(out[2]), float(out[3])
+
+    def signs(self) -> np.ndarray:
+        r = np.empty(self.N, dtype=np.int8)
+        _raise(lib.freivalds_signs(self.h, r.ctypes.data), "freivalds_signs")
+        return r
+
+    def close(self):
+        if self.h:
+            lib.freivalds_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def freivalds_prepare(W, seed: int) -> Freivalds:
+    """freivalds_prepare: the certificate handle of W [K, N] (host bf16 bits) with signs drawn from seed."""
+    return Freivalds(W, seed)
+
+
+def freivalds_prepare_signs(W, r):
+    """Host precompute (s, q, a) for W [K, N] (bf16 bits, host) and caller-drawn signs r (N, +-1)."""
     W = _np(W, np.uint16)
     r = np.ascontiguousarray(r, dtype=np.int8)
     K, N = W.shape
     s, q, a = (np.empty(K, dtype=np.float64) for _ in range(3))
-    _raise(lib.freivalds_prepare(W.ctypes.data, N, K, N, r.ctypes.data, s.ctypes.data, q.ctypes.data, a.ctypes.data),
-           "freivalds_prepare")
+    _raise(lib.freivalds_prepare_signs(W.ctypes.data, N, K, N, r.ctypes.data, s.ctypes.data, q.ctypes.data,
+                                       a.ctypes.data), "freivalds_prepare_signs")
     return s, q, a
 
 
-def freivalds_check(prep, r, x, y, c_f: float = 0.125):
+def freivalds_check_signs(prep, r, x, y, c_f: float = 0.125):
     """(accept, rho, sigma, tau, bound) for one host row x (bf16 bits, K) and y (float32, N)."""
     s, q, a = prep
     x = _np(x, np.uint16).reshape(-1)
     y = _np(y, np.float32).reshape(-1)
     r = np.ascontiguousarray(r, dtype=np.int8)
     out = np.empty(4, dtype=np.float64)
-    rc = lib.freivalds_check(s.ctypes.data, q.ctypes.data, a.ctypes.data, r.ctypes.data, s.shape[0], y.shape[0],
-                             x.ctypes.data, y.ctypes.data, float(c_f), out.ctypes.data)
-    _raise(rc, "freivalds_check")
+    rc = lib.freivalds_check_signs(s.ctypes.data, q.ctypes.data, a.ctypes.data, r.ctypes.data, s.shape[0],
+                                   y.shape[0], x.ctypes.data, y.ctypes.data, float(c_f), out.ctypes.data)
+    _raise(rc, "freivalds_check_signs")
     return bool(rc), float(out[0]), float(out[1]), float(out[2]), float(out[3])
 
 

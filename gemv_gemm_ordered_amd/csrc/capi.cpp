@@ -1,6 +1,8 @@
 // C-ABI shim: argument checks, launch geometry, error reporting.
-// Nothing here depends on M except grid extents; no entry point picks a kernel,
-// tile or split from the problem size.
+// The GEMM entry points choose their tile from the weight's shape and the operands' alignment, never
+// from M. The GEMV entry points choose, from M, how many rows of x a workgroup stages (and, for the
+// ordered GEMV, 64- or 128-k stages): instances that compute every output's chains, order and tree
+// identically. ggo_test_gemv_instance runs any instance at any M, so the tests compare them bit for bit.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -255,20 +257,18 @@ int gemm_ordered_grouped(const ggo_problem* problems, int64_t count, int a_dtype
     return run_group("gemm_ordered_grouped", problems, count, a_dtype, 0, static_cast<hipStream_t>(stream));
 }
 
-int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw, float* y, int64_t ldy, int64_t M,
-                 int64_t N, int64_t K, void* stream) {
-    const char* fn = "gemv_ordered";
-    hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+// gemv_ordered (wt = 0, W [K, N]) and gemv_ordered_wt (wt = 1, W^T [N, K]); form as in GemvArgs.
+static int run_gemv_ordered(const char* fn, int wt, const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
+                            float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s, int form) {
     int rc = check_mnk(fn, M, N, K);
     if (rc) return rc;
     if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d (gemm_ordered gives the same bits)", fn, (long long)M, GGO_GEMV_MAX_M);
     if (M == 0 || N == 0) return ok();
     if (!y || (K && (!x || !W))) return fail(GGO_EINVAL, "%s: null pointer", fn);
-    if (ldx < K || ldw < N || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
+    if (ldx < K || ldw < (wt ? K : N) || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
     if (K == 0) return launched(fn, fill_zero(y, ldy, M, N, s));
-    if (ldw > gemv_ordered_max_ldw() || K >= (int64_t(1) << 30))
-        return fail(GGO_EUNSUPPORTED, "%s: ldw=%lld or K=%lld too large for 32-bit buffer offsets (gemm_ordered gives the same bits)",
-                    fn, (long long)ldw, (long long)K);
     GemvArgs a;
     a.x = x;
     a.W = W;
@@ -279,50 +279,35 @@ int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
     a.M = (int32_t)M;
     a.N = (int32_t)N;
     a.K = (int32_t)K;
-    a.vec = 0;
-    a.wt = 0;
-    // wide loads: W as 4-byte column pairs at even n, x as 8-byte runs of 4 k
-    // (same arithmetic and bits either way; only the load width differs)
-    if (aligned(W, 4) && ldw % 2 == 0 && N % 2 == 0 && aligned(x, 8) && ldx % 4 == 0 && K % 4 == 0)
-        a.vec |= VEC_W | VEC_A;
-    return launched(fn, launch_gemv_ordered(a, s));
-}
-
-int gemv_ordered_wt(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy, int64_t M,
-                    int64_t N, int64_t K, void* stream) {
-    const char* fn = "gemv_ordered_wt";
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int rc = check_mnk(fn, M, N, K);
-    if (rc) return rc;
-    if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d (gemm_ordered gives the same bits)", fn, (long long)M, GGO_GEMV_MAX_M);
-    if (M == 0 || N == 0) return ok();
-    if (!y || (K && (!x || !WT))) return fail(GGO_EINVAL, "%s: null pointer", fn);
-    if (ldx < K || ldwt < K || ldy < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
-    if (K == 0) return launched(fn, fill_zero(y, ldy, M, N, s));
-    // 8-byte loads of 4 k from rows of x and W^T: no load may straddle the end of a row
-    if (!aligned(x, 8) || ldx % 4 || !aligned(WT, 8) || ldwt % 4 || K % 4)
-        return fail(GGO_EUNSUPPORTED,
-                    "%s: x and W^T must be 8-byte aligned with row strides and K multiples of 4 "
-                    "(gemv_ordered on W [K, N] takes any operands and gives the same bits)", fn);
-    if (ldwt > gemv_ordered_wt_max_ldw())
-        return fail(GGO_EUNSUPPORTED, "%s: ldwt=%lld too large for 32-bit buffer offsets", fn, (long long)ldwt);
-    GemvArgs a;
-    a.x = x;
-    a.W = WT;
-    a.y = y;
-    a.ldx = ldx;
-    a.ldw = ldwt;
-    a.ldy = ldy;
-    a.M = (int32_t)M;
-    a.N = (int32_t)N;
-    a.K = (int32_t)K;
-    a.vec = VEC_W | VEC_A;
-    a.wt = 1;
+    a.wt = wt;
+    a.form = form;
+    if (wt) {
+        // 8-byte loads of 4 k from rows of x and W^T: no load may straddle the end of a row
+        if (!aligned(x, 8) || ldx % 4 || !aligned(W, 8) || ldw % 4 || K % 4)
+            return fail(GGO_EUNSUPPORTED,
+                        "%s: x and W^T must be 8-byte aligned with row strides and K multiples of 4 "
+                        "(gemv_ordered on W [K, N] takes any operands and gives the same bits)", fn);
+        if (ldw > gemv_ordered_wt_max_ldw())
+            return fail(GGO_EUNSUPPORTED, "%s: ldwt=%lld too large for 32-bit buffer offsets", fn, (long long)ldw);
+        a.vec = VEC_W | VEC_A;
+    } else {
+        if (ldw > gemv_ordered_max_ldw() || K >= (int64_t(1) << 30))
+            return fail(GGO_EUNSUPPORTED, "%s: ldw=%lld or K=%lld too large for 32-bit buffer offsets (gemm_ordered gives the same bits)",
+                        fn, (long long)ldw, (long long)K);
+        // wide loads: W as 4-byte column pairs at even n, x as 8-byte runs of 4 k
+        // (same arithmetic and bits either way; only the load width differs)
+        a.vec = 0;
+        if (aligned(W, 4) && ldw % 2 == 0 && N % 2 == 0 && aligned(x, 8) && ldx % 4 == 0 && K % 4 == 0)
+            a.vec |= VEC_W | VEC_A;
+    }
+    if (form == 2 && !gemv_ordered_k128_ok(a))
+        return fail(GGO_EUNSUPPORTED, "%s: the 128-k instance needs 4-byte column pairs of W (or W^T) and ldw "
+                    "small enough for its stage ranges", fn);
     return launched(fn, launch_gemv_ordered(a, s));
 }
 
 static int run_tree(const char* fn, const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, void* y, int64_t ldy,
-                    int64_t M, int64_t N, int64_t K, hipStream_t s, const Epi& ep) {
+                    int64_t M, int64_t N, int64_t K, hipStream_t s, const Epi& ep, int rows = 0, int form = 0) {
     int rc = check_mnk(fn, M, N, K);
     if (rc) return rc;
     if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d", fn, (long long)M, GGO_GEMV_MAX_M);
@@ -345,7 +330,24 @@ static int run_tree(const char* fn, const uint16_t* x, int64_t ldx, const uint16
     // 16-byte tile loads when no tile can straddle the end of a row (same arithmetic and bits either way)
     a.wide = aligned(x, 16) && ldx % 8 == 0 && aligned(WT, 16) && ldwt % 8 == 0 && K % 8 == 0;
     a.ep = ep;
+    a.rows = rows;
+    a.form = form;
+    if (form == 1 && !(a.wide && K <= gemv_tree_persistent_max_k() && rows <= 8))
+        return fail(GGO_EUNSUPPORTED, "%s: the persistent instance needs 16-byte operands, K <= %d and at most 8 staged rows",
+                    fn, gemv_tree_persistent_max_k());
     return launched(fn, launch_gemv_tree(a, s));
+}
+
+extern "C" {
+
+int gemv_ordered(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw, float* y, int64_t ldy, int64_t M,
+                 int64_t N, int64_t K, void* stream) {
+    return run_gemv_ordered("gemv_ordered", 0, x, ldx, W, ldw, y, ldy, M, N, K, static_cast<hipStream_t>(stream), 0);
+}
+
+int gemv_ordered_wt(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy, int64_t M,
+                    int64_t N, int64_t K, void* stream) {
+    return run_gemv_ordered("gemv_ordered_wt", 1, x, ldx, WT, ldwt, y, ldy, M, N, K, static_cast<hipStream_t>(stream), 0);
 }
 
 int gemv_tree(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy, int64_t M,
@@ -412,8 +414,10 @@ int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, i
     return launched(fn, launch_gemm_mfma_invariant_wt(a, s));
 }
 
+}  // extern "C"
+
 static int run_gemv_mfma(const char* fn, const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, void* y,
-                         int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s, const Epi& ep) {
+                         int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s, const Epi& ep, int rows = 0) {
     int rc = check_mnk(fn, M, N, K);
     if (rc) return rc;
     if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d", fn, (long long)M, GGO_GEMV_MAX_M);
@@ -439,8 +443,11 @@ static int run_gemv_mfma(const char* fn, const uint16_t* x, int64_t ldx, const u
     a.N = (int32_t)N;
     a.K = (int32_t)K;
     a.ep = ep;
+    a.rows = rows;
     return launched(fn, launch_gemv_mfma(a, s));
 }
+
+extern "C" {
 
 int gemv_mfma_invariant(const uint16_t* x, int64_t ldx, const uint16_t* WT, int64_t ldwt, float* y, int64_t ldy,
                         int64_t M, int64_t N, int64_t K, void* stream) {
@@ -459,6 +466,26 @@ int gemv_mfma_invariant_ep(const uint16_t* x, int64_t ldx, const uint16_t* WT, i
 int ggo_test_gemm_mfma_tile128(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                                int64_t M, int64_t N, int64_t K, void* stream) {
     return run_mfma("ggo_test_gemm_mfma_tile128", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), true, no_epi());
+}
+
+int ggo_test_gemv_instance(int kind, int rows, int form, const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
+                           float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+    const char* fn = "ggo_test_gemv_instance";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool tiered = kind == GGO_TEST_GEMV_TREE || kind == GGO_TEST_GEMV_MFMA;
+    if (kind < GGO_TEST_GEMV_TREE || kind > GGO_TEST_GEMV_MFMA) return fail(GGO_EINVAL, "%s: unknown kind %d", fn, kind);
+    if (tiered && !(rows == 1 || rows == 2 || rows == 4 || rows == 8 || rows == 16))
+        return fail(GGO_EINVAL, "%s: rows must be 1, 2, 4, 8 or 16", fn);
+    if (tiered && rows < M) return fail(GGO_EUNSUPPORTED, "%s: an instance staging %d rows cannot serve M=%lld", fn, rows, (long long)M);
+    if (!tiered && rows != 0) return fail(GGO_EINVAL, "%s: rows must be 0 for the ordered GEMV", fn);
+    if (kind == GGO_TEST_GEMV_MFMA ? form != 0 : (form != 1 && form != 2))
+        return fail(GGO_EINVAL, "%s: form %d is not an instance of kind %d", fn, form, kind);
+    switch (kind) {
+    case GGO_TEST_GEMV_TREE: return run_tree(fn, x, ldx, W, ldw, y, ldy, M, N, K, s, no_epi(), rows, form);
+    case GGO_TEST_GEMV_ORDERED: return run_gemv_ordered(fn, 0, x, ldx, W, ldw, y, ldy, M, N, K, s, form);
+    case GGO_TEST_GEMV_ORDERED_WT: return run_gemv_ordered(fn, 1, x, ldx, W, ldw, y, ldy, M, N, K, s, form);
+    default: return run_gemv_mfma(fn, x, ldx, W, ldw, y, ldy, M, N, K, s, no_epi(), rows);
+    }
 }
 
 const char* ggo_build_info(void) { return GGO_BUILD_INFO; }

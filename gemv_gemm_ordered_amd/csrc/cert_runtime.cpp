@@ -27,6 +27,7 @@
 #include <condition_variable>
 #include <cstring>
 #include <deque>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -68,7 +69,12 @@ struct ggo_cert {
     hipEvent_t ready_evt = nullptr;    // recorded on the caller's stream, waited on by copy_stream
     uint32_t* flags = nullptr;         // pinned, one 64-byte line per slot (Slot::flag)
     uint32_t next_seq = 0;             // under submit_mu
-    std::vector<Matrix> mats;
+    // Registered matrices. A matrix is built, stored in its own entry and only then counted (release
+    // store); readers load the count (acquire) before touching an entry, and entries never move, so a
+    // matrix may be added while checks of earlier ones run.
+    std::unique_ptr<Matrix> mats[GGO_CERT_MAX_MATRICES];
+    std::atomic<int> nmats{0};
+    std::mutex add_mu;                 // one ggo_cert_add_matrix at a time
     std::vector<Slot> slots;
     std::mutex mu;
     std::condition_variable cv_work, cv_free, cv_idle;
@@ -79,7 +85,7 @@ struct ggo_cert {
     // statistics (under mu)
     int64_t submitted = 0, checked = 0, failed = 0;
     double max_ratio = 0.0, check_seconds = 0.0, wait_seconds = 0.0, submit_wait_seconds = 0.0;
-    double submit_seconds = 0.0;   // launching thread's time inside ggo_cert_submit_rows (under submit_mu)
+    std::atomic<int64_t> submit_ns{0};   // launching thread's time inside ggo_cert_submit_rows
     std::vector<std::pair<int64_t, int>> failures;   // (token, matrix), oldest first
     int copy_error = 0;
 };
@@ -128,7 +134,7 @@ void worker_loop(ggo_cert* c) {
         bool copy_ok = true;
         const auto tw = Clock::now();
         if (sl.device) copy_ok = wait_copy(c->copy_stream, sl);
-        const Matrix& m = c->mats[sl.matrix];
+        const Matrix& m = *c->mats[sl.matrix];
         bool pass = true;
         double worst = 0.0;
         const auto t0 = Clock::now();
@@ -382,15 +388,20 @@ int ggo_cert_add_matrix(ggo_cert* c, const uint16_t* W, int64_t ld, int transpos
         m.q[k] = std::sqrt(qk);
         m.a[k] = ak;
     }
-    std::lock_guard<std::mutex> lk(c->mu);
-    c->mats.push_back(std::move(m));
-    *id = static_cast<int>(c->mats.size()) - 1;
+    std::lock_guard<std::mutex> lk(c->add_mu);
+    const int n = c->nmats.load(std::memory_order_relaxed);
+    if (n >= GGO_CERT_MAX_MATRICES) return GGO_EUNSUPPORTED;
+    c->mats[n].reset(new Matrix(std::move(m)));
+    c->nmats.store(n + 1, std::memory_order_release);
+    *id = n;
     return GGO_OK;
 }
 
+static bool matrix_known(ggo_cert* c, int id) { return id >= 0 && id < c->nmats.load(std::memory_order_acquire); }
+
 int ggo_cert_submit(ggo_cert* c, int id, const uint16_t* x_dev, const float* y_dev, int64_t token, void* stream) {
-    if (!c || c->host_only || !x_dev || !y_dev || id < 0 || id >= static_cast<int>(c->mats.size())) return GGO_EINVAL;
-    const Matrix& m = c->mats[id];
+    if (!c || c->host_only || !x_dev || !y_dev || !matrix_known(c, id)) return GGO_EINVAL;
+    const Matrix& m = *c->mats[id];
     std::lock_guard<std::mutex> one_submit(c->submit_mu);
     const int sid = take_slot(c);
     Slot& s = c->slots[sid];
@@ -418,22 +429,28 @@ int ggo_cert_submit(ggo_cert* c, int id, const uint16_t* x_dev, const float* y_d
 
 int ggo_cert_submit_rows(ggo_cert* c, int64_t n, const int* ids, const uint16_t* const* x_dev,
                          const float* const* y_dev, int64_t token, void* stream) {
-    if (!c || c->host_only || n < 1 || n > MAX_BATCH || !ids || !x_dev || !y_dev) return GGO_EINVAL;
+    // n slots are held until all are taken, so a batch larger than the ring could never be served
+    if (!c || c->host_only || n < 1 || n > MAX_BATCH || n > static_cast<int64_t>(c->slots.size()) || !ids || !x_dev ||
+        !y_dev)
+        return GGO_EINVAL;
     for (int64_t i = 0; i < n; ++i)
-        if (ids[i] < 0 || ids[i] >= static_cast<int>(c->mats.size()) || !x_dev[i] || !y_dev[i]) return GGO_EINVAL;
+        if (!matrix_known(c, ids[i]) || !x_dev[i] || !y_dev[i]) return GGO_EINVAL;
     std::lock_guard<std::mutex> one_submit(c->submit_mu);
     const auto t_submit = Clock::now();
     struct AddTime {   // on every return path
         ggo_cert* c;
         Clock::time_point t0;
-        ~AddTime() { c->submit_seconds += std::chrono::duration<double>(Clock::now() - t0).count(); }
+        ~AddTime() {
+            c->submit_ns.fetch_add(std::chrono::duration_cast<std::chrono::nanoseconds>(Clock::now() - t0).count(),
+                                   std::memory_order_relaxed);
+        }
     } add_time{c, t_submit};
     int sid[MAX_BATCH];
     take_slots(c, n, sid);
     GatherArgs ga;
     int64_t longest = 1;
     for (int64_t i = 0; i < n; ++i) {
-        const Matrix& m = c->mats[ids[i]];
+        const Matrix& m = *c->mats[ids[i]];
         Slot& s = c->slots[sid[i]];
         s.matrix = ids[i];
         s.token = token;
@@ -474,8 +491,8 @@ int ggo_cert_submit_rows(ggo_cert* c, int64_t n, const int* ids, const uint16_t*
 }
 
 int ggo_cert_submit_host(ggo_cert* c, int id, const uint16_t* x, const float* y, int64_t token) {
-    if (!c || !x || !y || id < 0 || id >= static_cast<int>(c->mats.size())) return GGO_EINVAL;
-    const Matrix& m = c->mats[id];
+    if (!c || !x || !y || !matrix_known(c, id)) return GGO_EINVAL;
+    const Matrix& m = *c->mats[id];
     const int sid = take_slot(c);
     Slot& s = c->slots[sid];
     s.matrix = id;
@@ -500,7 +517,7 @@ int ggo_cert_drain(ggo_cert* c, ggo_cert_stats* out) {
         out->copy_error = c->copy_error;
         out->wait_seconds = c->wait_seconds;
         out->submit_wait_seconds = c->submit_wait_seconds;
-        out->submit_seconds = c->submit_seconds;
+        out->submit_seconds = 1e-9 * static_cast<double>(c->submit_ns.load(std::memory_order_relaxed));
     }
     return GGO_OK;
 }

@@ -11,6 +11,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <new>
+#include <vector>
 
 #include "../../include/ggo.h"
 #include "kernels.hpp"
@@ -130,10 +132,29 @@ int freivalds_check_multi(int t, const double* s, const double* q, const double*
     }
 }
 
+namespace {
+// Sign n of the stream `seed`: the top bit of splitmix64 (Steele, Lea and Flood, OOPSLA 2014) at counter n,
+// i.e. of mix(seed + (n + 1) * 0x9E3779B97F4A7C15); a set bit gives -1.
+int8_t sign_of(uint64_t seed, int64_t n) {
+    uint64_t z = seed + (static_cast<uint64_t>(n) + 1u) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (z >> 63) ? int8_t(-1) : int8_t(1);
+}
+}  // namespace
+
+// The per-matrix state of the certificate: the signs drawn from the seed and s = W r, q, a.
+struct ggo_freivalds {
+    int64_t K = 0, N = 0;
+    std::vector<int8_t> r;
+    std::vector<double> s, q, a;
+};
+
 extern "C" {
 
-int freivalds_prepare(const uint16_t* W, int64_t ldw, int64_t K, int64_t N, const int8_t* r, double* s, double* q,
-                      double* a) {
+int freivalds_prepare_signs(const uint16_t* W, int64_t ldw, int64_t K, int64_t N, const int8_t* r, double* s,
+                            double* q, double* a) {
     if (K < 0 || N < 0 || ldw < N) return GGO_EINVAL;
     if ((K && (!s || !q || !a)) || (K && N && !W) || (N && !r)) return GGO_EINVAL;
     for (int64_t n = 0; n < N; ++n)
@@ -154,9 +175,44 @@ int freivalds_prepare(const uint16_t* W, int64_t ldw, int64_t K, int64_t N, cons
     return GGO_OK;
 }
 
-int freivalds_check(const double* s, const double* q, const double* a, const int8_t* r, int64_t K, int64_t N,
-                    const uint16_t* x, const float* y, double c_f, double* out) {
+int freivalds_check_signs(const double* s, const double* q, const double* a, const int8_t* r, int64_t K, int64_t N,
+                          const uint16_t* x, const float* y, double c_f, double* out) {
     return freivalds_check_multi(1, s, q, a, r, K, N, x, y, c_f, out);
 }
+
+int freivalds_prepare(const uint16_t* W, int64_t ldw, int64_t K, int64_t N, uint64_t seed, ggo_freivalds** out) {
+    if (!out) return GGO_EINVAL;
+    *out = nullptr;
+    if (K < 0 || N < 0 || ldw < N || (K && N && !W)) return GGO_EINVAL;
+    ggo_freivalds* f = new (std::nothrow) ggo_freivalds;
+    if (!f) return GGO_ELAUNCH;
+    f->K = K;
+    f->N = N;
+    f->r.resize(static_cast<size_t>(N));
+    for (int64_t n = 0; n < N; ++n) f->r[n] = sign_of(seed, n);
+    f->s.resize(static_cast<size_t>(K));
+    f->q.resize(static_cast<size_t>(K));
+    f->a.resize(static_cast<size_t>(K));
+    const int rc = freivalds_prepare_signs(W, ldw, K, N, f->r.data(), f->s.data(), f->q.data(), f->a.data());
+    if (rc != GGO_OK) {
+        delete f;
+        return rc;
+    }
+    *out = f;
+    return GGO_OK;
+}
+
+int freivalds_check(const ggo_freivalds* f, const uint16_t* x, const float* y, double c_f, double* out) {
+    if (!f) return GGO_EINVAL;
+    return freivalds_check_multi(1, f->s.data(), f->q.data(), f->a.data(), f->r.data(), f->K, f->N, x, y, c_f, out);
+}
+
+int freivalds_signs(const ggo_freivalds* f, int8_t* r) {
+    if (!f || (f->N && !r)) return GGO_EINVAL;
+    std::memcpy(r, f->r.data(), static_cast<size_t>(f->N));
+    return GGO_OK;
+}
+
+void freivalds_free(ggo_freivalds* f) { delete f; }
 
 }  // extern "C"

@@ -41,8 +41,10 @@ struct GemvArgs {
     int32_t M, N, K;
     uint32_t vec;
     int32_t wt;
+    int32_t form;     // 0: chosen from M (64-k stages for M <= 4, else 128-k where allowed); 1: 64-k; 2: 128-k
 };
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream);
+bool gemv_ordered_k128_ok(const GemvArgs& a);   // the 128-k stages can serve these operands
 int gemv_ordered_max_ldw();   // buffer offsets of the GEMV kernel are 32-bit
 int gemv_ordered_wt_max_ldw();   // the same for W^T: a 16-row slab of W^T in one 32-bit range
 
@@ -54,9 +56,12 @@ struct TreeArgs {
     int32_t M, N, K;
     int32_t wide;     // 16-byte loads allowed (alignment, strides and K multiples of 8)
     Epi ep;
+    int32_t rows;     // rows of x staged per workgroup (1, 2, 4, 8 or 16, >= M); 0: chosen from M
+    int32_t form;     // 0: persistent where it can serve, else one group per workgroup; 1: persistent; 2: one group
 };
 hipError_t launch_gemv_tree(const TreeArgs& a, hipStream_t stream);
 int gemv_tree_max_k();   // byte offsets along a row are 32-bit
+int gemv_tree_persistent_max_k();   // the persistent form keeps at most this many k of x per lane in registers
 
 // Float Freivalds check of one row against t <= FREIVALDS_MAX_T sign vectors in one pass (freivalds.cpp);
 // the same values and verdicts as t calls of freivalds_check.
@@ -87,6 +92,7 @@ struct GemvMfmaArgs {
     int64_t ldx, ldwt, ldy;
     int32_t M, N, K;
     Epi ep;
+    int32_t rows;     // rows of x staged per stage (1, 2, 4, 8 or 16, >= M); 0: chosen from M
 };
 hipError_t launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t stream);   // 16-byte operands, K % 8 == 0
 int gemv_mfma_max_k();   // byte offsets along a row are 32-bit

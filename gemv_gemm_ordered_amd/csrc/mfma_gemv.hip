@@ -215,11 +215,15 @@ hipError_t launch_mt(const GemvMfmaArgs& a, hipStream_t stream) {
 int gemv_mfma_max_k() { return (1 << 29) - (NST + 1) * SK; }
 
 hipError_t launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t stream) {
-    // MT (rows of x staged per stage) only sets how many rows are loaded; the instruction always
-    // covers 16, and no output's operands or order depend on it.
-    if (a.M <= 1) return launch_mt<1>(a, stream);
-    if (a.M <= 2) return launch_mt<2>(a, stream);
-    if (a.M <= 4) return launch_mt<4>(a, stream);
-    if (a.M <= 8) return launch_mt<8>(a, stream);
-    return launch_mt<16>(a, stream);
+    // MT (rows of x staged per stage: M rounded up to a power of two, or the caller's forced value) only
+    // sets how many rows are loaded; the instruction always covers 16, and no output's operands or order
+    // depend on it.
+    const int mt = a.rows ? a.rows : a.M <= 1 ? 1 : a.M <= 2 ? 2 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
+    switch (mt) {
+    case 1: return launch_mt<1>(a, stream);
+    case 2: return launch_mt<2>(a, stream);
+    case 4: return launch_mt<4>(a, stream);
+    case 8: return launch_mt<8>(a, stream);
+    default: return launch_mt<16>(a, stream);
+    }
 }

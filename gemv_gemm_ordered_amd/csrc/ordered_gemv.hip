@@ -525,12 +525,18 @@ __global__ __launch_bounds__(THREADS) void k_gemv_ordered_k128(const GemvArgs a)
 }
 }  // namespace
 
+bool gemv_ordered_k128_ok(const GemvArgs& a) {
+    return a.wt || ((a.vec & VEC_W) && a.ldw <= ((1 << 30) - (1 << 16)) / (KC2 + 1));   // 32-bit stage ranges
+}
+
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
     const dim3 grid((a.N + NS - 1) / NS, (a.M + RG - 1) / RG);
-    // M > 4 with 16-byte-capable operands: the 128-k form (same bits; see k_gemv_ordered_k128)
-    if (a.M > 4 && a.wt)
+    // M > 4 with operands it can take: the 128-k form (same bits; see k_gemv_ordered_k128); form 1 or 2
+    // forces the 64-k or the 128-k form (the caller has checked that the latter can serve)
+    const bool k128 = a.form == 2 || (a.form == 0 && a.M > 4 && gemv_ordered_k128_ok(a));
+    if (k128 && a.wt)
         hipLaunchKernelGGL((k_gemv_ordered_k128<true>), grid, dim3(THREADS), 0, stream, a);
-    else if (a.M > 4 && (a.vec & VEC_W) && a.ldw <= ((1 << 30) - (1 << 16)) / (KC2 + 1))   // 32-bit stage ranges
+    else if (k128)
         hipLaunchKernelGGL((k_gemv_ordered_k128<false>), grid, dim3(THREADS), 0, stream, a);
     else if (a.wt)
         hipLaunchKernelGGL((k_gemv_ordered<true, true>), grid, dim3(THREADS), 0, stream, a);

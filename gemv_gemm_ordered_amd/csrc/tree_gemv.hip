@@ -398,31 +398,33 @@ hipError_t launch_mt(const TreeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The instance for MT staged rows: the persistent form for 16-byte operands with at most two steps per
+// chain (MT <= 8), unless the caller forces one group per workgroup (form 2), else one group per workgroup.
 template <int MT>
 hipError_t launch_any(const TreeArgs& a, hipStream_t stream) {
-    const int steps = (a.K + TILE * CHAINS - 1) / (TILE * CHAINS);
-    if (a.wide && steps <= 1) return launch_persistent<MT, 1>(a, stream);
-    if (a.wide && steps == 2) return launch_persistent<MT, 2>(a, stream);
+    if constexpr (MT <= 8) {
+        const int steps = (a.K + TILE * CHAINS - 1) / (TILE * CHAINS);
+        if (a.form != 2 && a.wide && steps <= 1) return launch_persistent<MT, 1>(a, stream);
+        if (a.form != 2 && a.wide && steps == 2) return launch_persistent<MT, 2>(a, stream);
+    }
     return a.wide ? launch_mt<MT, true>(a, stream) : launch_mt<MT, false>(a, stream);
-}
-
-template <bool WIDE>
-hipError_t launch_w(const TreeArgs& a, hipStream_t stream) {
-    if (a.M <= 1) return launch_mt<1, WIDE>(a, stream);
-    if (a.M <= 2) return launch_mt<2, WIDE>(a, stream);
-    if (a.M <= 4) return launch_mt<4, WIDE>(a, stream);
-    if (a.M <= 8) return launch_mt<8, WIDE>(a, stream);
-    return launch_mt<16, WIDE>(a, stream);
 }
 
 }  // namespace
 
 int gemv_tree_max_k() { return (1 << 29) - 3 * TILE * CHAINS; }
 
+int gemv_tree_persistent_max_k() { return 2 * TILE * CHAINS; }
+
+// MT, the rows of x a workgroup stages, is M rounded up to a power of two (or the caller's forced
+// value): it sets how many x rows ride in registers, never an output's chains, order or tree.
 hipError_t launch_gemv_tree(const TreeArgs& a, hipStream_t stream) {
-    if (a.M <= 1) return launch_any<1>(a, stream);
-    if (a.M <= 2) return launch_any<2>(a, stream);
-    if (a.M <= 4) return launch_any<4>(a, stream);
-    if (a.M <= 8) return launch_any<8>(a, stream);
-    return a.wide ? launch_w<true>(a, stream) : launch_w<false>(a, stream);
+    const int mt = a.rows ? a.rows : a.M <= 1 ? 1 : a.M <= 2 ? 2 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
+    switch (mt) {
+    case 1: return launch_any<1>(a, stream);
+    case 2: return launch_any<2>(a, stream);
+    case 4: return launch_any<4>(a, stream);
+    case 8: return launch_any<8>(a, stream);
+    default: return launch_any<16>(a, stream);
+    }
 }

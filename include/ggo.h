@@ -20,7 +20,15 @@
  *  - C must not overlap A or W. Inputs need no particular alignment: 16-byte
  *    aligned operands with strides that are multiples of 8 take vector loads,
  *    anything else takes element loads, with the same arithmetic and bits.
- *  - No entry point selects a kernel, tile or split from M.
+ *  - Dispatch. M never chooses anything that decides an output's order: no
+ *    split of K, no tile of the matrix-core or ordered GEMM (those follow the
+ *    weight's shape and the operands' alignment). The decode GEMVs
+ *    (gemv_ordered, gemv_ordered_wt, gemv_tree, gemv_mfma_invariant) do
+ *    choose, from M, an instance of their kernel: how many rows of x a
+ *    workgroup stages (M rounded up to 1, 2, 4, 8 or 16), and for the ordered
+ *    GEMV 64- or 128-k stages. Every instance gives every output the same
+ *    chains, order and tree, hence the same bits; ggo_test_gemv_instance runs
+ *    any instance at any M so that this is tested, not assumed.
  *  - Return value: GGO_OK (0), or a negative error code; the calling thread's
  *    message is then available from ggo_last_error(). Zero-sized problems
  *    (M, N or K == 0) are valid: C is filled with +0.0 when K == 0, and nothing
@@ -324,23 +332,53 @@ int ggo_test_gemm_mfma_tile128(const uint16_t *A, int64_t lda,
                                int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * ggo_test_gemv_instance -- test hook, not a production entry point: one of
+ * the decode GEMVs executed by a chosen kernel instance instead of the one its
+ * entry point picks from M, so the tests can run every instance on the same
+ * rows at the same M and compare bits ("Taming Bitwise Behavior in GPU Kernels
+ * with Tensor Core", section 3.2.2: block sizes move work between threads but
+ * must not move the order).
+ *   kind  GGO_TEST_GEMV_TREE        gemv_tree(x, W^T): rows in {1,2,4,8,16};
+ *                                   form 1 = persistent (16-byte operands,
+ *                                   K <= 4096, rows <= 8), 2 = one group of
+ *                                   outputs per workgroup
+ *         GGO_TEST_GEMV_ORDERED     gemv_ordered(x, W): rows 0; form 1 = 64-k
+ *                                   stages, 2 = 128-k stages
+ *         GGO_TEST_GEMV_ORDERED_WT  gemv_ordered_wt(x, W^T): as above
+ *         GGO_TEST_GEMV_MFMA        gemv_mfma_invariant(x, W^T): rows in
+ *                                   {1,2,4,8,16}; form 0
+ *   rows  rows of x the instance stages per workgroup; must be >= M
+ *   The remaining arguments, their rules and errors are those of the entry
+ *   point named by kind (W is W^T [N, K] where that entry point takes W^T).
+ *   GGO_EUNSUPPORTED when the chosen instance cannot serve the operands.
+ */
+#define GGO_TEST_GEMV_TREE       0
+#define GGO_TEST_GEMV_ORDERED    1
+#define GGO_TEST_GEMV_ORDERED_WT 2
+#define GGO_TEST_GEMV_MFMA       3
+int ggo_test_gemv_instance(int kind, int rows, int form,
+                           const uint16_t *x, int64_t ldx,
+                           const uint16_t *W, int64_t ldw,
+                           float *y, int64_t ldy,
+                           int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * Float Freivalds certificate, run on the host.
  * Source: "Same Bits on the CPU and the GPU", section "The CPU as a checker: a
  * float Freivalds certificate": for a sampled GEMV y = xW and a random vector
  * r of +1/-1 over the outputs, the residual |r.y - (W r).x| is compared with a
  * bound; W r is computed once per matrix in binary64 (8 bytes per input index).
  *
- * freivalds_prepare: once per matrix.
- *   W   host, [K, N] bfloat16 bits, row stride ldw
- *   r   host, N signs, each +1 or -1 (else GGO_EINVAL)
- *   s, q, a   host, K doubles each, written:
- *       s[k] = sum_n w[k,n] r[n],  q[k] = ||w[k,:]||_2,  a[k] = sum_n |w[k,n]|
- */
-int freivalds_prepare(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
-                      const int8_t *r, double *s, double *q, double *a);
-
-/*
- * freivalds_check: one sampled row.
+ * freivalds_prepare: once per matrix. Draws the N signs from `seed` and
+ *   precomputes, in binary64, s[k] = sum_n w[k,n] r[n], q[k] = ||w[k,:]||_2 and
+ *   a[k] = sum_n |w[k,n]| (each sum over n ascending). Sign n is the top bit
+ *   of splitmix64 (Steele, Lea and Flood, OOPSLA 2014) at counter n of the
+ *   stream `seed`, i.e. of mix(seed + (n + 1) * 0x9E3779B97F4A7C15): set -> -1.
+ *   W    host, [K, N] bfloat16 bits, row stride ldw >= N; read during the call only
+ *   out  receives a handle the caller owns (free it with freivalds_free);
+ *        NULL on error. GGO_EINVAL for bad sizes or pointers, GGO_ELAUNCH when
+ *        host memory runs out.
+ * freivalds_check: one sampled row; thread safe (the handle is only read).
  *   x    host, K bfloat16 bits (the GEMV input row)
  *   y    host, N binary32 (the GPU output row, copied back by the caller)
  *   c_f  the calibrated constant (0.125 is the frozen value of the pages)
@@ -348,13 +386,33 @@ int freivalds_prepare(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
  *        rigorous bound gamma_{K-1} * sum_k |x_k| a[k] (+ host rounding), where
  *        rho = |sum_n r[n] y[n] - sum_k x[k] s[k]|,
  *        sigma = 2^-24 * sqrt(K) * sum_k |x[k]| q[k].
- * Returns 1 when rho <= tau (accept), 0 when not (reject), <0 on bad arguments.
- * A single faulty output off by delta moves rho by exactly |delta|; a fault
- * spread over outputs so that it cancels under r escapes with probability 1/2.
+ *   Returns 1 when rho <= tau (accept), 0 when not (reject), <0 on bad arguments.
+ *   A single faulty output off by delta moves rho by exactly |delta|; a fault
+ *   spread over outputs so that it cancels under r escapes with probability 1/2.
+ * freivalds_signs: copies the handle's N signs into r (host, N int8).
+ * freivalds_free: releases a handle (NULL is allowed).
  */
-int freivalds_check(const double *s, const double *q, const double *a,
-                    const int8_t *r, int64_t K, int64_t N,
-                    const uint16_t *x, const float *y, double c_f, double *out);
+typedef struct ggo_freivalds ggo_freivalds;
+
+int freivalds_prepare(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, uint64_t seed, ggo_freivalds **out);
+int freivalds_check(const ggo_freivalds *f, const uint16_t *x, const float *y, double c_f, double *out);
+int freivalds_signs(const ggo_freivalds *f, int8_t *r);
+void freivalds_free(ggo_freivalds *f);
+
+/*
+ * The same certificate for callers that draw their own signs and keep the
+ * binary64 vectors themselves (the certificate engine below holds several
+ * sign vectors per matrix this way).
+ * freivalds_prepare_signs: r host, N signs, each +1 or -1 (else GGO_EINVAL);
+ *   s, q, a host, K doubles each, written with freivalds_prepare's definitions.
+ * freivalds_check_signs: freivalds_check on those vectors (same values and
+ *   verdict as freivalds_check with a handle holding the same signs).
+ */
+int freivalds_prepare_signs(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
+                            const int8_t *r, double *s, double *q, double *a);
+int freivalds_check_signs(const double *s, const double *q, const double *a,
+                          const int8_t *r, int64_t K, int64_t N,
+                          const uint16_t *x, const float *y, double c_f, double *out);
 
 /* Target, compiler, flags and the SHA-256 of every source the library was built from. */
 const char *ggo_build_info(void);
@@ -381,7 +439,8 @@ const char *ggo_last_error(void);
  *   transpose [N, K] when `transposed` (a linear layer's weight, as gemv_tree
  *   takes it); r: nr x N signs (each +1 or -1, nr <= 64). Precomputes
  *   s_v = W r_v, q and a in binary64 (freivalds_prepare's definitions) and
- *   returns the matrix id.
+ *   returns the matrix id. At most GGO_CERT_MAX_MATRICES matrices per engine
+ *   (then GGO_EUNSUPPORTED); a matrix may be added while checks of others run.
  * ggo_cert_submit: queue the check of one output row: x_dev (device, K bf16)
  *   and y_dev (device, N binary32) are copied to a slot on the engine's stream
  *   after all work already queued on `stream`; the caller's stream does not
@@ -394,7 +453,8 @@ const char *ggo_last_error(void);
  * ggo_cert_submit_rows: ggo_cert_submit for n <= 16 rows at once (ids[i],
  *   x_dev[i], y_dev[i]): one kernel on the engine's stream writes all of them
  *   into their pinned slots, so a token's rows cost one launch instead of two
- *   runtime copies each.
+ *   runtime copies each. A batch holds its n slots until all are taken, so n
+ *   above the engine's slot count gives GGO_EINVAL (it could never be served).
  * ggo_cert_submit_host: the same from host buffers (copied before return).
  * ggo_cert_drain: wait until every submitted check has run; fill `out`.
  *   A row fails when any of its matrix's sign vectors rejects it (or its copy
@@ -404,6 +464,7 @@ const char *ggo_last_error(void);
  * ggo_cert_destroy: stop the workers (after the queued checks) and free all.
  */
 typedef struct ggo_cert ggo_cert;
+#define GGO_CERT_MAX_MATRICES 1024
 
 typedef struct ggo_cert_stats {
     int64_t submitted, checked, failed;

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_tree", "gemm_mfma_invariant",
-              "freivalds_prepare", "freivalds_check", "ggo_build_info", "ggo_last_error"):
+              "freivalds_prepare", "freivalds_check", "freivalds_free", "ggo_build_info", "ggo_last_error",
+              "ggo_test_gemv_instance"):
         assert n in names, names
 
 
@@ -92,23 +93,72 @@ def test_bad_arguments_are_rejected_without_touching_the_gpu(g):
 
 
 def test_freivalds_host_matches_oracle(g):
+    """The handle API draws its signs from the seed (splitmix64, top bit): with the seed set to the key of
+    the generator's stream they are the generator's signs, and every value and verdict equals the
+    oracle's on the same signs."""
     x, W, r = synth.decode_gemv(2, 4, k=512, n=768)
     y = oracle.gemm_ordered(x, W)
-    prep_g = g.freivalds_prepare(W, r)
+    f = g.freivalds_prepare(W, synth.stream_key(2, "gemv.r"))
+    assert np.array_equal(f.signs(), r)
+    prep_a = g.freivalds_prepare_signs(W, r)
     prep_o = oracle.freivalds_prepare(W, r)
-    for a, b in zip(prep_g, prep_o):
+    for a, b in zip(prep_a, prep_o):
         assert np.array_equal(a, b)
     for m in range(4):
         yb = y[m].copy()
         if m == 3:
             yb[100] += np.float32(0.005)
-        res_g = g.freivalds_check(prep_g, r, x[m], yb, 0.125)
+        res_h = f.check(x[m], yb, 0.125)
+        res_a = g.freivalds_check_signs(prep_a, r, x[m], yb, 0.125)
         res_o = oracle.freivalds_check(prep_o, r, x[m], yb, 0.125)
-        assert res_g[0] == res_o[0] == (m != 3)
-        assert np.allclose(res_g[1:], res_o[1:], rtol=1e-12, atol=1e-15)
+        assert res_h == res_a
+        assert res_h[0] == res_o[0] == (m != 3)
+        assert np.allclose(res_h[1:], res_o[1:], rtol=1e-12, atol=1e-15)
+    f.close()
+    f.close()   # a second close is a no-op
 
 
-def test_freivalds_rejects_bad_signs(g):
+def test_freivalds_signs_follow_the_seed(g):
+    """Sign n is the top bit of splitmix64 at counter n of the stream `seed`: the generator's definition,
+    for several seeds, including 0 and the all-ones seed."""
+    W = np.zeros((3, 1000), dtype=np.uint16)
+    for seed in (0, 1, 12345, 2 ** 64 - 1, synth.stream_key(7, "x")):
+        want = (1 - 2 * (synth.bits64(seed, 0, 1000) >> np.uint64(63)).astype(np.int64)).astype(np.int8)
+        assert np.array_equal(g.freivalds_prepare(W, seed).signs(), want), seed
+    # the two signs are about equally likely
+    r = g.freivalds_prepare(np.zeros((1, 100000), dtype=np.uint16), 99).signs()
+    assert abs(int(r.sum())) < 4 * 316
+
+
+def test_freivalds_rejects_bad_arguments(g):
     W = np.zeros((4, 4), dtype=np.uint16)
     with pytest.raises(g.GGOError):
-        g.freivalds_prepare(W, np.array([1, 0, -1, 1], dtype=np.int8))
+        g.freivalds_prepare_signs(W, np.array([1, 0, -1, 1], dtype=np.int8))
+    lib = g.lib
+    h = ct.c_void_p(1)
+    assert lib.freivalds_prepare(None, 4, 4, 4, 0, ct.byref(h)) == -1 and h.value is None   # null W
+    assert lib.freivalds_prepare(W.ctypes.data, 3, 4, 4, 0, ct.byref(h)) == -1             # ldw < N
+    assert lib.freivalds_prepare(W.ctypes.data, 4, 4, 4, 0, None) == -1                     # null out
+    out = np.empty(4)
+    assert lib.freivalds_check(None, W.ctypes.data, W.ctypes.data, 0.125, out.ctypes.data) == -1
+    lib.freivalds_free(None)
+
+
+def test_gemv_instance_hook_rejects_what_it_cannot_run(g):
+    lib, null = g.lib, None
+    # unknown kind, bad rows, rows below M, bad form: all before any GPU call
+    assert lib.ggo_test_gemv_instance(9, 1, 1, 16, 8, 16, 8, 16, 8, 1, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(0, 3, 1, 16, 8, 16, 8, 16, 8, 1, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(0, 2, 1, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -2
+    assert lib.ggo_test_gemv_instance(0, 4, 0, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(1, 4, 1, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1   # ordered takes rows 0
+    assert lib.ggo_test_gemv_instance(3, 4, 1, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1   # mfma takes form 0
+    # the persistent tree instance needs 16-byte operands, K <= 4096 and rows <= 8
+    assert lib.ggo_test_gemv_instance(0, 16, 1, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -2
+    assert lib.ggo_test_gemv_instance(0, 4, 1, 16, 8200, 16, 8200, 16, 8, 4, 8, 8200, null) == -2
+    assert lib.ggo_test_gemv_instance(0, 4, 1, 18, 8, 16, 8, 16, 8, 4, 8, 8, null) == -2
+    # the 128-k ordered instance needs 4-byte column pairs of W
+    assert lib.ggo_test_gemv_instance(1, 0, 2, 16, 8, 16, 7, 16, 8, 4, 7, 8, null) == -2
+    assert lib.ggo_test_gemv_instance(1, 0, 2, 16, 8, 18, 8, 16, 8, 4, 8, 8, null) == -2
+    # empty problems launch nothing
+    assert lib.ggo_test_gemv_instance(0, 1, 2, null, 8, null, 8, null, 8, 0, 8, 8, null) == 0

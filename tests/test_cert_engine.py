@@ -125,3 +125,31 @@ def test_bad_arguments(g, data):
     with pytest.raises(g.GGOError):
         eng.add_matrix(np.zeros((1024, 768), np.uint16), signs(1, 1, 768))   # K above max_K
     eng.close()
+
+
+def test_matrices_added_while_checks_run(g, data):
+    """Matrices registered while other rows are being checked: every earlier matrix stays valid (entries
+    never move), every row is checked against its own matrix, and an unknown id is refused."""
+    import threading
+    x, W, y = data
+    eng = g.CertEngine(512, 768, slots=4, workers=3, host_only=True)
+    mid0 = eng.add_matrix(W, signs(11, 1, 768))
+    added = []
+
+    def adder():
+        for i in range(40):
+            added.append(eng.add_matrix(W, signs(20 + i, 1, 768)))
+
+    th = threading.Thread(target=adder)
+    th.start()
+    for i in range(300):
+        eng.submit_host(mid0 if i % 3 or not added else added[-1], x[i % 8], y[i % 8], token=i)
+    th.join()
+    for mid in added:
+        eng.submit_host(mid, x[mid % 8], y[mid % 8], token=1000 + mid)
+    st = eng.drain()
+    assert added == list(range(1, 41))
+    assert st["checked"] == 340 and st["failed"] == 0
+    xr, yr = np.ascontiguousarray(x[0]), np.ascontiguousarray(y[0])
+    assert g.lib.ggo_cert_submit_host(eng.h, 41, xr.ctypes.data, yr.ctypes.data, 0) == -1
+    eng.close()

@@ -134,3 +134,21 @@ def test_late_copy_takes_the_stream_path(g):
     assert st["wait_seconds"] > 0.002, st
     eng.close()
     del C
+
+
+def test_batch_larger_than_the_ring_is_refused(g):
+    """A batch holds its slots until all are taken, so one larger than the ring could never be served: the
+    call must return an error at once instead of waiting forever."""
+    import torch
+    WT = synth.normal_bf16(3, "certr.WT", (64, 128), 0.02)
+    eng = g.CertEngine(128, 64, slots=2, workers=1)
+    mid = eng.add_matrix(WT, synth.rademacher(3, "certr.r", 64)[None, :], transposed=True)
+    x = dev_bf16(synth.normal_bf16(3, "certr.x", (3, 128)))
+    y = g.gemv_tree(x, dev_bf16(WT))
+    with pytest.raises(g.GGOError):
+        eng.submit_rows([mid] * 3, [x[i] for i in range(3)], [y[i] for i in range(3)], token=0)
+    eng.submit_rows([mid] * 2, [x[i] for i in range(2)], [y[i] for i in range(2)], token=1)
+    st = eng.drain()
+    torch.cuda.synchronize()
+    assert st["submitted"] == st["checked"] == 2 and st["failed"] == 0 and not st["copy_error"]
+    eng.close()

@@ -18,14 +18,16 @@ def test_gpu_gemv_certified(tmp_path):
     y = g.gemv_ordered(dev_bf16(x), dev_bf16(W))
     torch.cuda.synchronize()
     yh = y.cpu().numpy()
-    prep = g.freivalds_prepare(W, r)
+    f = g.freivalds_prepare(W, synth.stream_key(0, "gemv.r"))
+    assert np.array_equal(f.signs(), r)
     j = int(synth.bits64(synth.stream_key(0, "fault.j"), 0, 1)[0] % 4096)
     oprep = oracle.freivalds_prepare(W, r)
     for m in range(8):
-        ok, rho, sigma, tau, bound = g.freivalds_check(prep, r, x[m], yh[m])
+        ok, rho, sigma, tau, bound = f.check(x[m], yh[m])
         assert ok and rho <= bound, (m, rho, tau)
         assert oracle.freivalds_check(oprep, r, x[m], yh[m])[0]
         for delta in (0.005, 0.05):
             yb = yh[m].copy()
             yb[j] += np.float32(delta)
-            assert not g.freivalds_check(prep, r, x[m], yb)[0]
+            assert not f.check(x[m], yb)[0]
+            assert not oracle.freivalds_check(oprep, r, x[m], yb)[0]

@@ -63,6 +63,18 @@ def test_ragged_shapes(g, M, N, K, a_dtype):
     assert np.array_equal(host_bits(g.gemm_ordered(dA, dev_bf16(W))), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(37, 1100, 1001), (70, 2048, 1000), (5, 1056, 1992), (130, 1040, 1016)])
+def test_ragged_shapes_on_the_64x64_tile(g, M, N, K):
+    """Weights of more than 2^20 elements take the 64 x 64 tile: its element loads (odd K or N) and, with
+    K and N multiples of 8, its wide loads with a partial last k-step (K not a multiple of 32)."""
+    A = synth.normal_bf16(M + N + K, "rag64.A", (M, K))
+    W = synth.normal_bf16(M + N + K, "rag64.W", (K, N), 0.02)
+    assert N * K > 1 << 20
+    say(f"gemm_ordered 64x64 tile ragged M={M} N={N} K={K}")
+    ref = f32_bits(oracle.gemm_ordered(A, W, threads=8))
+    assert np.array_equal(host_bits(g.gemm_ordered(dev_bf16(A), dev_bf16(W))), ref)
+
+
 def test_strided_and_misaligned_views(g):
     A, W = synth.mlp_up(4, 96)
     # row strides not multiples of 8, base pointers off 16-byte alignment
@@ -244,3 +256,57 @@ def test_pv_long_sequences_sampled_rows(g):
         for h in range(heads):
             ref = f32_bits(oracle.gemm_ordered(np.ascontiguousarray(P[h][rows]), V[h]))
             assert np.array_equal(got[h][rows], ref), (L, h)
+
+
+def _device_pv(L, heads, seed):
+    """P = softmax of N(0, 1) logits (binary32, on the device) and V ~ N(0, 1) bf16 for one sequence of the
+    value product at its full size; drawn with torch's seeded generator on the device, since a host draw of
+    32 x 5000 x 5000 values would take minutes. Both sides read the same bytes."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    P = torch.softmax(torch.randn((heads, L, L), device="cuda", generator=gen), dim=-1)
+    V = torch.randn((heads, L, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    return P, V
+
+
+def _pv_rows_vs_oracle(P, V, O, rows, what):
+    import torch
+    torch.cuda.synchronize()
+    for h in range(P.shape[0]):
+        Ph = P[h, rows].cpu().numpy()
+        Vh = V[h].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = f32_bits(oracle.gemm_ordered(np.ascontiguousarray(Ph), Vh))
+        got = O[h, rows].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, ref), (what, h, rows)
+
+
+def test_pv_full_size_32_heads(g):
+    """The value product at the configuration's full size: 32 heads at L = 5000 (P is 3.2 GB, so the later
+    heads sit more than 2^31 bytes past P's start) and 32 heads at L = 1024 in one launch, then a mixed
+    batch with both among short sequences in another order; sampled rows of every head, head 31
+    included, against the oracle, and each output equal bit for bit across the two launches."""
+    import torch
+    say("pv full size: drawing P and V on the device (L=5000 and L=1024, 32 heads)")
+    P5, V5 = _device_pv(5000, 32, 50)
+    P1, V1 = _device_pv(1024, 32, 51)
+    P15, V15 = _device_pv(15, 32, 52)
+    P16, V16 = _device_pv(16, 32, 53)
+    assert P5[31].data_ptr() - P5.data_ptr() > 1 << 31     # head 31 starts past 2^31 bytes
+    O5 = torch.full((32, 5000, 128), float("nan"), device="cuda")
+    O1 = torch.full((32, 1024, 128), float("nan"), device="cuda")
+    say("pv full size: 32 x L=5000 + 32 x L=1024 in one launch")
+    g.gemm_ordered_grouped([(P5, V5, O5), (P1, V1, O1)])
+    _pv_rows_vs_oracle(P5, V5, O5, [0, 1, 2500, 4998, 4999], "L=5000")
+    _pv_rows_vs_oracle(P1, V1, O1, [0, 511, 1023], "L=1024")
+    assert not torch.isnan(O5).any() and not torch.isnan(O1).any()
+    say("pv full size: mixed batch [15, 5000, 16, 1024] in another order")
+    M5, M1 = torch.empty_like(O5), torch.empty_like(O1)
+    M15 = torch.empty((32, 15, 128), device="cuda")
+    M16 = torch.empty((32, 16, 128), device="cuda")
+    g.gemm_ordered_grouped([(P15, V15, M15), (P1, V1, M1), (P16, V16, M16), (P5, V5, M5)])
+    torch.cuda.synchronize()
+    assert torch.equal(M5.view(torch.int32), O5.view(torch.int32))
+    assert torch.equal(M1.view(torch.int32), O1.view(torch.int32))
+    _pv_rows_vs_oracle(P15, V15, M15, list(range(15)), "L=15")
+    _pv_rows_vs_oracle(P16, V16, M16, list(range(16)), "L=16")

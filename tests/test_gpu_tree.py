@@ -44,6 +44,20 @@ def test_row_content_at_any_position(g, decode):
         assert np.array_equal(got[pos], ref[9]), (M, pos)
 
 
+@pytest.mark.parametrize("N,K", [(11008, 4096), (4096, 11008)])
+def test_7b_decode_shapes(g, N, K):
+    """The up- and down-projection decode shapes of a 7B layer (the persistent form at K = 4096, the
+    one-group form at K = 11008), every row of M = 1 and M = 8 against the oracle."""
+    x = synth.normal_bf16(7, f"tree7b.x{K}", (8, K))
+    WT = synth.normal_bf16(7, f"tree7b.WT{N}x{K}", (N, K), 0.02)
+    say(f"gemv_tree 7B shape N={N} K={K}: oracle")
+    ref = f32_bits(oracle.gemv_tree(x, WT, threads=16))
+    dx, dWT = dev_bf16(x), dev_bf16(WT)
+    for M in (1, 8):
+        got = host_bits(g.gemv_tree(dx[:M], dWT))
+        assert np.array_equal(got, ref[:M]), (N, K, M, int(np.count_nonzero(got != ref[:M])))
+
+
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 1), (1, 7, 8), (2, 9, 2047), (3, 13, 2048), (5, 100, 2049), (8, 4095, 4096), (16, 33, 4100),
     (4, 17, 6144), (9, 5, 6152), (16, 3, 777), (7, 600, 16392), (1, 1000, 3),
