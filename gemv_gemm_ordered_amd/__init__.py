@@ -76,6 +76,7 @@ def _load():
     lib.gemv_mfma_invariant_ep.argtypes = [P, I64, P, I64, ct.POINTER(Epilogue), P, I64, I64, I64, I64, P]
     PP = ct.POINTER(ct.c_void_p)
     lib.ggo_test_gemv_instance.argtypes = [I, I, I, P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.ggo_test_gemm_ordered_tile.argtypes = [I, P, I, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.freivalds_prepare.argtypes = [P, I64, I64, I64, ct.c_uint64, PP]
     lib.freivalds_check.argtypes = [P, P, P, ct.c_double, P]
     lib.freivalds_signs.argtypes = [P, P]
@@ -101,7 +102,8 @@ def _load():
     lib.ggo_last_error.restype = ct.c_char_p
     for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered_wt", "gemv_tree", "gemv_tree_ep",
               "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
-              "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "gemm_mfma_invariant_wt", "gemv_mfma_invariant",
+              "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "ggo_test_gemm_ordered_tile",
+              "gemm_mfma_invariant_wt", "gemv_mfma_invariant",
               "gemv_mfma_invariant_ep", "freivalds_prepare", "freivalds_check", "freivalds_signs",
               "freivalds_prepare_signs", "freivalds_check_signs"):
         getattr(lib, f).restype = I
@@ -113,7 +115,8 @@ lib = _load()
 EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered_wt", "gemv_tree", "gemv_tree_ep",
            "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
            "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep",
-           "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "freivalds_prepare", "freivalds_check",
+           "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "ggo_test_gemm_ordered_tile",
+           "freivalds_prepare", "freivalds_check",
            "freivalds_signs", "freivalds_free", "freivalds_prepare_signs", "freivalds_check_signs",
            "ggo_build_info", "ggo_last_error",
            "ggo_cert_create", "ggo_cert_create_host", "ggo_cert_add_matrix", "ggo_cert_submit", "ggo_cert_submit_rows",
@@ -183,6 +186,28 @@ def gemm_ordered(A, W, C=None, stream=None):
     ldc = _rowmajor(C, "C") if M and N else N
     _raise(lib.gemm_ordered(A.data_ptr(), ad, lda, W.data_ptr(), ldw, C.data_ptr(), ldc, M, N, K, _stream(stream)),
            "gemm_ordered")
+    return C
+
+
+ORDERED_TILES = {"64x64": 0, "16x16": 1, "64x32": 2}
+
+
+def test_gemm_ordered_tile(tile, A, W, C=None, stream=None):
+    """Test hook: gemm_ordered on the chosen tile ('64x64', '64x32' or '16x16'); must give gemm_ordered's
+    bits."""
+    torch = _torch()
+    lda, ldw = _rowmajor(A, "A"), _rowmajor(W, "W")
+    M, K = A.shape
+    if W.shape[0] != K or not _is_bf16(W):
+        raise ValueError("W must be bf16 [K, N]")
+    N = W.shape[1]
+    ad = GGO_BF16 if _is_bf16(A) else GGO_F32 if A.dtype == torch.float32 else None
+    if ad is None:
+        raise ValueError(f"A must be bf16 or float32, got {A.dtype}")
+    C = _out(C, M, N, A)
+    ldc = _rowmajor(C, "C") if M and N else N
+    _raise(lib.ggo_test_gemm_ordered_tile(ORDERED_TILES[tile], A.data_ptr(), ad, lda, W.data_ptr(), ldw, C.data_ptr(),
+                                          ldc, M, N, K, _stream(stream)), "ggo_test_gemm_ordered_tile")
     return C
 
 

@@ -99,7 +99,7 @@ int make_epi(const char* fn, const ggo_epilogue* e, int64_t N, Epi* out) {
     return GGO_OK;
 }
 
-int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, int small, OrdProblem& p, int64_t& tiles) {
+int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, int kind, OrdProblem& p, int64_t& tiles) {
     int rc = check_mnk(fn, q.M, q.N, q.K);
     if (rc) return rc;
     if (q.batch < 0) return fail(GGO_EINVAL, "%s: negative batch", fn);
@@ -112,7 +112,7 @@ int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, int small, O
             return fail(GGO_EINVAL, "%s: negative batch stride", fn);
     }
     int bm, bn;
-    ordered_tile_shape(small, &bm, &bn);
+    ordered_tile_shape(kind, &bm, &bn);
     p.A = q.A;
     p.W = q.W;
     p.C = q.C;
@@ -139,13 +139,15 @@ int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, int small, O
     return GGO_OK;
 }
 
-// Tile of the ordered kernel: the 16 x 16 tile for gemm_ordered on a weight of at most 2^20 elements
-// (one output per lane, so small weights fill the chip at small M), else 64 x 64. The choice depends on
-// the entry point and the weight's shape, never on M; every output's chain, and so its bits, is the
-// same under either tile. Grouped launches (the value product) keep 64 x 64.
-constexpr int64_t ORDERED_SMALL_WEIGHT = int64_t(1) << 20;
+// Tile of the ordered kernel, for gemm_ordered: 16 x 16 (one output per lane) on a weight of at most
+// 2^20 elements, 64 x 32 (4 x 2 per lane) on one of at most 2^22, else 64 x 64 (4 x 4 per lane): the
+// smaller the weight, the more outputs a tile gives up so that the weight still fills the chip at small
+// M. The choice depends on the entry point and the weight's shape, never on M; every output's chain,
+// and so its bits, is the same under every tile. Grouped launches (the value product) keep 64 x 64.
+constexpr int64_t ORDERED_SMALL_WEIGHT = int64_t(1) << 20, ORDERED_MID_WEIGHT = int64_t(1) << 22;
 
-int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype, int small_ok, hipStream_t s) {
+int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype, int small_ok, hipStream_t s,
+              int force_kind = -1) {
     if (a_dtype != GGO_BF16 && a_dtype != GGO_F32) return fail(GGO_EINVAL, "%s: a_dtype must be GGO_BF16 or GGO_F32", fn);
     if (!qs) return fail(GGO_EINVAL, "%s: null problem array", fn);
     if (count < 1 || count > GGO_MAX_PROBLEMS) return fail(GGO_EINVAL, "%s: count must be 1..%d", fn, GGO_MAX_PROBLEMS);
@@ -153,12 +155,16 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     std::memset(&g, 0, sizeof g);
     int64_t total = 0;
     int n = 0;
-    const int small = small_ok && count == 1 && qs[0].batch == 1 && qs[0].N * qs[0].K <= ORDERED_SMALL_WEIGHT;
+    const bool single = small_ok && count == 1 && qs[0].batch == 1;
+    const int kind = force_kind >= 0                                            ? force_kind
+                   : single && qs[0].N * qs[0].K <= ORDERED_SMALL_WEIGHT ? ORD_TILE_SMALL
+                   : single && qs[0].N * qs[0].K <= ORDERED_MID_WEIGHT   ? ORD_TILE_MID
+                                                                         : ORD_TILE_BIG;
     int wide = 1;   // the launch takes the wide loads only if every problem allows them
     for (int64_t i = 0; i < count; ++i) {
         int64_t tiles = 0;
         OrdProblem p;
-        int rc = fill_problem(fn, qs[i], a_dtype, small, p, tiles);
+        int rc = fill_problem(fn, qs[i], a_dtype, kind, p, tiles);
         if (rc) return rc;
         if (qs[i].K == 0 && qs[i].M && qs[i].N) {
             // empty folds: +0.0 for every output of every batch entry
@@ -169,7 +175,7 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
             continue;
         }
         if (tiles == 0) continue;
-        const int64_t max_ld = ordered_wide_max_ld(small, a_dtype == GGO_F32);
+        const int64_t max_ld = ordered_wide_max_ld(kind, a_dtype == GGO_F32);
         if (!((p.vec & VEC_A) && (p.vec & VEC_W) && p.K % 8 == 0 && p.N % 8 == 0 && p.lda <= max_ld && p.ldw <= max_ld))
             wide = 0;
         g.p[n] = p;
@@ -181,7 +187,7 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     if (n == 0) return ok();
     g.count = n;
     g.tile_start[n] = (int32_t)total;
-    return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, small, wide, s));
+    return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, kind, wide, s));
 }
 
 // The 256x128 instance needs 16-byte aligned operands with row strides that
@@ -255,6 +261,29 @@ int gemm_ordered(const void* A, int a_dtype, int64_t lda, const uint16_t* W, int
 
 int gemm_ordered_grouped(const ggo_problem* problems, int64_t count, int a_dtype, void* stream) {
     return run_group("gemm_ordered_grouped", problems, count, a_dtype, 0, static_cast<hipStream_t>(stream));
+}
+
+int ggo_test_gemm_ordered_tile(int tile, const void* A, int a_dtype, int64_t lda, const uint16_t* W, int64_t ldw, float* C,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+    const char* fn = "ggo_test_gemm_ordered_tile";
+    if (tile != GGO_TEST_ORDERED_TILE_64x64 && tile != GGO_TEST_ORDERED_TILE_16x16 && tile != GGO_TEST_ORDERED_TILE_64x32)
+        return fail(GGO_EINVAL, "%s: unknown tile %d", fn, tile);
+    const int kind = tile == GGO_TEST_ORDERED_TILE_16x16 ? ORD_TILE_SMALL
+                   : tile == GGO_TEST_ORDERED_TILE_64x32 ? ORD_TILE_MID
+                                                         : ORD_TILE_BIG;
+    ggo_problem q;
+    q.A = A;
+    q.W = W;
+    q.C = C;
+    q.lda = lda;
+    q.ldw = ldw;
+    q.ldc = ldc;
+    q.batch = 1;
+    q.stride_a = q.stride_w = q.stride_c = 0;
+    q.M = M;
+    q.N = N;
+    q.K = K;
+    return run_group(fn, &q, 1, a_dtype, 1, static_cast<hipStream_t>(stream), kind);
 }
 
 }  // extern "C"

@@ -26,12 +26,14 @@ struct OrdGroup {
     OrdProblem p[GGO_MAX_PROBLEMS];
 };
 
-// small != 0: the 16 x 16 tile (one output per lane), for single-problem launches on small weights
-void ordered_tile_shape(int small, int* bm, int* bn);
+// Tile of the ordered kernel: 64 x 64 (4 x 4 per lane), 64 x 32 (4 x 2 per lane) or 16 x 16 (one output
+// per lane); the caller chooses from the weight's shape and the entry point, never from M.
+enum { ORD_TILE_BIG = 0, ORD_TILE_SMALL = 1, ORD_TILE_MID = 2 };
+void ordered_tile_shape(int kind, int* bm, int* bn);
 // wide != 0: every problem has 16-byte aligned A, W, row strides (and batch strides) of whole 16-byte
-// chunks, K and N multiples of 8, and lda, ldw <= ordered_wide_max_ld(small, a_f32)
-hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, int wide, hipStream_t stream);
-int64_t ordered_wide_max_ld(int small, int a_f32);
+// chunks, K and N multiples of 8, and lda, ldw <= ordered_wide_max_ld(kind, a_f32)
+hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int kind, int wide, hipStream_t stream);
+int64_t ordered_wide_max_ld(int kind, int a_f32);
 
 struct GemvArgs {
     const uint16_t* x;

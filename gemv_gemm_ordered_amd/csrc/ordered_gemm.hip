@@ -27,9 +27,13 @@ namespace {
 
 constexpr int THREADS = 256, APAD = 4;
 
-// Tile shapes. Both give every output the same chain, so the same bits; which one a launch uses
+// Tile shapes. All give every output the same chain, so the same bits; which one a launch uses
 // depends only on the weight's shape and the entry point, never on M.
 //   Big:   64 x 64 outputs, 32-k steps, a 4 x 4 micro-tile per lane (16 chains: the VALU stays busy).
+//   Mid:   64 x 32 outputs, 32-k steps, a 4 x 2 micro-tile (8 chains), for weights of 2^20 < N K <=
+//          2^22: twice the workgroups of the big tile at every M, so at M = 256 on a 1024 x 4096 weight
+//          each SIMD holds two waves instead of one (one wave alone issues binary32 operations at
+//          about half the rate two waves reach).
 //   Small: 16 x 16 outputs, 128-k steps, one output per lane, for small weights (N K <= 2^20): at
 //          M <= 64 the big tile leaves most CUs idle (12 workgroups for a 768 x 768 weight) and each
 //          lane's 16 chains run one after another.
@@ -37,10 +41,13 @@ constexpr int THREADS = 256, APAD = 4;
 template <int BM_, int BN_, int BK_, int TM_, int TN_, int DEPTH_> struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, TM = TM_, TN = TN_, DEPTH = DEPTH_;
     static constexpr int CA = BK / 8, CW = BN / 8;   // 8-element chunks per A row / per W k-row
-    static_assert(BM * CA == THREADS && BK * CW == THREADS, "each thread loads one chunk of A and one of W");
+    static constexpr int WCH = BK * CW;               // W chunks per k-step: threads 0 .. WCH-1 load one each
+    static_assert(BM * CA == THREADS && WCH <= THREADS && WCH % 64 == 0,
+                  "each thread loads one chunk of A; whole waves load one chunk of W each");
     static_assert((BM / TM) * (BN / TN) == THREADS, "one micro-tile per lane");
 };
 using BigTile = Tile<64, 64, 32, 4, 4, 1>;
+using MidTile = Tile<64, 32, 32, 4, 2, 1>;
 using SmallTile = Tile<16, 16, 128, 1, 1, 1>;   // deeper rings measured no faster
 
 // One 8-element chunk as loaded: bf16 pairs in u[0..3] (element 2i in the low half of u[i]) or eight
@@ -82,6 +89,7 @@ GGO_DEV void load_a(const OrdProblem& P, const void* Abase, int m0, int k0, int 
 
 template <class T>
 GGO_DEV void load_w(const OrdProblem& P, const uint16_t* Wb, int n0, int k0, int t, Chunk& out) {
+    if (T::WCH < THREADS && t >= T::WCH) return;   // uniform per wave: this wave loads no W
     const int kr = t / T::CW, nc = (t % T::CW) * 8;
     const int k = k0 + kr, n = n0 + nc;
     const uint16_t* W = Wb + static_cast<int64_t>(k) * P.ldw + n;
@@ -125,6 +133,7 @@ GGO_DEV void load_a_wide(const OrdProblem& P, const void* Abase, int m0, int k0,
 
 template <class T>
 GGO_DEV void load_w_wide(const OrdProblem& P, const uint16_t* Wb, int n0, int k0, int t, Chunk& out) {
+    if (T::WCH < THREADS && t >= T::WCH) return;   // uniform per wave: this wave loads no W
     const int kr = t / T::CW, nc = (t % T::CW) * 8;
     const int krows = P.K - k0 < T::BK ? P.K - k0 : T::BK;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -147,6 +156,7 @@ GGO_DEV void store_tiles(float (*As)[T::BM + APAD], float (*Ws)[T::BN], int t, c
     const int r = t / T::CA, kc = (t % T::CA) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) As[kc + i][r] = elem<AF32>(a, i);
+    if (T::WCH < THREADS && t >= T::WCH) return;   // uniform per wave
     const int kr = t / T::CW, nc = (t % T::CW) * 8;
     *reinterpret_cast<float4*>(&Ws[kr][nc]) = make_float4(elem<0>(w, 0), elem<0>(w, 1), elem<0>(w, 2), elem<0>(w, 3));
     *reinterpret_cast<float4*>(&Ws[kr][nc + 4]) = make_float4(elem<0>(w, 4), elem<0>(w, 5), elem<0>(w, 6), elem<0>(w, 7));
@@ -167,6 +177,9 @@ GGO_DEV void fold_step(float (&acc)[T::TM][T::TN], const float (*As)[T::BM + APA
     if constexpr (T::TN == 4) {
         const float4 w4 = *reinterpret_cast<const float4*>(&Ws[kk][tx * 4]);
         w[0] = w4.x; w[1] = w4.y; w[2] = w4.z; w[3] = w4.w;
+    } else if constexpr (T::TN == 2) {
+        const float2 w2 = *reinterpret_cast<const float2*>(&Ws[kk][tx * 2]);
+        w[0] = w2.x; w[1] = w2.y;
     } else {
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) w[j] = Ws[kk][tx * T::TN + j];
@@ -270,10 +283,13 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
                             acc[0][0] = acc[0][0] + p;
                         }
                     }
-                } else {
+                } else if constexpr (T::TN == 4) {
                     // 4 x 4 micro-tile: the next k's two 16-byte reads are issued before this k's 32
-                    // operations (the same reasoning at small M, where a CU holds one workgroup)
-                    static_assert(T::TM == 4 && T::TN == 4, "");
+                    // operations (the same reasoning at small M, where a CU holds one workgroup). Taking A
+                    // through a DPP row broadcast instead (the 16 lanes of a row share their rows of A, so
+                    // one 4-byte read per lane covers four k) measured slower: 36.7 against 50.2 TFLOP/s at
+                    // M = 2048 on the 1024 x 4096 weight, same bits.
+                    static_assert(T::TM == 4, "");
                     float4 a4[2], w4[2];
                     a4[0] = *reinterpret_cast<const float4*>(&As[0][ty * 4]);
                     w4[0] = *reinterpret_cast<const float4*>(&Ws[0][tx * 4]);
@@ -289,6 +305,29 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
+                                const float p = a[i] * w[j];   // first rounding
+                                acc[i][j] = acc[i][j] + p;     // second rounding
+                            }
+                    }
+                } else {
+                    // 4 x 2 micro-tile: the same schedule with an 8-byte read of W
+                    static_assert(T::TM == 4 && T::TN == 2, "");
+                    float4 a4[2];
+                    float2 w2[2];
+                    a4[0] = *reinterpret_cast<const float4*>(&As[0][ty * 4]);
+                    w2[0] = *reinterpret_cast<const float2*>(&Ws[0][tx * 2]);
+#pragma unroll
+                    for (int kk = 0; kk < BK; ++kk) {
+                        if (kk + 1 < BK) {
+                            a4[(kk + 1) & 1] = *reinterpret_cast<const float4*>(&As[kk + 1][ty * 4]);
+                            w2[(kk + 1) & 1] = *reinterpret_cast<const float2*>(&Ws[kk + 1][tx * 2]);
+                        }
+                        const float a[4] = {a4[kk & 1].x, a4[kk & 1].y, a4[kk & 1].z, a4[kk & 1].w};
+                        const float w[2] = {w2[kk & 1].x, w2[kk & 1].y};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
                                 const float p = a[i] * w[j];   // first rounding
                                 acc[i][j] = acc[i][j] + p;     // second rounding
                             }
@@ -317,6 +356,11 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
                 *reinterpret_cast<float4*>(c) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
                 done = true;
             }
+        } else if constexpr (TN == 2) {
+            if (col + TN <= P.N && (P.vec & VEC_C)) {
+                *reinterpret_cast<float2*>(c) = make_float2(acc[i][0], acc[i][1]);
+                done = true;
+            }
         }
         if (!done) {
 #pragma unroll
@@ -328,28 +372,34 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
 
 }  // namespace
 
-void ordered_tile_shape(int small, int* bm, int* bn) {
-    *bm = small ? SmallTile::BM : BigTile::BM;
-    *bn = small ? SmallTile::BN : BigTile::BN;
+void ordered_tile_shape(int kind, int* bm, int* bn) {
+    *bm = kind == ORD_TILE_SMALL ? SmallTile::BM : kind == ORD_TILE_MID ? MidTile::BM : BigTile::BM;
+    *bn = kind == ORD_TILE_SMALL ? SmallTile::BN : kind == ORD_TILE_MID ? MidTile::BN : BigTile::BN;
 }
 
-hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int small, int wide, hipStream_t stream) {
+template <class T>
+void launch_tile(const OrdGroup& g, int total_tiles, int a_f32, int wide, hipStream_t stream) {
     const dim3 grid(total_tiles), block(THREADS);
-#define GGO_ORDERED_LAUNCH(TILE, F32, W) hipLaunchKernelGGL((k_gemm_ordered<TILE, F32, W>), grid, block, 0, stream, g)
-    if (small) {
-        if (wide) { if (a_f32) GGO_ORDERED_LAUNCH(SmallTile, 1, true); else GGO_ORDERED_LAUNCH(SmallTile, 0, true); }
-        else { if (a_f32) GGO_ORDERED_LAUNCH(SmallTile, 1, false); else GGO_ORDERED_LAUNCH(SmallTile, 0, false); }
+    if (wide) {
+        if (a_f32) hipLaunchKernelGGL((k_gemm_ordered<T, 1, true>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((k_gemm_ordered<T, 0, true>), grid, block, 0, stream, g);
     } else {
-        if (wide) { if (a_f32) GGO_ORDERED_LAUNCH(BigTile, 1, true); else GGO_ORDERED_LAUNCH(BigTile, 0, true); }
-        else { if (a_f32) GGO_ORDERED_LAUNCH(BigTile, 1, false); else GGO_ORDERED_LAUNCH(BigTile, 0, false); }
+        if (a_f32) hipLaunchKernelGGL((k_gemm_ordered<T, 1, false>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((k_gemm_ordered<T, 0, false>), grid, block, 0, stream, g);
     }
-#undef GGO_ORDERED_LAUNCH
+}
+
+hipError_t launch_gemm_ordered(const OrdGroup& g, int total_tiles, int a_f32, int kind, int wide, hipStream_t stream) {
+    if (kind == ORD_TILE_SMALL) launch_tile<SmallTile>(g, total_tiles, a_f32, wide, stream);
+    else if (kind == ORD_TILE_MID) launch_tile<MidTile>(g, total_tiles, a_f32, wide, stream);
+    else launch_tile<BigTile>(g, total_tiles, a_f32, wide, stream);
     return hipGetLastError();
 }
 
 // Largest row stride (elements) the wide form takes: its byte ranges and offsets stay below 2^30.
-int64_t ordered_wide_max_ld(int small, int a_f32) {
-    const int64_t rows = small ? (SmallTile::BK > SmallTile::BM ? SmallTile::BK : SmallTile::BM)
-                               : (BigTile::BK > BigTile::BM ? BigTile::BK : BigTile::BM);
+int64_t ordered_wide_max_ld(int kind, int a_f32) {
+    const int64_t rows = kind == ORD_TILE_SMALL ? (SmallTile::BK > SmallTile::BM ? SmallTile::BK : SmallTile::BM)
+                       : kind == ORD_TILE_MID   ? (MidTile::BK > MidTile::BM ? MidTile::BK : MidTile::BM)
+                                                : (BigTile::BK > BigTile::BM ? BigTile::BK : BigTile::BM);
     return (int64_t(1) << 30) / ((rows + 1) * (a_f32 ? 4 : 2));
 }

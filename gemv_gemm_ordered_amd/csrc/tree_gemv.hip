@@ -366,16 +366,21 @@ int device_cus() {
 }
 
 // Persistent launch: R outputs per group, NB groups in rotation, two workgroups per CU (8 waves).
-// Measured on the decode shape (N = K = 4096): smaller groups keep more workgroups streaming at
-// M = 4 and 8, where the fold per group is largest; deeper rotation (NB = 3, 4) spreads the requests
-// in flight over more of the matrix and reads slower.
+// Measured on the decode shape (N = K = 4096): two outputs per group at M <= 4 (M = 1: 6.8 us against
+// 7.0 with four), one at M = 8, where the fold per group is largest. Slower, each measured at M = 8 in
+// the same process: deeper rotation (NB = 3, 4: 9.5, 9.9 against 9.0 us); three workgroups per CU or one
+// (9.6, 11.3); issuing the first groups' weight loads before the x tiles are widened (no change);
+// raising the wave priority around the weight loads (no change); splitting the rows of x over twice or
+// four times the waves, each set fetching the same weight tiles (10.8-17.7); producer waves streaming
+// the weight into an LDS ring with direct-to-LDS loads and four folding waves (12.3-15.2: a barrier per
+// group exposes one stage's latency to the whole workgroup).
 template <int MT, int S>
 hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
     // RB: groups per cross-wave batch. At M = 8 a barrier per group kept the waves in step and the folds
     // from overlapping the stream (R = 2: 9.6 us; batches of 4: 9.2 us; one output per group in batches
     // of 8: 8.9 us); at M <= 4, with two to four groups per workgroup, deferring the last levels only
     // lengthens the tail (7.7 -> 7.9 us at M = 4).
-    constexpr int R = MT >= 8 ? 1 : MT >= 4 ? 2 : 4, NB = 2, PER_CU = 2, RB = MT >= 8 ? 8 : 1;
+    constexpr int R = MT >= 8 ? 1 : 2, NB = 2, PER_CU = 2, RB = MT >= 8 ? 8 : 1;
     const int64_t groups = (a.N + R - 1) / R;
     const int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
     if (epi_identity(a.ep))

@@ -332,6 +332,24 @@ int ggo_test_gemm_mfma_tile128(const uint16_t *A, int64_t lda,
                                int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * ggo_test_gemm_ordered_tile -- test hook, not a production entry point:
+ * gemm_ordered executed on a chosen tile of its kernel instead of the one
+ * gemm_ordered picks from the weight's shape (64 x 64 outputs per workgroup
+ * with 4 x 4 per lane, 64 x 32 with 4 x 2, or 16 x 16 with one output per
+ * lane). Every output's chain is the same under every tile, so the bits must
+ * equal gemm_ordered's; the tests use it to show that the tile is a speed knob
+ * only ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section
+ * 3.2.2). Same arguments and errors as gemm_ordered.
+ */
+#define GGO_TEST_ORDERED_TILE_64x64 0
+#define GGO_TEST_ORDERED_TILE_16x16 1
+#define GGO_TEST_ORDERED_TILE_64x32 2
+int ggo_test_gemm_ordered_tile(int tile, const void *A, int a_dtype, int64_t lda,
+                               const uint16_t *W, int64_t ldw,
+                               float *C, int64_t ldc,
+                               int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * ggo_test_gemv_instance -- test hook, not a production entry point: one of
  * the decode GEMVs executed by a chosen kernel instance instead of the one its
  * entry point picks from M, so the tests can run every instance on the same

@@ -63,16 +63,54 @@ def test_ragged_shapes(g, M, N, K, a_dtype):
     assert np.array_equal(host_bits(g.gemm_ordered(dA, dev_bf16(W))), ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(37, 1100, 1001), (70, 2048, 1000), (5, 1056, 1992), (130, 1040, 1016)])
-def test_ragged_shapes_on_the_64x64_tile(g, M, N, K):
-    """Weights of more than 2^20 elements take the 64 x 64 tile: its element loads (odd K or N) and, with
-    K and N multiples of 8, its wide loads with a partial last k-step (K not a multiple of 32)."""
+@pytest.mark.parametrize("M,N,K", [(37, 1100, 1001), (70, 2048, 1000), (5, 1056, 1992), (130, 1040, 1016),
+                                   (37, 2100, 2001), (70, 4096, 1032), (3, 2056, 2048), (129, 2053, 2047)])
+def test_ragged_shapes_on_the_64x32_and_64x64_tiles(g, M, N, K):
+    """Weights of 2^20 < N K <= 2^22 elements take the 64 x 32 tile, larger ones the 64 x 64 tile: their
+    element loads (odd K or N) and, with K and N multiples of 8, their wide loads with a partial last
+    k-step (K not a multiple of 32)."""
     A = synth.normal_bf16(M + N + K, "rag64.A", (M, K))
     W = synth.normal_bf16(M + N + K, "rag64.W", (K, N), 0.02)
     assert N * K > 1 << 20
-    say(f"gemm_ordered 64x64 tile ragged M={M} N={N} K={K}")
+    say(f"gemm_ordered {'64x32' if N * K <= 1 << 22 else '64x64'} tile ragged M={M} N={N} K={K}")
     ref = f32_bits(oracle.gemm_ordered(A, W, threads=8))
     assert np.array_equal(host_bits(g.gemm_ordered(dev_bf16(A), dev_bf16(W))), ref)
+
+
+TILES = ("64x64", "64x32", "16x16")
+
+
+def test_every_tile_gives_the_same_bits(g, gpt2):
+    """The tile is a speed knob ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.2.2):
+    each of the three tiles, forced on the same rows at the same M, gives the oracle's bits."""
+    A, W, ref, dA, dW = gpt2
+    for M in (1, 7, 64, 130, 512):
+        for tile in TILES:
+            say(f"gemm_ordered tile {tile} gpt2 M={M}")
+            assert np.array_equal(host_bits(g.test_gemm_ordered_tile(tile, dA[:M], dW)), ref[:M]), (tile, M)
+    Am, Wm = synth.mlp_up(5, 256)
+    refm = f32_bits(oracle.gemm_ordered(Am, Wm, threads=16))
+    dAm, dWm = dev_bf16(Am), dev_bf16(Wm)
+    for tile in TILES:
+        say(f"gemm_ordered tile {tile} mlp M=256")
+        assert np.array_equal(host_bits(g.test_gemm_ordered_tile(tile, dAm, dWm)), refm), tile
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 333, 129), (5, 70, 1000), (66, 130, 64)])
+@pytest.mark.parametrize("a_dtype", ["bf16", "f32"])
+def test_every_tile_on_ragged_shapes(g, M, N, K, a_dtype):
+    Af = synth.normal_f32(M + N + K, "ragt.A", (M, K))
+    A = synth.f32_to_bf16_bits(Af) if a_dtype == "bf16" else Af
+    W = synth.normal_bf16(M + N + K, "ragt.W", (K, N), 0.02)
+    ref = f32_bits(oracle.gemm_ordered(A, W))
+    dA = dev_bf16(A) if a_dtype == "bf16" else dev_f32(A)
+    dW = dev_bf16(W)
+    for tile in TILES:
+        assert np.array_equal(host_bits(g.test_gemm_ordered_tile(tile, dA, dW)), ref), tile
+    # misaligned views take the element loads of every tile
+    dAb = dev_bf16(np.pad(A, ((0, 0), (1, 0)))) if a_dtype == "bf16" else dev_f32(np.pad(A, ((0, 0), (1, 0))))
+    for tile in TILES:
+        assert np.array_equal(host_bits(g.test_gemm_ordered_tile(tile, dAb[:, 1:], dW)), ref), tile
 
 
 def test_strided_and_misaligned_views(g):
