@@ -95,38 +95,109 @@ def gemv_bytes(M, K=4096, N=4096):
     return 2 * K * N + 2 * M * K + 4 * M * N
 
 
-def cpu_baseline(x, WT, ms, seconds):
-    """The oracle of the headline step (oracle.gemv_tree), one thread, whole steps until `seconds` pass."""
-    import oracle
-    steps, t0 = 0, time.perf_counter()
+# Host threads for the all-cores legs: the CPU share of one GPU on the MI355X boxes is 16 cores, whatever
+# nproc reports there, so the leg uses at most that many (nproc and the affinity mask are recorded beside it).
+HOST_SHARE_THREADS = 16
+
+
+def _host_threads():
+    return max(1, min(HOST_SHARE_THREADS, len(os.sched_getaffinity(0))))
+
+
+class _one_core:
+    """Pin the calling thread (where a threads=1 oracle call runs) to one core of its mask, then restore."""
+
+    def __enter__(self):
+        self.mask = os.sched_getaffinity(0)
+        self.core = min(self.mask)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.mask)
+
+
+def _repeat(fn, seconds):
+    """Calls of fn() until `seconds` pass; returns (calls, elapsed)."""
+    n, t0 = 0, time.perf_counter()
     while True:
-        for M in ms:
-            oracle.gemv_tree(x[:M], WT, threads=1)
-        steps += 1
+        fn()
+        n += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
-            break
+            return n, dt
+
+
+def cpu_baseline(x, WT, ms, seconds):
+    """The oracle of the headline step (oracle.gemv_tree): one core (pinned), whole steps until `seconds`
+    pass, then over the host threads for half as long."""
+    import oracle
+    with _one_core() as pin:
+        steps, dt = _repeat(lambda: [oracle.gemv_tree(x[:M], WT, threads=1) for M in ms], seconds)
     gbs = steps * sum(gemv_bytes(M) for M in ms) / dt / 1e9
-    # the same oracle over all host threads (rows split across threads; same bits), for half the time
-    threads = max(1, min(16, os.cpu_count() or 1))
-    steps_all, t0 = 0, time.perf_counter()
-    while True:
-        for M in ms:
-            oracle.gemv_tree(x[:M], WT, threads=threads)
-        steps_all += 1
-        dt_all = time.perf_counter() - t0
-        if dt_all >= seconds / 2:
-            break
+    threads = _host_threads()
+    steps_all, dt_all = _repeat(lambda: [oracle.gemv_tree(x[:M], WT, threads=threads) for M in ms], seconds / 2)
     gbs_all = steps_all * sum(gemv_bytes(M) for M in ms) / dt_all / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} full decode steps (M={','.join(map(str, ms))}, K=N=4096) of the tree-order "
-                      f"oracle, plain C, single-threaded, {dt:.1f} s",
+                      f"oracle, plain C, single-threaded, pinned to core {pin.core}, {dt:.1f} s",
             "all_cores": {"value": round(gbs_all, 4), "cores": threads,
-                          "sample": f"{steps_all} steps, rows split over {threads} threads, {dt_all:.1f} s"},
-            "cpu_model": cpu_model()}
+                          "sample": f"{steps_all} steps, outputs split over {threads} threads (the CPU share of "
+                                    f"one GPU), {dt_all:.1f} s"},
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_oracle_configs(seconds=1.0):
+    """The oracle on every workload of the path, one core (pinned) and over the host threads: a stated
+    sample of each (whole outputs; rows are independent, so a row subset scales linearly), repeated for
+    about `seconds`, as GFLOP/s of algorithmic work and the time the whole workload would take."""
+    import oracle
+    import synth
+    threads = _host_threads()
+    out = {}
+
+    def leg(name, path, fn_one, fn_all, flop, sample, full_flop, flop_all=None):
+        with _one_core():
+            n1, t1 = _repeat(fn_one, seconds)
+        na, ta = _repeat(fn_all, seconds / 2)
+        g1, ga = n1 * flop / t1 / 1e9, na * (flop_all or flop) / ta / 1e9
+        out[name] = {"oracle": path, "gflops_1core": round(g1, 4), "gflops_all_cores": round(ga, 4),
+                     "threads": threads, "sample": sample,
+                     "full_workload_s_1core": round(full_flop / (g1 * 1e9), 2),
+                     "full_workload_s_all_cores": round(full_flop / (ga * 1e9), 2)}
+
+    A, W = synth.gpt2_projection(0, 512)
+    f = 2.0 * 512 * 768 * 768
+    leg("gpt2_proj_M512_N768_K768", "gemm_ordered", lambda: oracle.gemm_ordered(A, W),
+        lambda: oracle.gemm_ordered(A, W, threads=threads), f, "all 512 rows", f)
+    x, Wd, _ = synth.decode_gemv(0, 8)
+    f = 2.0 * 8 * 4096 * 4096
+    leg("decode_M8_N4096_K4096", "gemm_ordered (one-lane chain)", lambda: oracle.gemm_ordered(x, Wd),
+        lambda: oracle.gemm_ordered(x, Wd, threads=8), f, "all 8 rows (at most 8 threads: one per row)", f)
+    A = synth.normal_bf16(0, "mlp.A", (256, 1024), 1.0)
+    W = synth.normal_bf16(0, "mlp.W", (1024, 4096), 0.02)
+    leg("mlp_up_M2048_N4096_K1024", "gemm_ordered", lambda: oracle.gemm_ordered(A, W),
+        lambda: oracle.gemm_ordered(A, W, threads=threads), 2.0 * 256 * 4096 * 1024,
+        "rows 0-255 of 2048, scaled", 2.0 * 2048 * 4096 * 1024)
+    leg("mlp_up_M2048_N4096_K1024_mfma_model", "gemm_mfma (bit model of the matrix-core GEMM)",
+        lambda: oracle.gemm_mfma(A[:2], W), lambda: oracle.gemm_mfma(A[:2 * threads], W, threads=threads),
+        2.0 * 2 * 4096 * 1024, f"rows 0-1 of 2048 on one core, rows 0-{2 * threads - 1} over the threads, scaled",
+        2.0 * 2048 * 4096 * 1024, flop_all=2.0 * 2 * threads * 4096 * 1024)
+    A = synth.normal_bf16(0, "7b.A", (32, 4096), 1.0)
+    W = synth.normal_bf16(0, "7b.W4096", (4096, 4096), 0.02)
+    leg("7b_qkvo_M4096_N4096_K4096", "gemm_ordered", lambda: oracle.gemm_ordered(A, W),
+        lambda: oracle.gemm_ordered(A, W, threads=threads), 2.0 * 32 * 4096 * 4096,
+        "rows 0-31 of 4096, scaled", 2.0 * 4096 ** 3)
+    P = synth.softmax_rows_f32(0, "pv.P.0.0.5000", 256, 5000)
+    V = synth.normal_bf16(0, "pv.V.0.5000", (5000, 128), 1.0)
+    leg("pv_L5000_h32_d128", "gemm_ordered (binary32 P)", lambda: oracle.gemm_ordered(P, V),
+        lambda: oracle.gemm_ordered(P, V, threads=threads), 2.0 * 256 * 5000 * 128,
+        "query rows 0-255 of head 0, scaled to 32 heads x 5000 rows", 2.0 * 32 * 5000 * 5000 * 128)
+    return out
 
 
 def cpu_model():
+    """The host CPU's full model name as /proc/cpuinfo reports it."""
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -227,6 +298,7 @@ def paths(g, reps):
             t = time_region(lambda: g.gemm_ordered(A, W, C=C), max(2, reps // 4), 1)
             rec["ordered_tflops"] = round(flop / t / 1e9, 2)
             rec["ordered_frac_contract_peak"] = round(flop / t / 1e9 / VALU_CONTRACT_PEAK_TFS, 4)
+            rec["ordered_frac_nominal_peak"] = round(flop / t / 1e9 / VALU_NOMINAL_PEAK_TFS, 4)
         t = time_region(lambda: g.gemm_mfma_invariant(A, W, C=C), reps)
         rec["mfma_tflops"] = round(flop / t / 1e9, 1)
         rec["mfma_frac_peak"] = round(flop / t / 1e9 / MFMA_BF16_PEAK_TFS, 4)
@@ -297,13 +369,27 @@ def paths(g, reps):
             out[f"decode_gemv_M{M}_N{N}_K{K}"] = rec
         del WTs
     # attention value product, 32 heads, head_dim 128 (L = 5000: P is 3.2 GB, 204.8 GFLOP)
+    import numpy as np
+    import oracle
     for L in (256, 1024, 5000):
         P = torch.softmax(torch.randn((32, L, L), device="cuda"), dim=-1)
         V = randn_bf16((32, L, 128), 1.0)
         O = torch.empty((32, L, 128), device="cuda")
         t = time_region(lambda: g.gemm_ordered_grouped([(P, V, O)]), max(2, reps // 4), 1)
         flop = 2.0 * 32 * L * L * 128
-        out[f"pv_L{L}_h32"] = {"ordered_tflops": round(flop / t / 1e9, 2), "ms": round(t, 4)}
+        # the timed launch's output: rows 0, L/2 and L-1 of the last two heads (head 31 starts past 2^31
+        # bytes of P at L = 5000) against the oracle, bit for bit
+        torch.cuda.synchronize()
+        rows = sorted({0, L // 2, L - 1})
+        same = all(np.array_equal(
+            O[h, rows].cpu().numpy().view(np.uint32),
+            oracle.gemm_ordered(np.ascontiguousarray(P[h, rows].cpu().numpy()),
+                                V[h].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)).view(np.uint32))
+            for h in (30, 31))
+        out[f"pv_L{L}_h32"] = {"ordered_tflops": round(flop / t / 1e9, 2), "ms": round(t, 4),
+                               "ordered_frac_contract_peak": round(flop / t / 1e9 / VALU_CONTRACT_PEAK_TFS, 4),
+                               "ordered_frac_nominal_peak": round(flop / t / 1e9 / VALU_NOMINAL_PEAK_TFS, 4),
+                               "parity_heads_30_31_rows_0_mid_last": "bit-exact" if same else "MISMATCH"}
         del P, V, O
     return out
 
@@ -762,6 +848,8 @@ def main():
     extra = {} if args.no_paths else paths(g, 10)
     log("cpu baseline")
     cpu = cpu_baseline(x, WT, ms, args.cpu_seconds)
+    log("cpu oracle on the other workloads")
+    cpu["configs"] = cpu_oracle_configs(max(0.2, args.cpu_seconds / 10))
 
     achieved = (step_bytes / len(ms)) / (avg_launch_us * 1e-6) / 1e9
     line = {

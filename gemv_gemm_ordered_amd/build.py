@@ -35,8 +35,8 @@ def _sha(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def build_info() -> str:
-    files = {os.path.normpath(s): _sha(os.path.join(CSRC, s)) for s in SOURCES + HEADERS}
+def build_info(csrc: str = CSRC) -> str:
+    files = {os.path.normpath(s): _sha(os.path.join(csrc, s)) for s in SOURCES + HEADERS}
     try:
         ver = subprocess.run([HIPCC, "--version"], capture_output=True, text=True).stdout.splitlines()
         ver = [v for v in ver if "clang version" in v][:1]
@@ -46,28 +46,33 @@ def build_info() -> str:
                       sort_keys=True)
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    info = build_info()
+def build(jobs: int = 8, csrc: str = CSRC, lib: str = LIB, build_dir: str = BUILD_DIR, only=None) -> str:
+    """Compile every source of `csrc` (a copy of this package's csrc/ beside a copy of include/ serves
+    too) into `build_dir` and link `lib`. With `only`, compile just those sources (capi.cpp, which
+    carries the build info, always) and link the others' objects from this package's own build."""
+    os.makedirs(build_dir, exist_ok=True)
+    info = build_info(csrc)
     define = '-DGGO_BUILD_INFO="' + info.replace("\\", "\\\\").replace('"', '\\"') + '"'
+    fresh = SOURCES if only is None else [s for s in SOURCES if s in set(only) | {"capi.cpp"}]
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *FLAGS, define, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *FLAGS, define, "-c", os.path.join(csrc, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    with ThreadPoolExecutor(min(jobs, len(fresh))) as ex:
+        built = dict(zip(fresh, ex.map(compile_one, fresh)))
+    objs = [built[s] if s in built else os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in SOURCES]
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
