@@ -77,6 +77,7 @@ def _load():
     PP = ct.POINTER(ct.c_void_p)
     lib.ggo_test_gemv_instance.argtypes = [I, I, I, P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.ggo_test_gemm_ordered_tile.argtypes = [I, P, I, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.ggo_test_gemm_mfma_tile.argtypes = [I, P, I64, P, I64, P, I64, I64, I64, I64, P]
     lib.freivalds_prepare.argtypes = [P, I64, I64, I64, ct.c_uint64, PP]
     lib.freivalds_check.argtypes = [P, P, P, ct.c_double, P]
     lib.freivalds_signs.argtypes = [P, P]
@@ -103,7 +104,7 @@ def _load():
     for f in ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered_wt", "gemv_tree", "gemv_tree_ep",
               "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
               "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "ggo_test_gemm_ordered_tile",
-              "gemm_mfma_invariant_wt", "gemv_mfma_invariant",
+              "ggo_test_gemm_mfma_tile", "gemm_mfma_invariant_wt", "gemv_mfma_invariant",
               "gemv_mfma_invariant_ep", "freivalds_prepare", "freivalds_check", "freivalds_signs",
               "freivalds_prepare_signs", "freivalds_check_signs"):
         getattr(lib, f).restype = I
@@ -116,7 +117,7 @@ EXPORTS = ("gemm_ordered", "gemm_ordered_grouped", "gemv_ordered", "gemv_ordered
            "gemm_mfma_invariant_ep", "gemm_mfma_invariant",
            "gemm_mfma_invariant_wt", "gemv_mfma_invariant", "gemv_mfma_invariant_ep",
            "ggo_test_gemm_mfma_tile128", "ggo_test_gemv_instance", "ggo_test_gemm_ordered_tile",
-           "freivalds_prepare", "freivalds_check",
+           "ggo_test_gemm_mfma_tile", "freivalds_prepare", "freivalds_check",
            "freivalds_signs", "freivalds_free", "freivalds_prepare_signs", "freivalds_check_signs",
            "ggo_build_info", "ggo_last_error",
            "ggo_cert_create", "ggo_cert_create_host", "ggo_cert_add_matrix", "ggo_cert_submit", "ggo_cert_submit_rows",
@@ -406,6 +407,24 @@ def gemm_mfma_invariant_wt(A, WT, C=None, stream=None):
 def test_gemm_mfma_tile128(A, W, C=None, stream=None):
     """Test hook: the same descriptor on the 128x128 tile instance (must give the same bits)."""
     return _mfma("ggo_test_gemm_mfma_tile128", A, W, C, stream)
+
+
+MFMA_TILES = {"256x128": 0, "128x128": 1, "64x64": 2}
+
+
+def test_gemm_mfma_tile(tile, A, W, C=None, stream=None):
+    """Test hook: gemm_mfma_invariant on the chosen tile instance ('256x128', '128x128' or '64x64'); must
+    give gemm_mfma_invariant's bits."""
+    lda, ldw = _rowmajor(A, "A"), _rowmajor(W, "W")
+    M, K = A.shape
+    if not (_is_bf16(A) and _is_bf16(W)) or W.shape[0] != K:
+        raise ValueError("A and W must be bf16, W [K, N]")
+    N = W.shape[1]
+    C = _out(C, M, N, A)
+    ldc = _rowmajor(C, "C") if M and N else N
+    _raise(lib.ggo_test_gemm_mfma_tile(MFMA_TILES[tile], A.data_ptr(), lda, W.data_ptr(), ldw, C.data_ptr(), ldc,
+                                       M, N, K, _stream(stream)), "ggo_test_gemm_mfma_tile")
+    return C
 
 
 GEMV_KINDS = {"tree": 0, "ordered": 1, "ordered_wt": 2, "mfma": 3}

@@ -190,29 +190,43 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, kind, wide, s));
 }
 
-// The 256x128 instance needs 16-byte aligned operands with row strides that
-// are multiples of 8 and below 2^22 (its buffer offsets are 32-bit), and K and
-// N multiples of 8: it loads 16-byte chunks through range-checked buffer
-// descriptors that end at the caller's last element, and the range check
-// drops a whole dword that straddles that end, so no chunk may straddle it.
-// Every other call takes the 128x128 instance. Both give every output the
-// same bits (the same operand values in the same groups), so the choice,
-// which never looks at M, moves no bit.
+// Tile of the matrix-core GEMM, from the weight's shape and the operands' alignment, never from M:
+//  - a weight of at most 2^20 elements: 64x64 tiles (any operands), so that a small weight still puts
+//    more workgroups on the 256 CUs at small M (768 x 768: 12 instead of 6 at M <= 64);
+//  - otherwise 256x128 tiles for 16-byte aligned operands with row strides that are multiples of 8 (and
+//    below 2^22: its buffer offsets are 32-bit) and K and N multiples of 8 (it loads 16-byte chunks
+//    through range-checked buffer descriptors that end at the caller's last element, and the range check
+//    drops a whole dword that straddles that end, so no chunk may straddle it);
+//  - else 128x128 tiles (any operands).
+// Every instance gives every output the same bits (the same opcode, the same operand values in the same
+// groups of 32 k, ascending), so the choice moves no bit. `force` (a MFMA_TILE_* value, or -1) lets the
+// test hook run any instance.
+enum { MFMA_TILE_256x128 = 0, MFMA_TILE_128x128 = 1, MFMA_TILE_64x64 = 2 };
+constexpr int64_t MFMA_SMALL_WEIGHT = int64_t(1) << 20;
+
 int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, void* C, int64_t ldc,
-             int64_t M, int64_t N, int64_t K, hipStream_t s, bool force_t128, const Epi& ep) {
+             int64_t M, int64_t N, int64_t K, hipStream_t s, int force, const Epi& ep) {
     int rc = check_mnk(fn, M, N, K);
     if (rc) return rc;
     if (M == 0 || N == 0) return ok();
     if (!C || (K && (!A || !W))) return fail(GGO_EINVAL, "%s: null pointer", fn);
     if (lda < K || ldw < N || ldc < N) return fail(GGO_EINVAL, "%s: row stride below extent", fn);
     if (K == 0) return launched(fn, epi_zero(C, ldc, M, N, ep, s));
-    const bool wide = !force_t128 && aligned(A, 16) && lda % 8 == 0 && aligned(W, 16) && ldw % 8 == 0 &&
-                      lda < (int64_t(1) << 22) && ldw < (int64_t(1) << 22) && K % 8 == 0 && N % 8 == 0;
+    const bool wide_ok = aligned(A, 16) && lda % 8 == 0 && aligned(W, 16) && ldw % 8 == 0 &&
+                         lda < (int64_t(1) << 22) && ldw < (int64_t(1) << 22) && K % 8 == 0 && N % 8 == 0;
+    const int tile = force >= 0 ? force
+                   : N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x64
+                   : wide_ok ? MFMA_TILE_256x128 : MFMA_TILE_128x128;
+    if (tile == MFMA_TILE_256x128 && !wide_ok)
+        return fail(GGO_EUNSUPPORTED, "%s: the 256x128 instance needs 16-byte aligned operands with row strides and K, N "
+                    "multiples of 8", fn);
     int bm, bn;
-    if (wide)
+    if (tile == MFMA_TILE_256x128)
         mfma_tile_shape(&bm, &bn);
-    else
+    else if (tile == MFMA_TILE_128x128)
         mfma_tile_shape_t128(&bm, &bn);
+    else
+        mfma_tile_shape_t64(&bm, &bn);
     MfmaArgs a;
     a.A = A;
     a.W = W;
@@ -232,10 +246,17 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
     if (aligned(W, 8) && ldw % 4 == 0) a.vec |= VEC_W;
     if (aligned(C, 16) && ldc % 4 == 0) a.vec |= VEC_C;
     a.ep = ep;
+    // 64x64 tile, branch-free loads: 16-byte chunks of A and 8-byte pieces of W never straddle a row's end,
+    // and every offset into the A panel (64 rows) and the W panel (K rows) stays below 2^31 bytes
+    if (aligned(A, 16) && lda % 8 == 0 && aligned(W, 8) && ldw % 8 == 0 && K % 8 == 0 && N % 4 == 0 &&
+        64 * lda * 2 < (int64_t(1) << 31) && K * ldw * 2 < (int64_t(1) << 31))
+        a.vec |= VEC_WIDE64;
     if ((!ep.bias || aligned(ep.bias, 16)) && (!ep.res || (aligned(ep.res, 16) && ep.ldr % 4 == 0)) &&
         aligned(C, ep.out_bf16 ? 8 : 16) && ldc % 4 == 0)
         a.vec |= VEC_EP;
-    return launched(fn, wide ? launch_gemm_mfma_invariant(a, s) : launch_gemm_mfma_t128(a, s));
+    return launched(fn, tile == MFMA_TILE_256x128   ? launch_gemm_mfma_invariant(a, s)
+                        : tile == MFMA_TILE_128x128 ? launch_gemm_mfma_t128(a, s)
+                                                    : launch_gemm_mfma_t64(a, s));
 }
 
 }  // namespace
@@ -397,12 +418,12 @@ int gemm_mfma_invariant_ep(const uint16_t* A, int64_t lda, const uint16_t* W, in
     Epi e;
     int rc = make_epi("gemm_mfma_invariant_ep", ep, N, &e);
     if (rc) return rc;
-    return run_mfma("gemm_mfma_invariant_ep", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), false, e);
+    return run_mfma("gemm_mfma_invariant_ep", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), -1, e);
 }
 
 int gemm_mfma_invariant(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void* stream) {
-    return run_mfma("gemm_mfma_invariant", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), false, no_epi());
+    return run_mfma("gemm_mfma_invariant", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), -1, no_epi());
 }
 
 int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, int64_t ldwt, float* C, int64_t ldc,
@@ -494,7 +515,18 @@ int gemv_mfma_invariant_ep(const uint16_t* x, int64_t ldx, const uint16_t* WT, i
 
 int ggo_test_gemm_mfma_tile128(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C, int64_t ldc,
                                int64_t M, int64_t N, int64_t K, void* stream) {
-    return run_mfma("ggo_test_gemm_mfma_tile128", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), true, no_epi());
+    return run_mfma("ggo_test_gemm_mfma_tile128", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream),
+                    MFMA_TILE_128x128, no_epi());
+}
+
+int ggo_test_gemm_mfma_tile(int tile, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C,
+                            int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (tile != GGO_TEST_MFMA_TILE_256x128 && tile != GGO_TEST_MFMA_TILE_128x128 && tile != GGO_TEST_MFMA_TILE_64x64)
+        return fail(GGO_EINVAL, "ggo_test_gemm_mfma_tile: unknown tile %d", tile);
+    static_assert(GGO_TEST_MFMA_TILE_256x128 == MFMA_TILE_256x128 && GGO_TEST_MFMA_TILE_128x128 == MFMA_TILE_128x128 &&
+                  GGO_TEST_MFMA_TILE_64x64 == MFMA_TILE_64x64, "");
+    return run_mfma("ggo_test_gemm_mfma_tile", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), tile,
+                    no_epi());
 }
 
 int ggo_test_gemv_instance(int kind, int rows, int form, const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,

@@ -6,7 +6,10 @@
 #include "../../include/ggo.h"
 #include "epilogue.hpp"
 
-enum : uint32_t { VEC_A = 1u, VEC_W = 2u, VEC_C = 4u, VEC_EP = 8u };   // VEC_EP: 4-wide epilogue loads/stores
+// VEC_EP: 4-wide epilogue loads/stores. VEC_WIDE64: the 64x64 matrix-core tile may use its branch-free
+// buffer loads (16-byte aligned A, 8-byte aligned W, lda, ldw and K multiples of 8, N a multiple of 4,
+// A and W ranges below 2^31 bytes).
+enum : uint32_t { VEC_A = 1u, VEC_W = 2u, VEC_C = 4u, VEC_EP = 8u, VEC_WIDE64 = 16u };
 
 // One ordered problem as the kernel sees it (passed by value in the kernel arguments).
 struct OrdProblem {
@@ -83,8 +86,10 @@ struct MfmaArgs {
 };
 void mfma_tile_shape(int* bm, int* bn);        // 256x128 instance (16-byte aligned operands)
 void mfma_tile_shape_t128(int* bm, int* bn);   // 128x128 instance (any operands)
+void mfma_tile_shape_t64(int* bm, int* bn);    // 64x64 instance (any operands)
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_t128(const MfmaArgs& a, hipStream_t stream);
+hipError_t launch_gemm_mfma_t64(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream);   // W given as W^T [N, K]
 
 struct GemvMfmaArgs {

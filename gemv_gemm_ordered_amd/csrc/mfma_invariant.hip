@@ -31,6 +31,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -39,20 +40,85 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 namespace t128 {
 
-constexpr int BM = 128, BN = 128, BK = 64, THREADS = 256;
-constexpr int LDK = BK + 8;   // padded LDS row, in bf16 elements (144 bytes)
-
-struct Stage {
-    uint4 a[4];   // 4 chunks of 8 k of one row of A
-    uint2 w[8];   // 8 rows (k) x 4 columns (n) of W
+// Tile BM x BN x BK, four waves in a 2 x 2 grid, each owning (BM/2) x (BN/2) outputs. Per k-step each
+// thread loads A_CH chunks of 8 k of A and W_CH blocks of 8(k) x 4(n) of W into registers; the next
+// step's loads are in flight while the current step is multiplied.
+template <int BM_, int BN_, int BK_> struct Shape {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WI = BM / 32, WJ = BN / 32;           // 16 x 16 blocks per wave (rows, columns)
+    static constexpr int CK = BK / 8;                           // 8-k chunks per row of A
+    static constexpr int A_CH = BM * CK / 256;                  // A chunks per thread and step
+    static constexpr int NB4 = BN / 4;                          // 4-column blocks of W
+    static constexpr int W_BLOCKS = CK * NB4;                   // 8 x 4 blocks of W per step
+    static constexpr int W_CH = (W_BLOCKS + 255) / 256;         // ... per thread
+    static constexpr int LDK = BK + 8;                          // padded LDS row (bf16), 16 bytes over
+    static_assert(BM * CK % 256 == 0 && (W_BLOCKS % 256 == 0 || (W_BLOCKS < 256 && W_BLOCKS % 64 == 0)), "");
 };
 
-GGO_DEV void load_stage(const MfmaArgs& p, int m0, int n0, int k0, int t, Stage& s) {
-    // A: 128 rows x 64 k = 1024 chunks of 8; chunk c = t + 256 i
+constexpr int THREADS = 256;
+
+template <class S>
+struct Stage {
+    uint4 a[S::A_CH];      // chunks of 8 k of rows of A
+    uint2 w[S::W_CH][8];   // blocks of 8 rows (k) x 4 columns (n) of W
+};
+
+// Range-checked descriptors of the workgroup's panels, for the wide loads: A's rows m0 .. m0 + BM - 1
+// (ending at the caller's last element) and W's columns n0 .. (every row, ending at column N - 1 of row
+// K - 1). A load given OFF_PAST (or any offset past the range) returns 0 without touching memory.
+struct Panels128 {
+    __amdgpu_buffer_rsrc_t a, w;
+    int rows;
+};
+constexpr int BUF_DWORD3 = 0x00020000;
+constexpr int OFF_PAST = 0x7ffffff0;
+
+template <class S>
+GGO_DEV Panels128 panels128(const MfmaArgs& p, int m0, int n0) {
+    Panels128 q;
+    q.rows = p.M - m0 < S::BM ? p.M - m0 : S::BM;
+    q.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.A) + static_cast<int64_t>(m0) * p.lda, 0,
+                                            ((q.rows - 1) * static_cast<int>(p.lda) + p.K) * 2, BUF_DWORD3);
+    q.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.W) + n0, 0,
+                                            ((p.K - 1) * static_cast<int>(p.ldw) + (p.N - n0)) * 2, BUF_DWORD3);
+    return q;
+}
+
+// Wide loads (16-byte aligned A, 8-byte aligned W, row strides and K multiples of 8, N a multiple of 4,
+// ranges below 2^31 bytes): no per-lane branch around a load, so none has to land before its step.
+template <class S>
+GGO_DEV void load_stage_wide(const MfmaArgs& p, const Panels128& q, int n0, int k0, int t, Stage<S>& s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < S::A_CH; ++i) {
         const int c = t + THREADS * i;
-        const int row = m0 + (c >> 3), k = k0 + (c & 7) * 8;
+        const int r = c / S::CK, k = k0 + (c % S::CK) * 8;
+        const int off = (r < q.rows && k < p.K) ? (r * static_cast<int>(p.lda) + k) * 2 : OFF_PAST;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(q.a, off, 0, 0);
+        s.a[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    if (S::W_BLOCKS < THREADS && t >= S::W_BLOCKS) return;   // uniform per wave
+#pragma unroll
+    for (int i = 0; i < S::W_CH; ++i) {
+        const int blk = t + THREADS * i;
+        const int kb = k0 + 8 * (blk / S::NB4), nl = 4 * (blk % S::NB4);
+        const bool nin = n0 + nl < p.N;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int k = kb + r;
+            const int off = (nin && k < p.K) ? (k * static_cast<int>(p.ldw) + nl) * 2 : OFF_PAST;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(q.w, off, 0, 0);
+            s.w[i][r] = make_uint2(v[0], v[1]);
+        }
+    }
+}
+
+template <class S>
+GGO_DEV void load_stage(const MfmaArgs& p, int m0, int n0, int k0, int t, Stage<S>& s) {
+    // A: BM rows x BK k = BM * CK chunks of 8; chunk c = t + 256 i
+#pragma unroll
+    for (int i = 0; i < S::A_CH; ++i) {
+        const int c = t + THREADS * i;
+        const int row = m0 + c / S::CK, k = k0 + (c % S::CK) * 8;
         const uint16_t* src = p.A + static_cast<int64_t>(row) * p.lda + k;
         if (row < p.M && k + 8 <= p.K && (p.vec & VEC_A)) {
             s.a[i] = *reinterpret_cast<const uint4*>(src);
@@ -63,45 +129,84 @@ GGO_DEV void load_stage(const MfmaArgs& p, int m0, int n0, int k0, int t, Stage&
             s.a[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
         }
     }
-    // W: thread t covers k rows k0 + 8*(t>>5) .. +7 and columns n0 + 4*(t&31) .. +3
-    const int kb = k0 + 8 * (t >> 5), n = n0 + 4 * (t & 31);
+    // W: block b = t + 256 i covers k rows k0 + 8 (b / NB4) .. +7 and columns n0 + 4 (b % NB4) .. +3
+    if (S::W_BLOCKS < THREADS && t >= S::W_BLOCKS) return;   // uniform per wave
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int k = kb + r;
-        const uint16_t* src = p.W + static_cast<int64_t>(k) * p.ldw + n;
-        if (k < p.K && n + 4 <= p.N && (p.vec & VEC_W)) {
-            s.w[r] = *reinterpret_cast<const uint2*>(src);
-        } else {
-            uint32_t h[4];
+    for (int i = 0; i < S::W_CH; ++i) {
+        const int blk = t + THREADS * i;
+        const int kb = k0 + 8 * (blk / S::NB4), n = n0 + 4 * (blk % S::NB4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = (k < p.K && n + e < p.N) ? src[e] : 0u;
-            s.w[r] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        for (int r = 0; r < 8; ++r) {
+            const int k = kb + r;
+            const uint16_t* src = p.W + static_cast<int64_t>(k) * p.ldw + n;
+            if (k < p.K && n + 4 <= p.N && (p.vec & VEC_W)) {
+                s.w[i][r] = *reinterpret_cast<const uint2*>(src);
+            } else {
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = (k < p.K && n + e < p.N) ? src[e] : 0u;
+                s.w[i][r] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
         }
     }
 }
 
-GGO_DEV void store_stage(uint16_t (*As)[LDK], uint16_t (*Bs)[LDK], int t, const Stage& s) {
+template <class S>
+GGO_DEV void store_stage(uint16_t (*As)[S::LDK], uint16_t (*Bs)[S::LDK], int t, const Stage<S>& s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < S::A_CH; ++i) {
         const int c = t + THREADS * i;
-        *reinterpret_cast<uint4*>(&As[c >> 3][(c & 7) * 8]) = s.a[i];
+        *reinterpret_cast<uint4*>(&As[c / S::CK][(c % S::CK) * 8]) = s.a[i];
     }
-    // transpose the 8(k) x 4(n) block: column j gets k pairs (2p, 2p+1) packed in one dword
-    const int kc = 8 * (t >> 5), nb = 4 * (t & 31);
+    if (S::W_BLOCKS < THREADS && t >= S::W_BLOCKS) return;   // uniform per wave
+    // transpose each 8(k) x 4(n) block: column j gets k pairs (2p, 2p+1) packed in one dword
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t d[4];
+    for (int i = 0; i < S::W_CH; ++i) {
+        const int blk = t + THREADS * i;
+        const int kc = 8 * (blk / S::NB4), nb = 4 * (blk % S::NB4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = (j < 2) ? s.w[2 * q].x : s.w[2 * q].y;
-            const uint32_t hi = (j < 2) ? s.w[2 * q + 1].x : s.w[2 * q + 1].y;
-            d[q] = __builtin_amdgcn_perm(hi, lo, (j & 1) ? 0x07060302u : 0x05040100u);
+        for (int j = 0; j < 4; ++j) {
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = (j < 2) ? s.w[i][2 * q].x : s.w[i][2 * q].y;
+                const uint32_t hi = (j < 2) ? s.w[i][2 * q + 1].x : s.w[i][2 * q + 1].y;
+                d[q] = __builtin_amdgcn_perm(hi, lo, (j & 1) ? 0x07060302u : 0x05040100u);
+            }
+            *reinterpret_cast<uint4*>(&Bs[nb + j][kc]) = make_uint4(d[0], d[1], d[2], d[3]);
         }
-        *reinterpret_cast<uint4*>(&Bs[nb + j][kc]) = make_uint4(d[0], d[1], d[2], d[3]);
     }
 }
 
-__global__ __launch_bounds__(THREADS) void k_gemm_mfma_t128(const MfmaArgs p) {
+// One k-step of the register-staged tiles: the step's groups of 32 k in ascending order, fragments read
+// from the LDS copy of the step.
+template <class S>
+GGO_DEV void mfma_step(f32x4 (&acc)[S::WI][S::WJ], const uint16_t (*As)[S::LDK], const uint16_t (*Bs)[S::LDK], int wm,
+                       int wn, int lr, int lk) {
+#pragma unroll
+    for (int g = 0; g < S::BK / 32; ++g) {
+        bf16x8 af[S::WI], bfr[S::WJ];
+#pragma unroll
+        for (int i = 0; i < S::WI; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(&As[wm * (S::BM / 2) + i * 16 + lr][g * 32 + lk]);
+#pragma unroll
+        for (int j = 0; j < S::WJ; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[wn * (S::BN / 2) + j * 16 + lr][g * 32 + lk]);
+#pragma unroll
+        for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+            for (int j = 0; j < S::WJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// Wide form with a register ring of D k-steps in flight: step kt sits in slot kt % D until it is stored
+// to LDS, and the slot is refilled with step kt + D at once. Loads past K read zeros, so every step
+// issues the same loads and the compiler counts exactly which ones a store has to wait for.
+template <int BM, int BN, int BK, int D>
+__global__ __launch_bounds__(THREADS) void k_gemm_mfma_ring(const MfmaArgs p) {
+    using S = Shape<BM, BN, BK>;
+    constexpr int WI = S::WI, WJ = S::WJ, LDK = S::LDK;
     __shared__ __attribute__((aligned(16))) uint16_t As[BM][LDK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][LDK];
 
@@ -109,55 +214,117 @@ __global__ __launch_bounds__(THREADS) void k_gemm_mfma_t128(const MfmaArgs p) {
     const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;       // 2 x 2 waves, 64 x 64 outputs each
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 15, lk = (lane >> 4) * 8;
+
+    f32x4 acc[WI][WJ];
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nkt = (p.K + BK - 1) / BK;   // >= 1: K == 0 never reaches the kernel
+    const Panels128 q = panels128<S>(p, m0, n0);
+    Stage<S> st[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_stage_wide<S>(p, q, n0, d * BK, t, st[d]);
+    store_stage<S>(As, Bs, t, st[0]);
+    __syncthreads();
+    for (int kt0 = 0; kt0 < nkt; kt0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int kt = kt0 + d;
+            if (kt >= nkt) break;                                   // uniform
+            load_stage_wide<S>(p, q, n0, (kt + D) * BK, t, st[d]);  // slot d is in LDS: refill it
+            mfma_step<S>(acc, As, Bs, wm, wn, lr, lk);
+            __syncthreads();
+            if (kt + 1 < nkt) {
+                store_stage<S>(As, Bs, t, st[(d + 1) % D]);
+                __syncthreads();
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the loads past the end have landed before the workgroup ends
+
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            const int col = n0 + wn * (BN / 2) + j * 16 + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + r;
+                if (row < p.M && col < p.N) epi_store(p.ep, p.C, p.ldc, row, col, acc[i][j][r]);
+            }
+        }
+}
+
+template <int BM, int BN, int BK, bool WIDE = false>
+__global__ __launch_bounds__(THREADS) void k_gemm_mfma_reg(const MfmaArgs p) {
+    using S = Shape<BM, BN, BK>;
+    constexpr int WI = S::WI, WJ = S::WJ, LDK = S::LDK;
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM][LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][LDK];
+
+    const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;        // 2 x 2 waves, (BM/2) x (BN/2) outputs each
     const int lr = lane & 15, lk = (lane >> 4) * 8; // operand row/col and k offset of this lane
 
-    f32x4 acc[4][4];
+    f32x4 acc[WI][WJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nkt = (p.K + BK - 1) / BK;
-    Stage st;
+    Stage<S> st;
+    Panels128 q{};
+    if constexpr (WIDE) q = panels128<S>(p, m0, n0);
+    auto load = [&](int k0) {
+        if constexpr (WIDE) load_stage_wide<S>(p, q, n0, k0, t, st);
+        else load_stage<S>(p, m0, n0, k0, t, st);
+    };
     if (nkt > 0) {
-        load_stage(p, m0, n0, 0, t, st);
-        store_stage(As, Bs, t, st);
+        load(0);
+        store_stage<S>(As, Bs, t, st);
     }
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
-        if (kt + 1 < nkt) load_stage(p, m0, n0, (kt + 1) * BK, t, st);
+        if (kt + 1 < nkt) load((kt + 1) * BK);
 #pragma unroll
         for (int g = 0; g < BK / 32; ++g) {           // ascending groups of 32 k
-            bf16x8 af[4], bfr[4];
+            bf16x8 af[WI], bfr[WJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&As[wm * 64 + i * 16 + lr][g * 32 + lk]);
+            for (int i = 0; i < WI; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(&As[wm * (BM / 2) + i * 16 + lr][g * 32 + lk]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[wn * 64 + j * 16 + lr][g * 32 + lk]);
+            for (int j = 0; j < WJ; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[wn * (BN / 2) + j * 16 + lr][g * 32 + lk]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < WI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < WJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
         if (kt + 1 < nkt) {
-            store_stage(As, Bs, t, st);
+            store_stage<S>(As, Bs, t, st);
             __syncthreads();
         }
     }
 
     // lane holds D[4*(lane/16) + r][lane%16] of each 16x16 block
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 64 + j * 16 + lr;
+        for (int j = 0; j < WJ; ++j) {
+            const int col = n0 + wn * (BN / 2) + j * 16 + lr;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+                const int row = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + r;
                 if (row < p.M && col < p.N) epi_store(p.ep, p.C, p.ldc, row, col, acc[i][j][r]);
             }
         }
@@ -690,7 +857,8 @@ constexpr int BN_MAIN = 128, BK_MAIN = 64, NST_MAIN = 3;
 }  // namespace
 
 void mfma_tile_shape(int* bm, int* bn) { *bm = t256::BM; *bn = t256::BN_MAIN; }
-void mfma_tile_shape_t128(int* bm, int* bn) { *bm = t128::BM; *bn = t128::BN; }
+void mfma_tile_shape_t128(int* bm, int* bn) { *bm = 128; *bn = 128; }
+void mfma_tile_shape_t64(int* bm, int* bn) { *bm = 64; *bn = 64; }
 
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, false>),
@@ -705,6 +873,18 @@ hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream) 
 }
 
 hipError_t launch_gemm_mfma_t128(const MfmaArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(t128::k_gemm_mfma_t128, dim3(a.tiles_m * a.tiles_n), dim3(t128::THREADS), 0, stream, a);
+    hipLaunchKernelGGL((t128::k_gemm_mfma_reg<128, 128, 64>), dim3(a.tiles_m * a.tiles_n), dim3(t128::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+// 64x64 tiles, 128-k steps; aligned operands keep two steps in flight (measured on the 768 x 768 weight:
+// 7.9 / 9.4 / 9.8 us at M = 1 / 64 / 512, against 10.7 / 11.5 / 14.9 with 256x128 tiles; one, four or
+// eight steps of 64 to 256 k in flight were no faster). On a 1024 x 4096 weight the 64x64 workgroups
+// took about 11 us each whatever the prefetch depth, so that weight keeps the 256x128 tiles.
+hipError_t launch_gemm_mfma_t64(const MfmaArgs& a, hipStream_t stream) {
+    if (a.vec & VEC_WIDE64)
+        hipLaunchKernelGGL((t128::k_gemm_mfma_ring<64, 64, 128, 2>), dim3(a.tiles_m * a.tiles_n), dim3(t128::THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((t128::k_gemm_mfma_reg<64, 64, 128>), dim3(a.tiles_m * a.tiles_n), dim3(t128::THREADS), 0, stream, a);
     return hipGetLastError();
 }

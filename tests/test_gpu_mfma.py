@@ -102,20 +102,27 @@ def test_7b_projection_sampled(g, n):
     assert np.array_equal(sub, full[1000:1128])
 
 
+TILES = ("256x128", "128x128", "64x64")
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 128, 64), (300, 200, 100), (513, 1000, 1111), (1, 4096, 4096),
                                    (2048, 4096, 1024), (4096, 4096, 4096), (4096, 11008, 4096), (7, 33, 31),
                                    (513, 1000, 1112), (300, 200, 104), (257, 136, 1000), (1, 8, 8), (255, 1032, 72)])
 def test_tile_instances_agree_bitwise(g, M, N, K):
-    """The 256x128 and the 128x128 tile instances feed every output the same operand values in the
+    """The 256x128, 128x128 and 64x64 tile instances feed every output the same operand values in the
     same 32-k groups ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.2.2: block
-    sizes do not enter the order), so their outputs must be identical bit for bit."""
+    sizes do not enter the order), so their outputs, and the entry point's, must be identical bit for bit."""
     say(f"mfma tile instances M={M} N={N} K={K}")
     A = synth.normal_bf16(M + 1, "ti.A", (M, K))
     W = synth.normal_bf16(N + 2, "ti.W", (K, N), 0.02)
     dA, dW = dev_bf16(A), dev_bf16(W)
-    c256 = host_bits(g.gemm_mfma_invariant(dA, dW))
-    c128 = host_bits(g.test_gemm_mfma_tile128(dA, dW))
-    assert np.array_equal(c256, c128), f"{np.count_nonzero(c256 != c128)} outputs differ"
+    entry = host_bits(g.gemm_mfma_invariant(dA, dW))
+    for tile in TILES:
+        if tile == "256x128" and (K % 8 or N % 8):
+            continue
+        got = host_bits(g.test_gemm_mfma_tile(tile, dA, dW))
+        assert np.array_equal(got, entry), f"{tile}: {np.count_nonzero(got != entry)} outputs differ"
+    assert np.array_equal(host_bits(g.test_gemm_mfma_tile128(dA, dW)), entry)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 64), (300, 200, 104), (513, 1000, 1112), (1, 4096, 4096),
@@ -166,8 +173,8 @@ def test_gpt2_bits_equal_cpu_model(g):
     say("mfma gpt2 512x768x768 vs bit model")
     ref = oracle.gemm_mfma(A, W, threads=16).view(np.uint32)
     dA, dW = dev_bf16(A), dev_bf16(W)
-    for name, C in (("256x128", g.gemm_mfma_invariant(dA, dW)), ("128x128", g.test_gemm_mfma_tile128(dA, dW)),
-                    ("W^T", g.gemm_mfma_invariant_wt(dA, _wt(dW)))):
+    for name, C in [("entry", g.gemm_mfma_invariant(dA, dW)), ("W^T", g.gemm_mfma_invariant_wt(dA, _wt(dW)))] + \
+            [(t, g.test_gemm_mfma_tile(t, dA, dW)) for t in TILES]:
         got = host_bits(C)
         assert np.array_equal(got, ref), f"{name}: {np.count_nonzero(got != ref)} outputs differ from the model"
     for M in (1, 7, 64, 257):
@@ -183,7 +190,9 @@ def test_ragged_bits_equal_cpu_model(g, M, N, K):
     ref = oracle.gemm_mfma(A, W, threads=16).view(np.uint32)
     dA, dW = dev_bf16(A), dev_bf16(W)
     assert np.array_equal(host_bits(g.gemm_mfma_invariant(dA, dW)), ref)
-    assert np.array_equal(host_bits(g.test_gemm_mfma_tile128(dA, dW)), ref)
+    for tile in TILES:
+        if tile != "256x128" or (K % 8 == 0 and N % 8 == 0):
+            assert np.array_equal(host_bits(g.test_gemm_mfma_tile(tile, dA, dW)), ref), tile
     if K % 8 == 0:
         assert np.array_equal(host_bits(g.gemm_mfma_invariant_wt(dA, _wt(dW))), ref)
 
