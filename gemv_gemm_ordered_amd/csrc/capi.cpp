@@ -340,6 +340,7 @@ static int run_gemv_ordered(const char* fn, int wt, const uint16_t* x, int64_t l
         if (ldw > gemv_ordered_wt_max_ldw())
             return fail(GGO_EUNSUPPORTED, "%s: ldwt=%lld too large for 32-bit buffer offsets", fn, (long long)ldw);
         a.vec = VEC_W | VEC_A;
+        if (aligned(x, 16) && ldx % 8 == 0 && aligned(W, 16) && ldw % 8 == 0 && K % 8 == 0) a.vec |= VEC_W16;
     } else {
         if (ldw > gemv_ordered_max_ldw() || K >= (int64_t(1) << 30))
             return fail(GGO_EUNSUPPORTED, "%s: ldw=%lld or K=%lld too large for 32-bit buffer offsets (gemm_ordered gives the same bits)",
@@ -353,6 +354,9 @@ static int run_gemv_ordered(const char* fn, int wt, const uint16_t* x, int64_t l
     if (form == 2 && !gemv_ordered_k128_ok(a))
         return fail(GGO_EUNSUPPORTED, "%s: the 128-k instance needs 4-byte column pairs of W (or W^T) and ldw "
                     "small enough for its stage ranges", fn);
+    if (form == 3 && !gemv_ordered_m1_ok(a))
+        return fail(GGO_EUNSUPPORTED, "%s: the 512-k instance serves M = 1 with W^T, 16-byte aligned x and W^T and "
+                    "row strides and K multiples of 8", fn);
     return launched(fn, launch_gemv_ordered(a, s));
 }
 
@@ -539,7 +543,10 @@ int ggo_test_gemv_instance(int kind, int rows, int form, const uint16_t* x, int6
         return fail(GGO_EINVAL, "%s: rows must be 1, 2, 4, 8 or 16", fn);
     if (tiered && rows < M) return fail(GGO_EUNSUPPORTED, "%s: an instance staging %d rows cannot serve M=%lld", fn, rows, (long long)M);
     if (!tiered && rows != 0) return fail(GGO_EINVAL, "%s: rows must be 0 for the ordered GEMV", fn);
-    if (kind == GGO_TEST_GEMV_MFMA ? form != 0 : (form != 1 && form != 2))
+    if (kind == GGO_TEST_GEMV_MFMA ? form != 0
+        : kind == GGO_TEST_GEMV_TREE ? (form != 1 && form != 2)
+        : kind == GGO_TEST_GEMV_ORDERED ? (form != 1 && form != 2)
+                                        : (form < 1 || form > 3))
         return fail(GGO_EINVAL, "%s: form %d is not an instance of kind %d", fn, form, kind);
     switch (kind) {
     case GGO_TEST_GEMV_TREE: return run_tree(fn, x, ldx, W, ldw, y, ldy, M, N, K, s, no_epi(), rows, form);

@@ -9,7 +9,8 @@
 // VEC_EP: 4-wide epilogue loads/stores. VEC_WIDE64: the 64x64 matrix-core tile may use its branch-free
 // buffer loads (16-byte aligned A, 8-byte aligned W, lda, ldw and K multiples of 8, N a multiple of 4,
 // A and W ranges below 2^31 bytes).
-enum : uint32_t { VEC_A = 1u, VEC_W = 2u, VEC_C = 4u, VEC_EP = 8u, VEC_WIDE64 = 16u };
+enum : uint32_t { VEC_A = 1u, VEC_W = 2u, VEC_C = 4u, VEC_EP = 8u, VEC_WIDE64 = 16u, VEC_W16 = 32u };   // VEC_W16:
+// 16-byte loads of x and W^T rows (16-byte aligned, ldx, ldwt and K multiples of 8)
 
 // One ordered problem as the kernel sees it (passed by value in the kernel arguments).
 struct OrdProblem {
@@ -46,10 +47,12 @@ struct GemvArgs {
     int32_t M, N, K;
     uint32_t vec;
     int32_t wt;
-    int32_t form;     // 0: chosen from M (64-k stages for M <= 4, else 128-k where allowed); 1: 64-k; 2: 128-k
+    int32_t form;     // 0: chosen from M (512-k stages for M = 1 on W^T where allowed, 64-k stages for M <= 4,
+                      // else 128-k where allowed); 1: 64-k; 2: 128-k; 3: 512-k (M = 1, W^T)
 };
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream);
 bool gemv_ordered_k128_ok(const GemvArgs& a);   // the 128-k stages can serve these operands
+bool gemv_ordered_m1_ok(const GemvArgs& a);     // the 512-k stages (M = 1, W^T) can serve these operands
 int gemv_ordered_max_ldw();   // buffer offsets of the GEMV kernel are 32-bit
 int gemv_ordered_wt_max_ldw();   // the same for W^T: a 16-row slab of W^T in one 32-bit range
 

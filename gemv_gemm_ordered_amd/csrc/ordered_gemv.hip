@@ -46,6 +46,7 @@
 // and so are the bits.
 #include <type_traits>
 
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -523,7 +524,149 @@ __global__ __launch_bounds__(THREADS) void k_gemv_ordered_k128(const GemvArgs a)
         if (r < rows && nn < a.N) a.y[static_cast<int64_t>(m0 + r) * a.ldy + nn] = acc;
     }
 }
+// ---------------------------------------------------------------------------
+// M = 1 with the weight as W^T (16-byte operands): 512-k stages. The one-lane chain costs at least
+// K x 4.5 clocks whatever the kernel does; what the 64-k kernel adds on top is a barrier every 64 adds.
+// Here a stage is 512 k, so a 4096-long chain meets 8 barriers instead of 64, and every producer load
+// instruction reads 1 KiB of one weight row (lane l: k = 8 l .. 8 l + 7 of the stage), the access pattern
+// of the tree GEMV's weight stream.
+//   wave 0        consumer: lane c < 16 owns y[0, n0 + c] and folds the stage's 512 products of its
+//                 column in ascending k (16-byte LDS reads, four adds each)
+//   waves 1 - P1  producers: wave q forms the products of rows n0 + RW1 (q - 1) .. + RW1 - 1 of W^T
+//                 (P1 = 2 waves of 8 rows; 1 or 4 waves measured the same)
+// Products, their places in the chain and the adds are those of k_gemv_ordered, so the bits are too.
+// Clock stamps at K = 4096 put the time in three parts: about 5,600 clocks until stage 0 is formed (the
+// first loads' latency), 3,400 per stage (512 dependent adds at 4.5 plus about 6 for each 16-byte LDS
+// read), and 350 per barrier.
+constexpr int NS1 = 16, SL1 = 512, P1 = 2, NBUF1 = 2, DEPTH1 = 3, RW1 = NS1 / P1;
+constexpr int THREADS1 = 64 * (1 + P1);
+constexpr int NQ1 = SL1 / 4;   // 16-byte chunks of one column's products per stage
+
+// Position (in floats) of chunk k4 (products 4 k4 .. 4 k4 + 3) of column c in a stage buffer: the chunk
+// index is XORed with c, so the 16 consumer lanes reading chunk k4 of their columns, and a producer wave
+// writing one column's chunks, fall on distinct groups of 4 banks.
+GGO_DEV int slot1(int c, int k4) { return c * SL1 + ((k4 ^ c) << 2); }
+
+struct Fetch1 {
+    uint4 w[RW1];   // k = 8 l .. 8 l + 7 of the stage, for the wave's RW1 rows of W^T
+    uint4 x;        // the same 8 k of x
+};
+
+__global__ __launch_bounds__(THREADS1) void k_gemv_ordered_m1(const GemvArgs a) {
+    __shared__ __attribute__((aligned(16))) float ps[NBUF1][NS1 * SL1];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n0 = xcd_contiguous(blockIdx.x, gridDim.x) * NS1;
+    const int nst = (a.K + SL1 - 1) / SL1;
+    // Iteration s (one barrier each): the producers form stage s, the consumer folds stage s - 1. The
+    // count is padded to a whole number of DEPTH1 groups so the producers' loop has no exit or skip
+    // inside it: a branch there made the compiler wait for every load in flight, the prefetched stages
+    // too. Stages past the last are formed from zeros into the buffer no one reads next.
+    const int iters = (nst + DEPTH1) / DEPTH1 * DEPTH1;
+    const int kbytes = a.K * 2;
+    if (wave > 0) {
+        const int q = wave - 1;
+        __amdgpu_buffer_rsrc_t wr[RW1];
+#pragma unroll
+        for (int r = 0; r < RW1; ++r) {
+            const int64_t n = n0 + RW1 * q + r;
+            wr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.W) + n * a.ldw, 0, n < a.N ? kbytes : 0,
+                                                      BUF_DWORD3);
+        }
+        const auto xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, kbytes, BUF_DWORD3);
+        auto fetch1 = [&](int stage, Fetch1& f) {   // past K (or past the last stage): zeros, no memory access
+            const int off = stage * SL1 * 2 + lane * 16;
+#pragma unroll
+            for (int r = 0; r < RW1; ++r) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr[r], off, 0, 0);
+                f.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            f.x = make_uint4(v[0], v[1], v[2], v[3]);
+        };
+        Fetch1 f[DEPTH1];
+#pragma unroll
+        for (int d = 0; d < DEPTH1; ++d) {
+            fetch1(d, f[d]);
+            __builtin_amdgcn_sched_barrier(0);   // issued stage by stage, so stage 0's loads are the oldest
+        }
+        for (int s0 = 0; s0 < iters; s0 += DEPTH1) {
+#pragma unroll
+            for (int d = 0; d < DEPTH1; ++d) {
+                const int s = s0 + d;
+                {
+                    float* buf = ps[s % NBUF1];
+                    const float xv[8] = {bf16_lo(f[d].x.x), bf16_hi(f[d].x.x), bf16_lo(f[d].x.y), bf16_hi(f[d].x.y),
+                                         bf16_lo(f[d].x.z), bf16_hi(f[d].x.z), bf16_lo(f[d].x.w), bf16_hi(f[d].x.w)};
+#pragma unroll
+                    for (int r = 0; r < RW1; ++r) {
+                        const uint4 w = f[d].w[r];
+                        const float wv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+                        const int c = RW1 * q + r;
+                        *reinterpret_cast<float4*>(buf + slot1(c, 2 * lane)) =
+                            make_float4(xv[0] * wv[0], xv[1] * wv[1], xv[2] * wv[2], xv[3] * wv[3]);
+                        *reinterpret_cast<float4*>(buf + slot1(c, 2 * lane + 1)) =
+                            make_float4(xv[4] * wv[4], xv[5] * wv[5], xv[6] * wv[6], xv[7] * wv[7]);
+                    }
+                }
+                fetch1(s + DEPTH1, f[d]);
+                __syncthreads();
+                // keep each stage's conversions after its own barrier: hoisted ahead, they made the
+                // loads of later stages complete first
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        float acc = 0.0f;   // +0.0: the chain's start
+        const int c = lane & (NS1 - 1);
+        // The output pointer's scalar load completes here: outstanding inside the loop, it made each
+        // stage's first LDS wait a wait for every read in flight (scalar loads return out of order).
+        float* const y = a.y;
+        asm volatile("" ::"s"(y));
+        // The reads of the next 64 k are issued before the adds of the current 64. Measured against
+        // this: 8 or 4 chunks per burst (more bursts, each with a fixed cost), one read every four adds
+        // 12 chunks ahead (each read inside the chain costs more than in a burst), and all 64 lanes
+        // reading 16 k of 16 columns with the quad's products taken by DPP broadcasts in the adds
+        // (a quarter of the reads, but a dependent DPP add costs twice a plain one).
+        constexpr int G = 16, NG = NQ1 / G;
+        for (int s = 0; s < iters; ++s) {
+            if (s >= 1 && s <= nst && lane < NS1) {   // stage s - 1, formed in the previous iteration
+                const float* src = ps[(s - 1) % NBUF1];
+                float4 cb[2][G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) cb[0][j] = *reinterpret_cast<const float4*>(src + slot1(c, j));
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    if (gi + 1 < NG) {
+#pragma unroll
+                        for (int j = 0; j < G; ++j)
+                            cb[(gi + 1) & 1][j] = *reinterpret_cast<const float4*>(src + slot1(c, (gi + 1) * G + j));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {   // ascending k
+                        const float4 v = cb[gi & 1][j];
+                        acc = acc + v.x;
+                        acc = acc + v.y;
+                        acc = acc + v.z;
+                        acc = acc + v.w;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __syncthreads();
+        }
+        if (lane < NS1 && n0 + c < a.N) y[n0 + c] = acc;
+    }
+}
+
 }  // namespace
+
+// M = 1, W^T, 16-byte loads that never straddle the end of a row, byte offsets within 32 bits
+bool gemv_ordered_m1_ok(const GemvArgs& a) {
+    return a.wt && a.M == 1 && (a.vec & VEC_W16) && a.K <= (1 << 29) - 4 * DEPTH1 * SL1;
+}
 
 bool gemv_ordered_k128_ok(const GemvArgs& a) {
     return a.wt || ((a.vec & VEC_W) && a.ldw <= ((1 << 30) - (1 << 16)) / (KC2 + 1));   // 32-bit stage ranges
@@ -534,7 +677,9 @@ hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
     // M > 4 with operands it can take: the 128-k form (same bits; see k_gemv_ordered_k128); form 1 or 2
     // forces the 64-k or the 128-k form (the caller has checked that the latter can serve)
     const bool k128 = a.form == 2 || (a.form == 0 && a.M > 4 && gemv_ordered_k128_ok(a));
-    if (k128 && a.wt)
+    if (a.form == 3 || (a.form == 0 && a.M == 1 && gemv_ordered_m1_ok(a)))
+        hipLaunchKernelGGL(k_gemv_ordered_m1, dim3((a.N + NS1 - 1) / NS1), dim3(THREADS1), 0, stream, a);
+    else if (k128 && a.wt)
         hipLaunchKernelGGL((k_gemv_ordered_k128<true>), grid, dim3(THREADS), 0, stream, a);
     else if (k128)
         hipLaunchKernelGGL((k_gemv_ordered_k128<false>), grid, dim3(THREADS), 0, stream, a);

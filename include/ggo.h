@@ -26,7 +26,7 @@
  *    (gemv_ordered, gemv_ordered_wt, gemv_tree, gemv_mfma_invariant) do
  *    choose, from M, an instance of their kernel: how many rows of x a
  *    workgroup stages (M rounded up to 1, 2, 4, 8 or 16), and for the ordered
- *    GEMV 64- or 128-k stages. Every instance gives every output the same
+ *    GEMV 64-, 128- or (M = 1, W^T) 512-k stages. Every instance gives every output the same
  *    chains, order and tree, hence the same bits; ggo_test_gemv_instance runs
  *    any instance at any M so that this is tested, not assumed.
  *  - Return value: GGO_OK (0), or a negative error code; the calling thread's
@@ -378,7 +378,10 @@ int ggo_test_gemm_ordered_tile(int tile, const void *A, int a_dtype, int64_t lda
  *                                   outputs per workgroup
  *         GGO_TEST_GEMV_ORDERED     gemv_ordered(x, W): rows 0; form 1 = 64-k
  *                                   stages, 2 = 128-k stages
- *         GGO_TEST_GEMV_ORDERED_WT  gemv_ordered_wt(x, W^T): as above
+ *         GGO_TEST_GEMV_ORDERED_WT  gemv_ordered_wt(x, W^T): as above, and
+ *                                   form 3 = 512-k stages (M = 1, 16-byte
+ *                                   aligned x and W^T, row strides and K
+ *                                   multiples of 8)
  *         GGO_TEST_GEMV_MFMA        gemv_mfma_invariant(x, W^T): rows in
  *                                   {1,2,4,8,16}; form 0
  *   rows  rows of x the instance stages per workgroup; must be >= M

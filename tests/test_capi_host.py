@@ -160,5 +160,10 @@ def test_gemv_instance_hook_rejects_what_it_cannot_run(g):
     # the 128-k ordered instance needs 4-byte column pairs of W
     assert lib.ggo_test_gemv_instance(1, 0, 2, 16, 8, 16, 7, 16, 8, 4, 7, 8, null) == -2
     assert lib.ggo_test_gemv_instance(1, 0, 2, 16, 8, 18, 8, 16, 8, 4, 8, 8, null) == -2
+    # the 512-k ordered instance: W^T form only (form 3 of kind 2), M = 1, 16-byte operands
+    assert lib.ggo_test_gemv_instance(1, 0, 3, 16, 8, 16, 8, 16, 8, 1, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(2, 0, 3, 16, 8, 16, 8, 16, 8, 2, 8, 8, null) == -2
+    assert lib.ggo_test_gemv_instance(2, 0, 3, 8, 8, 16, 8, 16, 8, 1, 8, 8, null) == -2
+    assert lib.ggo_test_gemv_instance(2, 0, 4, 16, 8, 16, 8, 16, 8, 1, 8, 8, null) == -1
     # empty problems launch nothing
     assert lib.ggo_test_gemv_instance(0, 1, 2, null, 8, null, 8, null, 8, 0, 8, 8, null) == 0

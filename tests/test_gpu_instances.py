@@ -57,7 +57,7 @@ def test_tree_instances_at_the_decode_shape(g, decode, M):
 def test_ordered_instances_at_the_decode_shape(g, decode, M):
     ref = decode["ordered"][:M]
     for kind, W in (("ordered", decode["dW"]), ("ordered_wt", decode["dWT"])):
-        for form in (1, 2):
+        for form in (1, 2, 3) if kind == "ordered_wt" and M == 1 else (1, 2):
             say(f"gemv {kind} instance form={form} M={M}")
             got = host_bits(g.test_gemv_instance(kind, 0, form, decode["dx"][:M], W))
             assert np.array_equal(got, ref), (kind, M, form)
@@ -77,7 +77,7 @@ def test_mfma_gemv_instances_at_the_decode_shape(g, decode, M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 37, 200), (3, 100, 2056), (5, 33, 4096), (2, 300, 1000), (6, 17, 4104),
-                                   (8, 129, 776)])
+                                   (8, 129, 776), (1, 100, 4104), (1, 1000, 1536), (1, 17, 8)])
 def test_instances_on_ragged_shapes(g, M, N, K):
     x = synth.normal_bf16(M + N + K, "inst.x", (M, K))
     W = synth.normal_bf16(M + N + K, "inst.W", (K, N), 0.02)
@@ -93,6 +93,8 @@ def test_instances_on_ragged_shapes(g, M, N, K):
             assert np.array_equal(host_bits(g.test_gemv_instance("ordered", 0, form, dx, dW)), ref_o), form
         if K % 4 == 0:
             assert np.array_equal(host_bits(g.test_gemv_instance("ordered_wt", 0, form, dx, dWT)), ref_o), form
+    if M == 1 and K % 8 == 0:   # the 512-k stages of the W^T form
+        assert np.array_equal(host_bits(g.test_gemv_instance("ordered_wt", 0, 3, dx, dWT)), ref_o)
     if K % 8 == 0:
         ref_m = f32_bits(oracle.gemm_mfma(x, W))
         for rows in TIERS:
