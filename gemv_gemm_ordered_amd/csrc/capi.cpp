@@ -201,8 +201,8 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
 // Every instance gives every output the same bits (the same opcode, the same operand values in the same
 // groups of 32 k, ascending), so the choice moves no bit. `force` (a MFMA_TILE_* value, or -1) lets the
 // test hook run any instance.
-enum { MFMA_TILE_256x128 = 0, MFMA_TILE_128x128 = 1, MFMA_TILE_64x64 = 2 };
-constexpr int64_t MFMA_SMALL_WEIGHT = int64_t(1) << 20;
+enum { MFMA_TILE_256x128 = 0, MFMA_TILE_128x128 = 1, MFMA_TILE_64x64 = 2, MFMA_TILE_256x256 = 3 };
+constexpr int64_t MFMA_SMALL_WEIGHT = int64_t(1) << 20, MFMA_LARGE_WEIGHT = int64_t(1) << 24;
 
 int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, void* C, int64_t ldc,
              int64_t M, int64_t N, int64_t K, hipStream_t s, int force, const Epi& ep) {
@@ -214,15 +214,19 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
     if (K == 0) return launched(fn, epi_zero(C, ldc, M, N, ep, s));
     const bool wide_ok = aligned(A, 16) && lda % 8 == 0 && aligned(W, 16) && ldw % 8 == 0 &&
                          lda < (int64_t(1) << 22) && ldw < (int64_t(1) << 22) && K % 8 == 0 && N % 8 == 0;
+    // the tile follows the weight (and what the operands allow), never M
     const int tile = force >= 0 ? force
                    : N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x64
-                   : wide_ok ? MFMA_TILE_256x128 : MFMA_TILE_128x128;
-    if (tile == MFMA_TILE_256x128 && !wide_ok)
-        return fail(GGO_EUNSUPPORTED, "%s: the 256x128 instance needs 16-byte aligned operands with row strides and K, N "
-                    "multiples of 8", fn);
+                   : !wide_ok ? MFMA_TILE_128x128
+                   : N * K >= MFMA_LARGE_WEIGHT ? MFMA_TILE_256x256 : MFMA_TILE_256x128;
+    if ((tile == MFMA_TILE_256x128 || tile == MFMA_TILE_256x256) && !wide_ok)
+        return fail(GGO_EUNSUPPORTED, "%s: the %s instance needs 16-byte aligned operands with row strides and K, N "
+                    "multiples of 8", fn, tile == MFMA_TILE_256x128 ? "256x128" : "256x256");
     int bm, bn;
     if (tile == MFMA_TILE_256x128)
         mfma_tile_shape(&bm, &bn);
+    else if (tile == MFMA_TILE_256x256)
+        mfma_tile_shape_t256x256(&bm, &bn);
     else if (tile == MFMA_TILE_128x128)
         mfma_tile_shape_t128(&bm, &bn);
     else
@@ -255,6 +259,7 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
         aligned(C, ep.out_bf16 ? 8 : 16) && ldc % 4 == 0)
         a.vec |= VEC_EP;
     return launched(fn, tile == MFMA_TILE_256x128   ? launch_gemm_mfma_invariant(a, s)
+                        : tile == MFMA_TILE_256x256 ? launch_gemm_mfma_invariant_256(a, s)
                         : tile == MFMA_TILE_128x128 ? launch_gemm_mfma_t128(a, s)
                                                     : launch_gemm_mfma_t64(a, s));
 }
@@ -525,10 +530,11 @@ int ggo_test_gemm_mfma_tile128(const uint16_t* A, int64_t lda, const uint16_t* W
 
 int ggo_test_gemm_mfma_tile(int tile, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C,
                             int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
-    if (tile != GGO_TEST_MFMA_TILE_256x128 && tile != GGO_TEST_MFMA_TILE_128x128 && tile != GGO_TEST_MFMA_TILE_64x64)
+    if (tile != GGO_TEST_MFMA_TILE_256x128 && tile != GGO_TEST_MFMA_TILE_128x128 && tile != GGO_TEST_MFMA_TILE_64x64 &&
+        tile != GGO_TEST_MFMA_TILE_256x256)
         return fail(GGO_EINVAL, "ggo_test_gemm_mfma_tile: unknown tile %d", tile);
     static_assert(GGO_TEST_MFMA_TILE_256x128 == MFMA_TILE_256x128 && GGO_TEST_MFMA_TILE_128x128 == MFMA_TILE_128x128 &&
-                  GGO_TEST_MFMA_TILE_64x64 == MFMA_TILE_64x64, "");
+                  GGO_TEST_MFMA_TILE_64x64 == MFMA_TILE_64x64 && GGO_TEST_MFMA_TILE_256x256 == MFMA_TILE_256x256, "");
     return run_mfma("ggo_test_gemm_mfma_tile", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), tile,
                     no_epi());
 }

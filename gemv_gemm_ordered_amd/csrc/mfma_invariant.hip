@@ -694,8 +694,10 @@ GGO_DEV void stage_rows(const f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ], fl
 // NST, so every load and read names its buffer statically: the compiler can
 // then see that the loads into one buffer never alias the reads of another.
 // The stages fill most of the LDS, so one workgroup runs per CU (one wave per
-// SIMD), and registers are not worth saving.
-template <int BN, int BK, int NST, bool WT>
+// SIMD), and registers are not worth saving. EPI: the fused epilogue is compiled in (a separate
+// instance: with its code present the compiler moved the accumulators out of their registers before
+// the epilogue test, which at 256 x 256 spilled them on the plain path too).
+template <int BN, int BK, int NST, bool WT, bool EPI>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_mfma_invariant(const MfmaArgs p) {
     using G = Geo<BN, BK, WT>;
@@ -766,7 +768,7 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the trailing empty-range loads have landed before the workgroup ends
 
     // lane holds C[row][col .. col+3] of each block: row = lane % 16, col = 4 * (lane / 16)
-    if (!epi_identity(p.ep)) {
+    if constexpr (EPI) {
         // Fused epilogue. Each wave stages 32 rows of its 128 x (BN/2) results at a time in a region of its
         // own in LDS (the operand ring is free now), then walks them row-major in a plain loop: coalesced
         // bias / residual loads and stores, and the epilogue's code appears once instead of once per
@@ -797,18 +799,22 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
                 // Whole pass in range: every bias / residual load of the pass goes out first, so the
                 // pass waits for memory once instead of once per 4 results.
                 constexpr int IT = PR * (BN / 8) / 64;
-                float4 bv[IT], rv[IT];
+                constexpr int IC = IT < 8 ? IT : 8;   // bias and residual loads in flight per chunk
 #pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    const int e = lane + 64 * i, rl = e / (BN / 8), c4 = e % (BN / 8);
-                    bv[i] = epi_bias4(p.ep, col0 + 4 * c4);
-                    rv[i] = epi_res4(p.ep, row0 + rl, col0 + 4 * c4);
-                }
+                for (int i0 = 0; i0 < IT; i0 += IC) {
+                    float4 bv[IC], rv[IC];
 #pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    const int e = lane + 64 * i, rl = e / (BN / 8), c4 = e % (BN / 8);
-                    const float4 y = *reinterpret_cast<const float4*>(region + rl * RS + 4 * c4);
-                    epi_finish4(p.ep, p.C, p.ldc, row0 + rl, col0 + 4 * c4, y, bv[i], rv[i]);
+                    for (int i = 0; i < IC; ++i) {
+                        const int e = lane + 64 * (i0 + i), rl = e / (BN / 8), c4 = e % (BN / 8);
+                        bv[i] = epi_bias4(p.ep, col0 + 4 * c4);
+                        rv[i] = epi_res4(p.ep, row0 + rl, col0 + 4 * c4);
+                    }
+#pragma unroll
+                    for (int i = 0; i < IC; ++i) {
+                        const int e = lane + 64 * (i0 + i), rl = e / (BN / 8), c4 = e % (BN / 8);
+                        const float4 y = *reinterpret_cast<const float4*>(region + rl * RS + 4 * c4);
+                        epi_finish4(p.ep, p.C, p.ldc, row0 + rl, col0 + 4 * c4, y, bv[i], rv[i]);
+                    }
                 }
                 __syncthreads();                    // before the next pass overwrites the region
                 continue;
@@ -852,22 +858,40 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
 
 // The configuration both entry points run: 256 x 128 tiles, 64-k stages, three in flight.
 constexpr int BN_MAIN = 128, BK_MAIN = 64, NST_MAIN = 3;
+// The wide instance for large weights: 256 x 256 outputs per workgroup (256 accumulator registers per lane),
+// 32-k tiles four deep (128 KiB of LDS). Per k it reads a third less of A and W per product than 256 x 128;
+// with fewer tiles it fills the chip only on large weights.
+constexpr int BN_LARGE = 256, BK_LARGE = 32, NST_LARGE = 4;
 
 }  // namespace t256
 }  // namespace
 
 void mfma_tile_shape(int* bm, int* bn) { *bm = t256::BM; *bn = t256::BN_MAIN; }
+void mfma_tile_shape_t256x256(int* bm, int* bn) { *bm = t256::BM; *bn = t256::BN_LARGE; }
 void mfma_tile_shape_t128(int* bm, int* bn) { *bm = 128; *bn = 128; }
 void mfma_tile_shape_t64(int* bm, int* bn) { *bm = 64; *bn = 64; }
 
-hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, false>),
-                       dim3(a.tiles_m * a.tiles_n), dim3(t256::THREADS), 0, stream, a);
+template <int BN, int BK, int NST>
+static hipError_t launch_t256(const MfmaArgs& a, hipStream_t stream) {
+    if (epi_identity(a.ep))
+        hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<BN, BK, NST, false, false>), dim3(a.tiles_m * a.tiles_n),
+                           dim3(t256::THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<BN, BK, NST, false, true>), dim3(a.tiles_m * a.tiles_n),
+                           dim3(t256::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, true>),
+hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream) {
+    return launch_t256<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN>(a, stream);
+}
+
+hipError_t launch_gemm_mfma_invariant_256(const MfmaArgs& a, hipStream_t stream) {
+    return launch_t256<t256::BN_LARGE, t256::BK_LARGE, t256::NST_LARGE>(a, stream);
+}
+
+hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream) {   // no epilogue on this entry
+    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, true, false>),
                        dim3(a.tiles_m * a.tiles_n), dim3(t256::THREADS), 0, stream, a);
     return hipGetLastError();
 }

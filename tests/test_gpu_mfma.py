@@ -102,14 +102,15 @@ def test_7b_projection_sampled(g, n):
     assert np.array_equal(sub, full[1000:1128])
 
 
-TILES = ("256x128", "128x128", "64x64")
+TILES = ("256x128", "256x256", "128x128", "64x64")
+WIDE = ("256x128", "256x256")   # need K and N multiples of 8 (and aligned operands)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 64), (300, 200, 100), (513, 1000, 1111), (1, 4096, 4096),
                                    (2048, 4096, 1024), (4096, 4096, 4096), (4096, 11008, 4096), (7, 33, 31),
                                    (513, 1000, 1112), (300, 200, 104), (257, 136, 1000), (1, 8, 8), (255, 1032, 72)])
 def test_tile_instances_agree_bitwise(g, M, N, K):
-    """The 256x128, 128x128 and 64x64 tile instances feed every output the same operand values in the
+    """The 256x128, 256x256, 128x128 and 64x64 tile instances feed every output the same operand values in the
     same 32-k groups ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.2.2: block
     sizes do not enter the order), so their outputs, and the entry point's, must be identical bit for bit."""
     say(f"mfma tile instances M={M} N={N} K={K}")
@@ -118,7 +119,7 @@ def test_tile_instances_agree_bitwise(g, M, N, K):
     dA, dW = dev_bf16(A), dev_bf16(W)
     entry = host_bits(g.gemm_mfma_invariant(dA, dW))
     for tile in TILES:
-        if tile == "256x128" and (K % 8 or N % 8):
+        if tile in WIDE and (K % 8 or N % 8):
             continue
         got = host_bits(g.test_gemm_mfma_tile(tile, dA, dW))
         assert np.array_equal(got, entry), f"{tile}: {np.count_nonzero(got != entry)} outputs differ"
@@ -191,7 +192,7 @@ def test_ragged_bits_equal_cpu_model(g, M, N, K):
     dA, dW = dev_bf16(A), dev_bf16(W)
     assert np.array_equal(host_bits(g.gemm_mfma_invariant(dA, dW)), ref)
     for tile in TILES:
-        if tile != "256x128" or (K % 8 == 0 and N % 8 == 0):
+        if tile not in WIDE or (K % 8 == 0 and N % 8 == 0):
             assert np.array_equal(host_bits(g.test_gemm_mfma_tile(tile, dA, dW)), ref), tile
     if K % 8 == 0:
         assert np.array_equal(host_bits(g.gemm_mfma_invariant_wt(dA, _wt(dW))), ref)
