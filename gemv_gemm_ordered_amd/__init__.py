@@ -409,11 +409,11 @@ def test_gemm_mfma_tile128(A, W, C=None, stream=None):
     return _mfma("ggo_test_gemm_mfma_tile128", A, W, C, stream)
 
 
-MFMA_TILES = {"256x128": 0, "128x128": 1, "64x64": 2, "256x256": 3}
+MFMA_TILES = {"256x128": 0, "128x128": 1, "64x64": 2, "256x256": 3, "128x128_lds": 4, "64x128_lds": 5}
 
 
 def test_gemm_mfma_tile(tile, A, W, C=None, stream=None):
-    """Test hook: gemm_mfma_invariant on the chosen tile instance ('256x128', '256x256', '128x128' or '64x64'); must
+    """Test hook: gemm_mfma_invariant on the chosen tile instance (a key of MFMA_TILES); must
     give gemm_mfma_invariant's bits."""
     lda, ldw = _rowmajor(A, "A"), _rowmajor(W, "W")
     M, K = A.shape

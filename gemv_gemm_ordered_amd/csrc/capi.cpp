@@ -190,19 +190,28 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     return launched(fn, launch_gemm_ordered(g, (int)total, a_dtype == GGO_F32, kind, wide, s));
 }
 
-// Tile of the matrix-core GEMM, from the weight's shape and the operands' alignment, never from M:
-//  - a weight of at most 2^20 elements: 64x64 tiles (any operands), so that a small weight still puts
-//    more workgroups on the 256 CUs at small M (768 x 768: 12 instead of 6 at M <= 64);
-//  - otherwise 256x128 tiles for 16-byte aligned operands with row strides that are multiples of 8 (and
-//    below 2^22: its buffer offsets are 32-bit) and K and N multiples of 8 (it loads 16-byte chunks
-//    through range-checked buffer descriptors that end at the caller's last element, and the range check
-//    drops a whole dword that straddles that end, so no chunk may straddle it);
-//  - else 128x128 tiles (any operands).
+// Tile of the matrix-core GEMM, from the weight's shape and the operands' alignment, never from M.
+// "Wide" operands are 16-byte aligned with row strides that are multiples of 8 (and below 2^22: buffer
+// offsets are 32-bit) and K and N multiples of 8: the direct-to-LDS instances load 16-byte chunks through
+// range-checked buffer descriptors that end at the caller's last element, and the range check drops a
+// whole dword that straddles that end, so no chunk may straddle it. With wide operands:
+//  - a weight of at most 2^20 elements: 64x128 tiles, so that a small weight still fills more CUs at
+//    small M;
+//  - up to 2^24 elements with K <= 1024: 128x128 tiles (few k-steps per workgroup: the first loads' latency
+//    and the stores weigh more than a larger tile's efficiency);
+//  - up to 2^24 elements with a longer K: 256x128;
+//  - from 2^24 elements: 256x256.
+// Other operands take the register-staged instances: 64x64 tiles for weights of at most 2^20 elements,
+// else 128x128.
 // Every instance gives every output the same bits (the same opcode, the same operand values in the same
 // groups of 32 k, ascending), so the choice moves no bit. `force` (a MFMA_TILE_* value, or -1) lets the
 // test hook run any instance.
-enum { MFMA_TILE_256x128 = 0, MFMA_TILE_128x128 = 1, MFMA_TILE_64x64 = 2, MFMA_TILE_256x256 = 3 };
+enum {
+    MFMA_TILE_256x128 = 0, MFMA_TILE_128x128 = 1, MFMA_TILE_64x64 = 2, MFMA_TILE_256x256 = 3,
+    MFMA_TILE_128x128_LDS = 4, MFMA_TILE_64x128_LDS = 5
+};
 constexpr int64_t MFMA_SMALL_WEIGHT = int64_t(1) << 20, MFMA_LARGE_WEIGHT = int64_t(1) << 24;
+constexpr int64_t MFMA_SHORT_K = 1024;
 
 int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, void* C, int64_t ldc,
              int64_t M, int64_t N, int64_t K, hipStream_t s, int force, const Epi& ep) {
@@ -216,17 +225,26 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
                          lda < (int64_t(1) << 22) && ldw < (int64_t(1) << 22) && K % 8 == 0 && N % 8 == 0;
     // the tile follows the weight (and what the operands allow), never M
     const int tile = force >= 0 ? force
-                   : N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x64
-                   : !wide_ok ? MFMA_TILE_128x128
-                   : N * K >= MFMA_LARGE_WEIGHT ? MFMA_TILE_256x256 : MFMA_TILE_256x128;
-    if ((tile == MFMA_TILE_256x128 || tile == MFMA_TILE_256x256) && !wide_ok)
+                   : !wide_ok ? (N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x64 : MFMA_TILE_128x128)
+                   : N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x128_LDS
+                   : N * K >= MFMA_LARGE_WEIGHT ? MFMA_TILE_256x256
+                   : K <= MFMA_SHORT_K ? MFMA_TILE_128x128_LDS : MFMA_TILE_256x128;
+    static const char* const names[] = {"256x128", "128x128", "64x64", "256x256", "128x128 direct-to-LDS",
+                                        "64x128 direct-to-LDS"};
+    const bool needs_wide = tile == MFMA_TILE_256x128 || tile == MFMA_TILE_256x256 || tile == MFMA_TILE_128x128_LDS ||
+                            tile == MFMA_TILE_64x128_LDS;
+    if (needs_wide && !wide_ok)
         return fail(GGO_EUNSUPPORTED, "%s: the %s instance needs 16-byte aligned operands with row strides and K, N "
-                    "multiples of 8", fn, tile == MFMA_TILE_256x128 ? "256x128" : "256x256");
+                    "multiples of 8", fn, names[tile]);
     int bm, bn;
     if (tile == MFMA_TILE_256x128)
         mfma_tile_shape(&bm, &bn);
     else if (tile == MFMA_TILE_256x256)
         mfma_tile_shape_t256x256(&bm, &bn);
+    else if (tile == MFMA_TILE_128x128_LDS)
+        mfma_tile_shape_lds128(&bm, &bn);
+    else if (tile == MFMA_TILE_64x128_LDS)
+        mfma_tile_shape_lds64x128(&bm, &bn);
     else if (tile == MFMA_TILE_128x128)
         mfma_tile_shape_t128(&bm, &bn);
     else
@@ -258,10 +276,12 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
     if ((!ep.bias || aligned(ep.bias, 16)) && (!ep.res || (aligned(ep.res, 16) && ep.ldr % 4 == 0)) &&
         aligned(C, ep.out_bf16 ? 8 : 16) && ldc % 4 == 0)
         a.vec |= VEC_EP;
-    return launched(fn, tile == MFMA_TILE_256x128   ? launch_gemm_mfma_invariant(a, s)
-                        : tile == MFMA_TILE_256x256 ? launch_gemm_mfma_invariant_256(a, s)
-                        : tile == MFMA_TILE_128x128 ? launch_gemm_mfma_t128(a, s)
-                                                    : launch_gemm_mfma_t64(a, s));
+    return launched(fn, tile == MFMA_TILE_256x128       ? launch_gemm_mfma_invariant(a, s)
+                        : tile == MFMA_TILE_256x256     ? launch_gemm_mfma_invariant_256(a, s)
+                        : tile == MFMA_TILE_128x128_LDS ? launch_gemm_mfma_lds128(a, s)
+                        : tile == MFMA_TILE_64x128_LDS  ? launch_gemm_mfma_lds64x128(a, s)
+                        : tile == MFMA_TILE_128x128     ? launch_gemm_mfma_t128(a, s)
+                                                        : launch_gemm_mfma_t64(a, s));
 }
 
 }  // namespace
@@ -530,11 +550,12 @@ int ggo_test_gemm_mfma_tile128(const uint16_t* A, int64_t lda, const uint16_t* W
 
 int ggo_test_gemm_mfma_tile(int tile, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* C,
                             int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
-    if (tile != GGO_TEST_MFMA_TILE_256x128 && tile != GGO_TEST_MFMA_TILE_128x128 && tile != GGO_TEST_MFMA_TILE_64x64 &&
-        tile != GGO_TEST_MFMA_TILE_256x256)
+    if (tile < GGO_TEST_MFMA_TILE_256x128 || tile > GGO_TEST_MFMA_TILE_64x128_LDS)
         return fail(GGO_EINVAL, "ggo_test_gemm_mfma_tile: unknown tile %d", tile);
     static_assert(GGO_TEST_MFMA_TILE_256x128 == MFMA_TILE_256x128 && GGO_TEST_MFMA_TILE_128x128 == MFMA_TILE_128x128 &&
-                  GGO_TEST_MFMA_TILE_64x64 == MFMA_TILE_64x64 && GGO_TEST_MFMA_TILE_256x256 == MFMA_TILE_256x256, "");
+                  GGO_TEST_MFMA_TILE_64x64 == MFMA_TILE_64x64 && GGO_TEST_MFMA_TILE_256x256 == MFMA_TILE_256x256 &&
+                  GGO_TEST_MFMA_TILE_128x128_LDS == MFMA_TILE_128x128_LDS &&
+                  GGO_TEST_MFMA_TILE_64x128_LDS == MFMA_TILE_64x128_LDS, "");
     return run_mfma("ggo_test_gemm_mfma_tile", A, lda, W, ldw, C, ldc, M, N, K, static_cast<hipStream_t>(stream), tile,
                     no_epi());
 }

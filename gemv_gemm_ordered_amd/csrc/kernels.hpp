@@ -89,10 +89,14 @@ struct MfmaArgs {
 };
 void mfma_tile_shape(int* bm, int* bn);        // 256x128 instance (16-byte aligned operands)
 void mfma_tile_shape_t256x256(int* bm, int* bn);   // 256x256 instance (the same operands)
+void mfma_tile_shape_lds128(int* bm, int* bn);     // 128x128 direct-to-LDS instance (the same operands)
+void mfma_tile_shape_lds64x128(int* bm, int* bn);  // 64x128 direct-to-LDS instance (the same operands)
 void mfma_tile_shape_t128(int* bm, int* bn);   // 128x128 instance (any operands)
 void mfma_tile_shape_t64(int* bm, int* bn);    // 64x64 instance (any operands)
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_invariant_256(const MfmaArgs& a, hipStream_t stream);   // the 256x256 instance
+hipError_t launch_gemm_mfma_lds128(const MfmaArgs& a, hipStream_t stream);           // 128x128, direct to LDS
+hipError_t launch_gemm_mfma_lds64x128(const MfmaArgs& a, hipStream_t stream);        // 64x128, direct to LDS
 hipError_t launch_gemm_mfma_t128(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_t64(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream);   // W given as W^T [N, K]

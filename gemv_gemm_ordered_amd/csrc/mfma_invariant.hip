@@ -356,7 +356,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_mfma_reg(const MfmaArgs p) {
 // gets element i of four consecutive 16-element rows).
 namespace t256 {
 
-constexpr int BM = 256, THREADS = 256;
+constexpr int BM_MAIN = 256, THREADS = 256;
 constexpr int BUF_DWORD3 = 0x00020000;   // buffer descriptor word 3: raw 32-bit data, range checked
 constexpr int WAIT_VM0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima)
 constexpr int WAIT_LGKM0 = 0xC07F;       // s_waitcnt lgkmcnt(0) (vmcnt, expcnt left at their maxima)
@@ -370,10 +370,10 @@ constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // Tile geometry: 256(m) x BN(n) x BK(k), BN in {128, 256}, BK in {32, 64};
 // four waves in a 2 x 2 grid, each owning 128 x BN/2 outputs. WT: the caller
 // passes W transposed ([N, K], k contiguous), and its tile is held like A's.
-template <int BN, int BK, bool WT = false> struct Geo {
+template <int BM, int BN, int BK, bool WT = false> struct Geo {
     static constexpr int CA = BK / 8;                      // 16-byte chunks per A row (and per W^T row)
     static constexpr int CB = WT ? BK / 8 : BN / 8;        // 16-byte chunks per W row (W^T: per row of n)
-    static constexpr int WI = 8, WJ = BN / 32;             // 16 x 16 blocks per wave (rows, columns)
+    static constexpr int WI = BM / 32, WJ = BN / 32;             // 16 x 16 blocks per wave (rows, columns)
     static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
     static constexpr int A_LOADS = BM * CA / THREADS;      // direct-to-LDS loads per thread and tile
     static constexpr int B_LOADS = BK * BN / 8 / THREADS;
@@ -426,7 +426,7 @@ struct Panels {
     int na, nb;
 };
 
-template <int BN, int BK, bool WT>
+template <int BM, int BN, int BK, bool WT>
 GGO_DEV Panels panels(const Ctx& c, int kt) {
     const MfmaArgs& p = *c.p;
     const bool live = kt < c.nkt;
@@ -448,25 +448,25 @@ GGO_DEV Panels panels(const Ctx& c, int kt) {
 
 // LDS destination of this wave's direct-to-LDS load l of a tile (A's chunks first, then W's): each load
 // instruction writes 64 consecutive 16-byte chunks.
-template <int BN, int BK, bool WT>
+template <int BM, int BN, int BK, bool WT>
 GGO_DEV lds_t* load_dst(const Ctx& c, uint16_t* __restrict__ sa, int l) {
-    using G = Geo<BN, BK, WT>;
+    using G = Geo<BM, BN, BK, WT>;
     return (lds_t*)(l < G::A_LOADS ? sa + (l * THREADS + c.wave * 64) * 8
                                    : sa + G::A_ELEMS + ((l - G::A_LOADS) * THREADS + c.wave * 64) * 8);
 }
 
-template <int BN, int BK, bool WT>
+template <int BM, int BN, int BK, bool WT>
 GGO_DEV void issue(const Ctx& c, int kt, uint16_t* __restrict__ sa) {
-    using G = Geo<BN, BK, WT>;
-    const Panels pn = panels<BN, BK, WT>(c, kt);
+    using G = Geo<BM, BN, BK, WT>;
+    const Panels pn = panels<BM, BN, BK, WT>(c, kt);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(pn.a, 0, pn.na, BUF_DWORD3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(pn.b, 0, pn.nb, BUF_DWORD3);
 #pragma unroll
     for (int l = 0; l < G::LOADS; ++l) {
         if (l < G::A_LOADS)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, load_dst<BN, BK, WT>(c, sa, l), 16, c.aoff[l], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, load_dst<BM, BN, BK, WT>(c, sa, l), 16, c.aoff[l], 0, 0, 0);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, load_dst<BN, BK, WT>(c, sa, l), 16, c.boff[l - G::A_LOADS], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, load_dst<BM, BN, BK, WT>(c, sa, l), 16, c.boff[l - G::A_LOADS], 0, 0, 0);
     }
 }
 
@@ -478,9 +478,9 @@ GGO_DEV void issue(const Ctx& c, int kt, uint16_t* __restrict__ sa) {
 // its own LDS writes and for its own reads of the tile before it, which is
 // all the ordering this barrier has to provide: after it, tile kt can be read
 // and the buffer of tile kt-1 can be refilled.
-template <int BN, int BK, int NST, bool WT>
+template <int BM, int BN, int BK, int NST, bool WT>
 GGO_DEV void land(const Ctx& c, int kt, uint16_t* __restrict__ cur) {
-    using G = Geo<BN, BK, WT>;
+    using G = Geo<BM, BN, BK, WT>;
     const MfmaArgs& p = *c.p;
     __builtin_amdgcn_s_waitcnt(wait_vm(G::LOADS * (NST - 2)));
     if (kt < c.nkt && (kt + 1) * BK > p.K) {
@@ -510,20 +510,20 @@ GGO_DEV void land(const Ctx& c, int kt, uint16_t* __restrict__ cur) {
 // The operand fragments of one group of 32 k: per lane 8 consecutive k of one
 // row of A per 16-row block, and of one column of W per 16-column block (W's
 // as two 4-k halves, one per transposing read, unless W^T is given).
-template <int BN, int BK, bool WT> struct Frags {
-    bf16x8 a[Geo<BN, BK, WT>::WI];
-    i16x4 wl[Geo<BN, BK, WT>::WJ], wh[Geo<BN, BK, WT>::WJ];
+template <int BM, int BN, int BK, bool WT> struct Frags {
+    bf16x8 a[Geo<BM, BN, BK, WT>::WI];
+    i16x4 wl[Geo<BM, BN, BK, WT>::WJ], wh[Geo<BM, BN, BK, WT>::WJ];
 };
 
 // LDS read instructions per group: A's blocks, then W's (two per block unless W^T is given).
-template <int BN, int BK, bool WT>
-constexpr int reads_per_group() { return Geo<BN, BK, WT>::WI + (WT ? 1 : 2) * Geo<BN, BK, WT>::WJ; }
+template <int BM, int BN, int BK, bool WT>
+constexpr int reads_per_group() { return Geo<BM, BN, BK, WT>::WI + (WT ? 1 : 2) * Geo<BM, BN, BK, WT>::WJ; }
 
 // Read r of group g of the tile in `buf` into f. The order (A block 0, then
 // W's blocks, then A's other blocks) is the order the MFMAs need them in.
-template <int BN, int BK, bool WT>
-GGO_DEV void read_one(const Ctx& c, const uint16_t* __restrict__ buf, int g, int r, Frags<BN, BK, WT>& f) {
-    using G = Geo<BN, BK, WT>;
+template <int BM, int BN, int BK, bool WT>
+GGO_DEV void read_one(const Ctx& c, const uint16_t* __restrict__ buf, int g, int r, Frags<BM, BN, BK, WT>& f) {
+    using G = Geo<BM, BN, BK, WT>;
     constexpr int ROW16 = 16 * G::CA * 16;   // bytes of 16 rows of A (or of W^T)
     constexpr int NW = (WT ? 1 : 2) * G::WJ;
     const char* base = reinterpret_cast<const char*>(buf);
@@ -552,9 +552,9 @@ GGO_DEV void read_one(const Ctx& c, const uint16_t* __restrict__ buf, int g, int
 // place among the LDS reads and loads around it, which fixes the interleaving.
 // Each accumulator gets exactly one instruction per group, so the order of q
 // inside a group is free; groups stay in ascending k.
-template <int BN, int BK, bool WT>
-GGO_DEV void mfma_one(const Frags<BN, BK, WT>& f, f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ], int q) {
-    constexpr int WJ = Geo<BN, BK, WT>::WJ;
+template <int BM, int BN, int BK, bool WT>
+GGO_DEV void mfma_one(const Frags<BM, BN, BK, WT>& f, f32x4 (&acc)[Geo<BM, BN, BK>::WI][Geo<BM, BN, BK>::WJ], int q) {
+    constexpr int WJ = Geo<BM, BN, BK, WT>::WJ;
     const int i = q / WJ, j = q % WJ;
     const bf16x8 w = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.wl[j], f.wh[j], 0, 1, 2, 3, 4, 5, 6, 7));
     __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(w), "v"(f.a[i]));
@@ -589,44 +589,50 @@ GGO_DEV void load_l(const Ctx& c, const Panels& pn, int l, int a_loads, lds_t* d
 // (cur, nxt and prv never overlap; saying so lets the compiler keep the loads
 // into one buffer in flight while another is read.) Past the last tile the
 // same steps run on empty ranges: the loads write zeros and touch no memory.
-template <int BN, int BK, int NST, bool WT>
+template <int BM, int BN, int BK, int NST, bool WT>
 GGO_DEV void tile(const Ctx& c, int kt, int par, uint16_t* __restrict__ cur, uint16_t* __restrict__ nxt,
-                  uint16_t* __restrict__ prv, Frags<BN, BK, WT> (&F)[2],
-                  f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ]) {
-    using G = Geo<BN, BK, WT>;
-    constexpr int NG = BK / 32, NQ = G::WI * G::WJ, HALF = NQ / 2, NR = reads_per_group<BN, BK, WT>();
+                  uint16_t* __restrict__ prv, Frags<BM, BN, BK, WT> (&F)[2],
+                  f32x4 (&acc)[Geo<BM, BN, BK>::WI][Geo<BM, BN, BK>::WJ]) {
+    using G = Geo<BM, BN, BK, WT>;
+    constexpr int NG = BK / 32, NQ = G::WI * G::WJ, HALF = NQ / 2, NR = reads_per_group<BM, BN, BK, WT>();
     constexpr int PRE = (NG - 1) * NQ + HALF, POST = NQ - HALF;   // MFMAs before and after the barrier
     constexpr int LA = (G::LOADS + 1) / 2, LB = G::LOADS - LA;     // loads after the barrier, and before the next
     constexpr int SA = POST / LA, SB = PRE / (LB > 0 ? LB : 1);    // MFMAs per load
+    // reads per MFMA inside a tile's groups and after the barrier: one on the larger tiles, more where a
+    // small tile has fewer MFMAs per group than fragment reads
+    constexpr int RG = (NR + NQ - 1) / NQ, RP = (NR + POST - 1) / POST;
     static_assert(NST >= 3, "a second half of loads issued before the next barrier needs a tile of slack");
-    static_assert(NR <= POST && SA >= 1 && SB >= 1, "one read and one load per MFMA at most");
+    static_assert(SA >= 1 && SB >= 1, "one load per MFMA at most");
     {
-        const Panels pp = panels<BN, BK, WT>(c, kt - 1 + NST);
+        const Panels pp = panels<BM, BN, BK, WT>(c, kt - 1 + NST);
 #pragma unroll
         for (int g = 0; g + 1 < NG; ++g) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                mfma_one<BN, BK, WT>(F[(par + g) & 1], acc, q);
-                if (q < NR) read_one<BN, BK, WT>(c, cur, g + 1, q, F[(par + g + 1) & 1]);
+                mfma_one<BM, BN, BK, WT>(F[(par + g) & 1], acc, q);
+#pragma unroll
+                for (int r = q * RG; r < (q + 1) * RG && r < NR; ++r)
+                    read_one<BM, BN, BK, WT>(c, cur, g + 1, r, F[(par + g + 1) & 1]);
                 const int u = g * NQ + q;
-                if (u % SB == 0 && u / SB < LB) load_l(c, pp, LA + u / SB, G::A_LOADS, load_dst<BN, BK, WT>(c, prv, LA + u / SB));
+                if (u % SB == 0 && u / SB < LB) load_l(c, pp, LA + u / SB, G::A_LOADS, load_dst<BM, BN, BK, WT>(c, prv, LA + u / SB));
             }
         }
 #pragma unroll
         for (int q = 0; q < HALF; ++q) {
-            mfma_one<BN, BK, WT>(F[(par + NG - 1) & 1], acc, q);
+            mfma_one<BM, BN, BK, WT>(F[(par + NG - 1) & 1], acc, q);
             const int u = (NG - 1) * NQ + q;
-            if (u % SB == 0 && u / SB < LB) load_l(c, pp, LA + u / SB, G::A_LOADS, load_dst<BN, BK, WT>(c, prv, LA + u / SB));
+            if (u % SB == 0 && u / SB < LB) load_l(c, pp, LA + u / SB, G::A_LOADS, load_dst<BM, BN, BK, WT>(c, prv, LA + u / SB));
         }
     }
-    land<BN, BK, NST, WT>(c, kt + 1, nxt);
-    const Panels pn = panels<BN, BK, WT>(c, kt + NST);
+    land<BM, BN, BK, NST, WT>(c, kt + 1, nxt);
+    const Panels pn = panels<BM, BN, BK, WT>(c, kt + NST);
 #pragma unroll
     for (int q = HALF; q < NQ; ++q) {
-        mfma_one<BN, BK, WT>(F[(par + NG - 1) & 1], acc, q);
+        mfma_one<BM, BN, BK, WT>(F[(par + NG - 1) & 1], acc, q);
         const int u = q - HALF;
-        if (u < NR) read_one<BN, BK, WT>(c, nxt, 0, u, F[(par + NG) & 1]);
-        if (u % SA == 0 && u / SA < LA) load_l(c, pn, u / SA, G::A_LOADS, load_dst<BN, BK, WT>(c, cur, u / SA));
+#pragma unroll
+        for (int r = u * RP; r < (u + 1) * RP && r < NR; ++r) read_one<BM, BN, BK, WT>(c, nxt, 0, r, F[(par + NG) & 1]);
+        if (u % SA == 0 && u / SA < LA) load_l(c, pn, u / SA, G::A_LOADS, load_dst<BM, BN, BK, WT>(c, cur, u / SA));
     }
 }
 
@@ -634,22 +640,22 @@ GGO_DEV void tile(const Ctx& c, int kt, int par, uint16_t* __restrict__ cur, uin
 // parameters: every LDS read and every direct-to-LDS load below then carries
 // alias scopes that tell the buffers apart, so the compiler never has to wait
 // for the loads into one buffer before reading another.
-template <int BN, int BK, int NST, bool WT>
+template <int BM, int BN, int BK, int NST, bool WT>
 GGO_DEV void kloop(const Ctx& c, uint16_t* __restrict__ b0, uint16_t* __restrict__ b1, uint16_t* __restrict__ b2,
-                   uint16_t* __restrict__ b3, f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ]) {
+                   uint16_t* __restrict__ b3, f32x4 (&acc)[Geo<BM, BN, BK>::WI][Geo<BM, BN, BK>::WJ]) {
     uint16_t* const buf[4] = {b0, b1, b2, b3};
 #pragma unroll
-    for (int s = 0; s + 1 < NST; ++s) issue<BN, BK, WT>(c, s, buf[s]);
-    Frags<BN, BK, WT> F[2];
-    land<BN, BK, NST, WT>(c, 0, buf[0]);
+    for (int s = 0; s + 1 < NST; ++s) issue<BM, BN, BK, WT>(c, s, buf[s]);
+    Frags<BM, BN, BK, WT> F[2];
+    land<BM, BN, BK, NST, WT>(c, 0, buf[0]);
     {   // the first half of tile NST-1's loads; tile 0 issues the second half
-        using G = Geo<BN, BK, WT>;
-        const Panels pn = panels<BN, BK, WT>(c, NST - 1);
+        using G = Geo<BM, BN, BK, WT>;
+        const Panels pn = panels<BM, BN, BK, WT>(c, NST - 1);
 #pragma unroll
-        for (int l = 0; l < (G::LOADS + 1) / 2; ++l) load_l(c, pn, l, G::A_LOADS, load_dst<BN, BK, WT>(c, buf[NST - 1], l));
+        for (int l = 0; l < (G::LOADS + 1) / 2; ++l) load_l(c, pn, l, G::A_LOADS, load_dst<BM, BN, BK, WT>(c, buf[NST - 1], l));
     }
 #pragma unroll
-    for (int r = 0; r < reads_per_group<BN, BK, WT>(); ++r) read_one<BN, BK, WT>(c, buf[0], 0, r, F[0]);
+    for (int r = 0; r < reads_per_group<BM, BN, BK, WT>(); ++r) read_one<BM, BN, BK, WT>(c, buf[0], 0, r, F[0]);
     // Full rounds of NST tiles carry no branch between a tile's loads and the
     // next tile's reads (a join there makes the compiler wait for every load
     // in flight); the last nkt % NST tiles follow.
@@ -660,30 +666,30 @@ GGO_DEV void kloop(const Ctx& c, uint16_t* __restrict__ b0, uint16_t* __restrict
     for (; kt + NST <= c.nkt; kt += NST) {
 #pragma unroll
         for (int s = 0; s < NST; ++s)
-            tile<BN, BK, NST, WT>(c, kt + s, (s * NG) & 1, buf[s], buf[(s + 1) % NST], buf[(s + NST - 1) % NST], F, acc);
+            tile<BM, BN, BK, NST, WT>(c, kt + s, (s * NG) & 1, buf[s], buf[(s + 1) % NST], buf[(s + NST - 1) % NST], F, acc);
     }
 #pragma unroll
     for (int s = 0; s + 1 < NST; ++s)
         if (kt + s < c.nkt)
-            tile<BN, BK, NST, WT>(c, kt + s, (s * NG) & 1, buf[s], buf[(s + 1) % NST], buf[(s + NST - 1) % NST], F, acc);
+            tile<BM, BN, BK, NST, WT>(c, kt + s, (s * NG) & 1, buf[s], buf[(s + 1) % NST], buf[(s + NST - 1) % NST], F, acc);
     // The compiler does not see the MFMAs above, so it cannot pad the hazard of
     // a VALU read of their results: wait here, in front of every later use, for
     // longer than the deepest matrix pipeline.
     __asm__ volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" :::);
 #pragma unroll
-    for (int i = 0; i < Geo<BN, BK>::WI; ++i)
+    for (int i = 0; i < Geo<BM, BN, BK>::WI; ++i)
 #pragma unroll
-        for (int j = 0; j < Geo<BN, BK>::WJ; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < Geo<BM, BN, BK>::WJ; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
 }
 
 // Write block rows P * NI .. P * NI + NI - 1 of this wave's accumulators into its LDS region (RS floats
 // per row); lane (lr, lg) holds columns 4 lg .. 4 lg + 3 of row lr of each 16 x 16 block.
-template <int BN, int BK, bool WT, int P, int NI>
-GGO_DEV void stage_rows(const f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ], float* region, int RS, const Ctx& c) {
+template <int BM, int BN, int BK, bool WT, int P, int NI>
+GGO_DEV void stage_rows(const f32x4 (&acc)[Geo<BM, BN, BK>::WI][Geo<BM, BN, BK>::WJ], float* region, int RS, const Ctx& c) {
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-        for (int j = 0; j < Geo<BN, BK, WT>::WJ; ++j) {
+        for (int j = 0; j < Geo<BM, BN, BK, WT>::WJ; ++j) {
             const f32x4 v = acc[P * NI + ii][j];
             *reinterpret_cast<float4*>(region + (ii * 16 + c.lr) * RS + j * 16 + 4 * c.lg) = make_float4(v[0], v[1], v[2], v[3]);
         }
@@ -697,10 +703,10 @@ GGO_DEV void stage_rows(const f32x4 (&acc)[Geo<BN, BK>::WI][Geo<BN, BK>::WJ], fl
 // SIMD), and registers are not worth saving. EPI: the fused epilogue is compiled in (a separate
 // instance: with its code present the compiler moved the accumulators out of their registers before
 // the epilogue test, which at 256 x 256 spilled them on the plain path too).
-template <int BN, int BK, int NST, bool WT, bool EPI>
+template <int BM, int BN, int BK, int NST, bool WT, bool EPI>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_mfma_invariant(const MfmaArgs p) {
-    using G = Geo<BN, BK, WT>;
+    using G = Geo<BM, BN, BK, WT>;
     static_assert(NST >= 2 && NST <= 4, "");
     __shared__ __attribute__((aligned(16))) uint16_t lds_stage0[G::STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_stage1[G::STAGE];
@@ -721,7 +727,7 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
     c.lg = (c.t & 63) >> 4;    // k-octet of the lane
 #pragma unroll
     for (int g = 0; g < BK / 32; ++g) {
-        c.ra[g] = G::a_phys(c.wm * 128 + c.lr, g * 4 + c.lg) * 16;
+        c.ra[g] = G::a_phys(c.wm * (BM / 2) + c.lr, g * 4 + c.lg) * 16;
         if (WT) c.rw[g] = G::A_ELEMS * 2 + G::t_phys(c.wn * (BN / 2) + c.lr, g * 4 + c.lg) * 16;
     }
     if (!WT) {
@@ -764,7 +770,7 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
         for (int j = 0; j < G::WJ; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
     __asm__ volatile("s_nop 4" :::);
 
-    kloop<BN, BK, NST, WT>(c, lds_stage0, lds_stage1, lds_stage2, lds_stage3, acc);
+    kloop<BM, BN, BK, NST, WT>(c, lds_stage0, lds_stage1, lds_stage2, lds_stage3, acc);
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the trailing empty-range loads have landed before the workgroup ends
 
     // lane holds C[row][col .. col+3] of each block: row = lane % 16, col = 4 * (lane / 16)
@@ -784,17 +790,18 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
         const int lane = c.t & 63;
         // The pass loop is not unrolled (its body is large); the accumulators are only ever indexed with
         // constants, through the switch, so they stay in registers.
+        constexpr int NP = (BM / 2) / PR;            // passes: a wave's BM/2 rows, 32 at a time
+        static_assert(NP >= 1 && NP <= 4 && NP * PR == BM / 2, "one to four passes of 32 rows");
 #pragma unroll 1
-        for (int pass = 0; pass < 128 / PR; ++pass) {
-            static_assert(128 / PR == 4, "four passes of 32 rows");
+        for (int pass = 0; pass < NP; ++pass) {
             switch (pass) {
-            case 0: stage_rows<BN, BK, WT, 0, PR / 16>(acc, region, RS, c); break;
-            case 1: stage_rows<BN, BK, WT, 1, PR / 16>(acc, region, RS, c); break;
-            case 2: stage_rows<BN, BK, WT, 2, PR / 16>(acc, region, RS, c); break;
-            default: stage_rows<BN, BK, WT, 3, PR / 16>(acc, region, RS, c); break;
+            case 0: stage_rows<BM, BN, BK, WT, 0, PR / 16>(acc, region, RS, c); break;
+            case 1: if constexpr (NP > 1) stage_rows<BM, BN, BK, WT, 1, PR / 16>(acc, region, RS, c); break;
+            case 2: if constexpr (NP > 2) stage_rows<BM, BN, BK, WT, 2, PR / 16>(acc, region, RS, c); break;
+            default: if constexpr (NP > 3) stage_rows<BM, BN, BK, WT, 3, PR / 16>(acc, region, RS, c); break;
             }
             __syncthreads();
-            const int row0 = c.m0 + c.wm * 128 + pass * PR, col0 = c.n0 + c.wn * (BN / 2);
+            const int row0 = c.m0 + c.wm * (BM / 2) + pass * PR, col0 = c.n0 + c.wn * (BN / 2);
             if ((p.vec & VEC_EP) && row0 + PR <= p.M && col0 + BN / 2 <= p.N) {
                 // Whole pass in range: every bias / residual load of the pass goes out first, so the
                 // pass waits for memory once instead of once per 4 results.
@@ -839,7 +846,7 @@ void k_gemm_mfma_invariant(const MfmaArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < G::WI; ++i) {
-        const int row = c.m0 + c.wm * 128 + i * 16 + c.lr;
+        const int row = c.m0 + c.wm * (BM / 2) + i * 16 + c.lr;
         if (row >= p.M) continue;
         float* crow = static_cast<float*>(p.C) + static_cast<int64_t>(row) * p.ldc;
 #pragma unroll
@@ -862,36 +869,50 @@ constexpr int BN_MAIN = 128, BK_MAIN = 64, NST_MAIN = 3;
 // 32-k tiles four deep (128 KiB of LDS). Per k it reads a third less of A and W per product than 256 x 128;
 // with fewer tiles it fills the chip only on large weights.
 constexpr int BN_LARGE = 256, BK_LARGE = 32, NST_LARGE = 4;
+// The same pipeline on smaller tiles, for weights whose tiles would leave most CUs idle at small M: 128 x 128
+// and 64 x 128 (BK = 64, three stages; 96 and 72 KiB of LDS). Each wave then owns 64 or 32 rows, and a
+// group's fragment reads outnumber its MFMAs, so the reads go out several per MFMA.
+constexpr int BM_MID = 128, BM_SMALL = 64, BN_NARROW = 128, BK_NARROW = 64, NST_NARROW = 3;
 
 }  // namespace t256
 }  // namespace
 
-void mfma_tile_shape(int* bm, int* bn) { *bm = t256::BM; *bn = t256::BN_MAIN; }
-void mfma_tile_shape_t256x256(int* bm, int* bn) { *bm = t256::BM; *bn = t256::BN_LARGE; }
+void mfma_tile_shape(int* bm, int* bn) { *bm = t256::BM_MAIN; *bn = t256::BN_MAIN; }
+void mfma_tile_shape_t256x256(int* bm, int* bn) { *bm = t256::BM_MAIN; *bn = t256::BN_LARGE; }
 void mfma_tile_shape_t128(int* bm, int* bn) { *bm = 128; *bn = 128; }
+void mfma_tile_shape_lds128(int* bm, int* bn) { *bm = t256::BM_MID; *bn = t256::BN_NARROW; }
+void mfma_tile_shape_lds64x128(int* bm, int* bn) { *bm = t256::BM_SMALL; *bn = t256::BN_NARROW; }
 void mfma_tile_shape_t64(int* bm, int* bn) { *bm = 64; *bn = 64; }
 
-template <int BN, int BK, int NST>
+template <int BM, int BN, int BK, int NST>
 static hipError_t launch_t256(const MfmaArgs& a, hipStream_t stream) {
     if (epi_identity(a.ep))
-        hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<BN, BK, NST, false, false>), dim3(a.tiles_m * a.tiles_n),
+        hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<BM, BN, BK, NST, false, false>), dim3(a.tiles_m * a.tiles_n),
                            dim3(t256::THREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<BN, BK, NST, false, true>), dim3(a.tiles_m * a.tiles_n),
+        hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<BM, BN, BK, NST, false, true>), dim3(a.tiles_m * a.tiles_n),
                            dim3(t256::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_mfma_invariant(const MfmaArgs& a, hipStream_t stream) {
-    return launch_t256<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN>(a, stream);
+    return launch_t256<t256::BM_MAIN, t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN>(a, stream);
 }
 
 hipError_t launch_gemm_mfma_invariant_256(const MfmaArgs& a, hipStream_t stream) {
-    return launch_t256<t256::BN_LARGE, t256::BK_LARGE, t256::NST_LARGE>(a, stream);
+    return launch_t256<t256::BM_MAIN, t256::BN_LARGE, t256::BK_LARGE, t256::NST_LARGE>(a, stream);
+}
+
+hipError_t launch_gemm_mfma_lds128(const MfmaArgs& a, hipStream_t stream) {
+    return launch_t256<t256::BM_MID, t256::BN_NARROW, t256::BK_NARROW, t256::NST_NARROW>(a, stream);
+}
+
+hipError_t launch_gemm_mfma_lds64x128(const MfmaArgs& a, hipStream_t stream) {
+    return launch_t256<t256::BM_SMALL, t256::BN_NARROW, t256::BK_NARROW, t256::NST_NARROW>(a, stream);
 }
 
 hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream) {   // no epilogue on this entry
-    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, true, false>),
+    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BM_MAIN, t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, true, false>),
                        dim3(a.tiles_m * a.tiles_n), dim3(t256::THREADS), 0, stream, a);
     return hipGetLastError();
 }

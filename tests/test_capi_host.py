@@ -170,12 +170,12 @@ def test_gemv_instance_hook_rejects_what_it_cannot_run(g):
 
 
 def test_mfma_tile_hook_rejects_what_it_cannot_run(g):
-    """ggo_test_gemm_mfma_tile: an unknown tile is refused, and the two wide tiles (256x128, 256x256) refuse
+    """ggo_test_gemm_mfma_tile: an unknown tile is refused, and the four direct-to-LDS tiles refuse
     operands they cannot load, all before any GPU call (fake addresses are never touched)."""
     lib, null = g.lib, None
-    for tile in (-1, 4):
+    for tile in (-1, 6):
         assert lib.ggo_test_gemm_mfma_tile(tile, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1
-    for tile in (0, 3):
+    for tile in (0, 3, 4, 5):
         assert lib.ggo_test_gemm_mfma_tile(tile, 16, 12, 16, 8, 16, 8, 4, 8, 12, null) == -2   # K = 12
         assert lib.ggo_test_gemm_mfma_tile(tile, 18, 8, 16, 8, 16, 8, 4, 8, 8, null) == -2     # A misaligned
     # empty problems launch nothing, whatever the tile

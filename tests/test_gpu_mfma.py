@@ -102,15 +102,15 @@ def test_7b_projection_sampled(g, n):
     assert np.array_equal(sub, full[1000:1128])
 
 
-TILES = ("256x128", "256x256", "128x128", "64x64")
-WIDE = ("256x128", "256x256")   # need K and N multiples of 8 (and aligned operands)
+TILES = ("256x128", "256x256", "128x128_lds", "64x128_lds", "128x128", "64x64")
+WIDE = ("256x128", "256x256", "128x128_lds", "64x128_lds")   # need K and N multiples of 8 (and aligned operands)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 64), (300, 200, 100), (513, 1000, 1111), (1, 4096, 4096),
                                    (2048, 4096, 1024), (4096, 4096, 4096), (4096, 11008, 4096), (7, 33, 31),
                                    (513, 1000, 1112), (300, 200, 104), (257, 136, 1000), (1, 8, 8), (255, 1032, 72)])
 def test_tile_instances_agree_bitwise(g, M, N, K):
-    """The 256x128, 256x256, 128x128 and 64x64 tile instances feed every output the same operand values in the
+    """The six tile instances (four direct-to-LDS, two register-staged) feed every output the same operand values in the
     same 32-k groups ("Taming Bitwise Behavior in GPU Kernels with Tensor Core", section 3.2.2: block
     sizes do not enter the order), so their outputs, and the entry point's, must be identical bit for bit."""
     say(f"mfma tile instances M={M} N={N} K={K}")
