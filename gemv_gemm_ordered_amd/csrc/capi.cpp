@@ -336,7 +336,8 @@ int ggo_test_gemm_ordered_tile(int tile, const void* A, int a_dtype, int64_t lda
 
 // gemv_ordered (wt = 0, W [K, N]) and gemv_ordered_wt (wt = 1, W^T [N, K]); form as in GemvArgs.
 static int run_gemv_ordered(const char* fn, int wt, const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw,
-                            float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s, int form) {
+                            float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s, int form,
+                            int rows = 0) {
     int rc = check_mnk(fn, M, N, K);
     if (rc) return rc;
     if (M > GGO_GEMV_MAX_M) return fail(GGO_EUNSUPPORTED, "%s: M=%lld exceeds %d (gemm_ordered gives the same bits)", fn, (long long)M, GGO_GEMV_MAX_M);
@@ -356,6 +357,7 @@ static int run_gemv_ordered(const char* fn, int wt, const uint16_t* x, int64_t l
     a.K = (int32_t)K;
     a.wt = wt;
     a.form = form;
+    a.rows = rows;
     if (wt) {
         // 8-byte loads of 4 k from rows of x and W^T: no load may straddle the end of a row
         if (!aligned(x, 8) || ldx % 4 || !aligned(W, 8) || ldw % 4 || K % 4)
@@ -379,6 +381,9 @@ static int run_gemv_ordered(const char* fn, int wt, const uint16_t* x, int64_t l
     if (form == 2 && !gemv_ordered_k128_ok(a))
         return fail(GGO_EUNSUPPORTED, "%s: the 128-k instance needs 4-byte column pairs of W (or W^T) and ldw "
                     "small enough for its stage ranges", fn);
+    if (form == 4 && !gemv_ordered_mr_ok(a))
+        return fail(GGO_EUNSUPPORTED, "%s: the MR-row instance serves W^T with 16-byte aligned x and W^T and row "
+                    "strides and K multiples of 8", fn);
     if (form == 3 && !gemv_ordered_m1_ok(a))
         return fail(GGO_EUNSUPPORTED, "%s: the 512-k instance serves M = 1 with W^T, 16-byte aligned x and W^T and "
                     "row strides and K multiples of 8", fn);
@@ -569,16 +574,18 @@ int ggo_test_gemv_instance(int kind, int rows, int form, const uint16_t* x, int6
     if (tiered && !(rows == 1 || rows == 2 || rows == 4 || rows == 8 || rows == 16))
         return fail(GGO_EINVAL, "%s: rows must be 1, 2, 4, 8 or 16", fn);
     if (tiered && rows < M) return fail(GGO_EUNSUPPORTED, "%s: an instance staging %d rows cannot serve M=%lld", fn, rows, (long long)M);
-    if (!tiered && rows != 0) return fail(GGO_EINVAL, "%s: rows must be 0 for the ordered GEMV", fn);
     if (kind == GGO_TEST_GEMV_MFMA ? form != 0
         : kind == GGO_TEST_GEMV_TREE ? (form != 1 && form != 2)
         : kind == GGO_TEST_GEMV_ORDERED ? (form != 1 && form != 2)
-                                        : (form < 1 || form > 3))
+                                        : (form < 1 || form > 4))
         return fail(GGO_EINVAL, "%s: form %d is not an instance of kind %d", fn, form, kind);
+    // the ordered GEMV stages rows only in its MR-row instance (form 4): 2, 4 or 8 rows per workgroup, any M
+    if (!tiered && form == 4 ? !(rows == 0 || rows == 2 || rows == 4 || rows == 8) : (!tiered && rows != 0))
+        return fail(GGO_EINVAL, "%s: rows must be 0 for the ordered GEMV (or 0, 2, 4 or 8 for form 4)", fn);
     switch (kind) {
     case GGO_TEST_GEMV_TREE: return run_tree(fn, x, ldx, W, ldw, y, ldy, M, N, K, s, no_epi(), rows, form);
     case GGO_TEST_GEMV_ORDERED: return run_gemv_ordered(fn, 0, x, ldx, W, ldw, y, ldy, M, N, K, s, form);
-    case GGO_TEST_GEMV_ORDERED_WT: return run_gemv_ordered(fn, 1, x, ldx, W, ldw, y, ldy, M, N, K, s, form);
+    case GGO_TEST_GEMV_ORDERED_WT: return run_gemv_ordered(fn, 1, x, ldx, W, ldw, y, ldy, M, N, K, s, form, rows);
     default: return run_gemv_mfma(fn, x, ldx, W, ldw, y, ldy, M, N, K, s, no_epi(), rows);
     }
 }

@@ -47,12 +47,15 @@ struct GemvArgs {
     int32_t M, N, K;
     uint32_t vec;
     int32_t wt;
-    int32_t form;     // 0: chosen from M (512-k stages for M = 1 on W^T where allowed, 64-k stages for M <= 4,
-                      // else 128-k where allowed); 1: 64-k; 2: 128-k; 3: 512-k (M = 1, W^T)
+    int32_t form;     // 0: chosen from M (on W^T where allowed: 512-k stages at M = 1, the MR-row instance at
+                      // M >= 2; else 64-k stages for M <= 4, else 128-k where allowed); 1: 64-k; 2: 128-k;
+                      // 3: 512-k (M = 1, W^T); 4: MR rows of x per workgroup (W^T)
+    int32_t rows;     // form 4: rows of x per workgroup (2, 4 or 8), or 0 for M rounded up
 };
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream);
 bool gemv_ordered_k128_ok(const GemvArgs& a);   // the 128-k stages can serve these operands
 bool gemv_ordered_m1_ok(const GemvArgs& a);     // the 512-k stages (M = 1, W^T) can serve these operands
+bool gemv_ordered_mr_ok(const GemvArgs& a);     // the MR-row instance (W^T) can serve these operands
 int gemv_ordered_max_ldw();   // buffer offsets of the GEMV kernel are 32-bit
 int gemv_ordered_wt_max_ldw();   // the same for W^T: a 16-row slab of W^T in one 32-bit range
 

@@ -661,11 +661,169 @@ __global__ __launch_bounds__(THREADS1) void k_gemv_ordered_m1(const GemvArgs a) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Two to eight rows of x, weight as W^T (16-byte operands): the structure of k_gemv_ordered_m1 for MR
+// rows. One consumer wave: lane m NSC + c folds y[m0 + m, n0 + c] (MR NSC <= 64 chains). Two producer
+// waves stream the workgroup's NSC weight rows, SL k per stage: a load instruction covers 64 / LPR rows,
+// LPR = SL / 8 lanes per row (lane l: row l / LPR of the load, k = 8 (l mod LPR) .. + 7 of the stage),
+// and each lane forms the MR products of each of its weight elements with the same 8 k of every row of x.
+// A stage holds MR NSC SL products. Products, their places in the chain and the adds are those of
+// k_gemv_ordered, so the bits are too.
+template <int MR, int NSC, int SL, int P_>
+struct MrGeo {
+    static constexpr int P = P_, CH = MR * NSC;            // producer waves, chains
+    static constexpr int LPR = SL / 8, RPL = 64 / LPR;     // lanes per weight row, rows per load instruction
+    static constexpr int RW = NSC / P, WL = RW / RPL;      // weight rows per producer wave, loads per stage
+    static constexpr int NQ = SL / 4;                      // 16-byte product chunks per chain and stage
+    static constexpr int SWZ = (NQ < 16 ? NQ : 16) - 1;    // chunk XOR: 16 consecutive chains on distinct banks
+    static constexpr int NBUF = 2, DEPTH = 3, THREADS = 64 * (1 + P);
+    static_assert(CH <= 64 && RW % RPL == 0 && WL >= 1 && NQ % 16 == 0, "MrGeo");
+};
+constexpr int OFF_PAST_MR = 0x7ffffff0;   // a buffer offset past every range used here: the load returns 0
+
+template <class G>
+GGO_DEV int slot_mr(int ch, int k4) { return ch * (G::NQ * 4) + ((k4 ^ (ch & G::SWZ)) << 2); }
+
+template <int MR, int NSC, int SL, int P>
+__global__ __launch_bounds__(64 * (1 + P)) void k_gemv_ordered_mr(const GemvArgs a) {
+    using G = MrGeo<MR, NSC, SL, P>;
+    __shared__ __attribute__((aligned(16))) float ps[G::NBUF][G::CH * SL];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n0 = xcd_contiguous(blockIdx.x, gridDim.x) * NSC, m0 = blockIdx.y * MR;
+    const int nst = (a.K + SL - 1) / SL;
+    // Iteration s (one barrier each): the producers form stage s, the consumer folds stage s - 1; the
+    // count is padded to whole rounds of DEPTH stages, as in k_gemv_ordered_m1 (no exit or skip inside the
+    // producers' loop; stages past the last are formed from zeros into the buffer no one reads next).
+    const int iters = (nst + G::DEPTH) / G::DEPTH * G::DEPTH;
+    if (wave > 0) {
+        const int q = wave - 1, kq = lane % G::LPR, rl = lane / G::LPR;
+        // one range for the workgroup's weight rows and one for its rows of x; a lane past K or past the
+        // last row gets an offset past the range (K is a multiple of 8: a lane's 8 k are all in or all out)
+        const int wrows = a.N - n0 < NSC ? a.N - n0 : NSC, xrows = a.M - m0 < MR ? a.M - m0 : MR;
+        const auto wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.W) + static_cast<int64_t>(n0) * a.ldw,
+                                                          0, ((wrows - 1) * static_cast<int>(a.ldw) + a.K) * 2, BUF_DWORD3);
+        const auto xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x) + static_cast<int64_t>(m0) * a.ldx,
+                                                          0, ((xrows - 1) * static_cast<int>(a.ldx) + a.K) * 2, BUF_DWORD3);
+        struct Fetch {
+            uint4 w[G::WL];   // k = 8 kq .. 8 kq + 7 of the stage, weight rows q RW + i RPL + rl
+            uint4 x[MR];      // the same 8 k of each row of x
+        };
+        auto fetch = [&](int stage, Fetch& f) {
+            const int k = stage * SL + 8 * kq;
+#pragma unroll
+            for (int i = 0; i < G::WL; ++i) {
+                const int r = q * G::RW + i * G::RPL + rl;
+                const int off = (k < a.K && r < wrows) ? (r * static_cast<int>(a.ldw) + k) * 2 : OFF_PAST_MR;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+                f.w[i] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const int off = (k < a.K && m < xrows) ? (m * static_cast<int>(a.ldx) + k) * 2 : OFF_PAST_MR;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+                f.x[m] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        };
+        Fetch f[G::DEPTH];
+#pragma unroll
+        for (int d = 0; d < G::DEPTH; ++d) {
+            fetch(d, f[d]);
+            __builtin_amdgcn_sched_barrier(0);   // issued stage by stage, so stage 0's loads are the oldest
+        }
+        for (int s0 = 0; s0 < iters; s0 += G::DEPTH) {
+#pragma unroll
+            for (int d = 0; d < G::DEPTH; ++d) {
+                const int s = s0 + d;
+                float* buf = ps[s % G::NBUF];
+                float xv[MR][8];
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const uint4 x = f[d].x[m];
+                    xv[m][0] = bf16_lo(x.x); xv[m][1] = bf16_hi(x.x); xv[m][2] = bf16_lo(x.y); xv[m][3] = bf16_hi(x.y);
+                    xv[m][4] = bf16_lo(x.z); xv[m][5] = bf16_hi(x.z); xv[m][6] = bf16_lo(x.w); xv[m][7] = bf16_hi(x.w);
+                }
+#pragma unroll
+                for (int i = 0; i < G::WL; ++i) {
+                    const uint4 w = f[d].w[i];
+                    const float wv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                         bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+                    const int r = q * G::RW + i * G::RPL + rl;
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        const int ch = m * NSC + r;
+                        *reinterpret_cast<float4*>(buf + slot_mr<G>(ch, 2 * kq)) =
+                            make_float4(xv[m][0] * wv[0], xv[m][1] * wv[1], xv[m][2] * wv[2], xv[m][3] * wv[3]);
+                        *reinterpret_cast<float4*>(buf + slot_mr<G>(ch, 2 * kq + 1)) =
+                            make_float4(xv[m][4] * wv[4], xv[m][5] * wv[5], xv[m][6] * wv[6], xv[m][7] * wv[7]);
+                    }
+                }
+                fetch(s + G::DEPTH, f[d]);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);   // each stage's conversions after its own barrier
+            }
+        }
+    } else {
+        float acc = 0.0f;   // +0.0: the chain's start
+        const int ch = lane, m = lane / NSC, c = lane % NSC;
+        float* const y = a.y;
+        asm volatile("" ::"s"(y));   // the output pointer's scalar load completes before the loop
+        constexpr int GR = 16, NGR = G::NQ / GR;   // reads of the next 64 k before the adds of the current 64
+        for (int s = 0; s < iters; ++s) {
+            if (s >= 1 && s <= nst && ch < G::CH) {   // stage s - 1, formed in the previous iteration
+                const float* src = ps[(s - 1) % G::NBUF];
+                float4 cb[2][GR];
+#pragma unroll
+                for (int j = 0; j < GR; ++j) cb[0][j] = *reinterpret_cast<const float4*>(src + slot_mr<G>(ch, j));
+#pragma unroll
+                for (int gi = 0; gi < NGR; ++gi) {
+                    if (gi + 1 < NGR) {
+#pragma unroll
+                        for (int j = 0; j < GR; ++j)
+                            cb[(gi + 1) & 1][j] = *reinterpret_cast<const float4*>(src + slot_mr<G>(ch, (gi + 1) * GR + j));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < GR; ++j) {   // ascending k
+                        const float4 v = cb[gi & 1][j];
+                        acc = acc + v.x;
+                        acc = acc + v.y;
+                        acc = acc + v.z;
+                        acc = acc + v.w;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __syncthreads();
+        }
+        if (ch < G::CH && m0 + m < a.M && n0 + c < a.N) y[static_cast<int64_t>(m0 + m) * a.ldy + n0 + c] = acc;
+    }
+}
+
+template <int MR, int NSC, int SL, int P>
+hipError_t launch_mr(const GemvArgs& a, hipStream_t stream) {
+    using G = MrGeo<MR, NSC, SL, P>;
+    hipLaunchKernelGGL((k_gemv_ordered_mr<MR, NSC, SL, P>), dim3((a.N + NSC - 1) / NSC, (a.M + MR - 1) / MR),
+                       dim3(G::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+// rows of x per workgroup for the MR instance: M rounded up to 2, 4 or 8, and 8-row groups above 8 rows
+// (two workgroups per CU; the 4-row shape's 64 KiB stages hold one, and at M = 12 / 16 its row groups ran
+// in rounds: 53.7 / 71.0 us against 54.7 / 55.2), or the caller's forced value
+int mr_rows(const GemvArgs& a) { return a.rows ? a.rows : a.M <= 2 ? 2 : a.M <= 4 ? 4 : 8; }
+
 }  // namespace
 
 // M = 1, W^T, 16-byte loads that never straddle the end of a row, byte offsets within 32 bits
 bool gemv_ordered_m1_ok(const GemvArgs& a) {
     return a.wt && a.M == 1 && (a.vec & VEC_W16) && a.K <= (1 << 29) - 4 * DEPTH1 * SL1;
+}
+
+// 2 <= M (per workgroup: 2, 4 or 8 rows), W^T, 16-byte loads; a 16-row slab of W^T and 8 rows of x in
+// 32-bit byte offsets below the past-the-end offset
+bool gemv_ordered_mr_ok(const GemvArgs& a) {
+    return a.wt && (a.vec & VEC_W16) && a.ldw <= (OFF_PAST_MR / 2 - a.K) / 16 && a.ldx <= (OFF_PAST_MR / 2 - a.K) / 8;
 }
 
 bool gemv_ordered_k128_ok(const GemvArgs& a) {
@@ -677,9 +835,18 @@ hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
     // M > 4 with operands it can take: the 128-k form (same bits; see k_gemv_ordered_k128); form 1 or 2
     // forces the 64-k or the 128-k form (the caller has checked that the latter can serve)
     const bool k128 = a.form == 2 || (a.form == 0 && a.M > 4 && gemv_ordered_k128_ok(a));
-    if (a.form == 3 || (a.form == 0 && a.M == 1 && gemv_ordered_m1_ok(a)))
+    if (a.form == 3 || (a.form == 0 && a.M == 1 && gemv_ordered_m1_ok(a))) {
         hipLaunchKernelGGL(k_gemv_ordered_m1, dim3((a.N + NS1 - 1) / NS1), dim3(THREADS1), 0, stream, a);
-    else if (k128 && a.wt)
+    } else if (a.form == 4 || (a.form == 0 && a.M >= 2 && gemv_ordered_mr_ok(a))) {
+        // rows x columns x k per stage, producer waves: 2 x 16 x 512 and 4 x 16 x 256 (64 KiB stages, one
+        // workgroup per CU), 8 x 8 x 128 with two workgroups per CU (32 KiB stages). Measured on 4096 x 4096
+        // against these: 256-k stages at two rows (18.9 against 17.1 us), 128-k stages or two producer waves
+        // at four rows (21.6 / 20.5 against 19.5), 256-k stages at eight rows (37-42 against 27.9: one
+        // workgroup per CU, two rounds of the 512 workgroups)
+        const int mr = mr_rows(a);
+        return mr == 2 ? launch_mr<2, 16, 512, 2>(a, stream) : mr == 4 ? launch_mr<4, 16, 256, 4>(a, stream)
+                                                                       : launch_mr<8, 8, 128, 2>(a, stream);
+    } else if (k128 && a.wt)
         hipLaunchKernelGGL((k_gemv_ordered_k128<true>), grid, dim3(THREADS), 0, stream, a);
     else if (k128)
         hipLaunchKernelGGL((k_gemv_ordered_k128<false>), grid, dim3(THREADS), 0, stream, a);

@@ -26,7 +26,8 @@
  *    (gemv_ordered, gemv_ordered_wt, gemv_tree, gemv_mfma_invariant) do
  *    choose, from M, an instance of their kernel: how many rows of x a
  *    workgroup stages (M rounded up to 1, 2, 4, 8 or 16), and for the ordered
- *    GEMV 64-, 128- or (M = 1, W^T) 512-k stages. Every instance gives every output the same
+ *    GEMV 64- or 128-k stages, or on W^T 512-k stages (M = 1) or 2, 4 or 8
+ *    rows of x per workgroup. Every instance gives every output the same
  *    chains, order and tree, hence the same bits; ggo_test_gemv_instance runs
  *    any instance at any M so that this is tested, not assumed.
  *  - Return value: GGO_OK (0), or a negative error code; the calling thread's
@@ -388,10 +389,15 @@ int ggo_test_gemm_ordered_tile(int tile, const void *A, int a_dtype, int64_t lda
  *         GGO_TEST_GEMV_ORDERED_WT  gemv_ordered_wt(x, W^T): as above, and
  *                                   form 3 = 512-k stages (M = 1, 16-byte
  *                                   aligned x and W^T, row strides and K
- *                                   multiples of 8)
+ *                                   multiples of 8); form 4 = 2, 4 or 8
+ *                                   rows of x per workgroup (rows 2, 4 or
+ *                                   8, or 0 for the entry point's choice;
+ *                                   any M; the same operands as form 3)
  *         GGO_TEST_GEMV_MFMA        gemv_mfma_invariant(x, W^T): rows in
  *                                   {1,2,4,8,16}; form 0
- *   rows  rows of x the instance stages per workgroup; must be >= M
+ *   rows  rows of x the instance stages per workgroup; must be >= M for the
+ *         tree and matrix-core kinds; 0 for the ordered kinds except form 4,
+ *         where it may be below M (several row groups)
  *   The remaining arguments, their rules and errors are those of the entry
  *   point named by kind (W is W^T [N, K] where that entry point takes W^T).
  *   GGO_EUNSUPPORTED when the chosen instance cannot serve the operands.

@@ -164,7 +164,13 @@ def test_gemv_instance_hook_rejects_what_it_cannot_run(g):
     assert lib.ggo_test_gemv_instance(1, 0, 3, 16, 8, 16, 8, 16, 8, 1, 8, 8, null) == -1
     assert lib.ggo_test_gemv_instance(2, 0, 3, 16, 8, 16, 8, 16, 8, 2, 8, 8, null) == -2
     assert lib.ggo_test_gemv_instance(2, 0, 3, 8, 8, 16, 8, 16, 8, 1, 8, 8, null) == -2
-    assert lib.ggo_test_gemv_instance(2, 0, 4, 16, 8, 16, 8, 16, 8, 1, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(2, 0, 5, 16, 8, 16, 8, 16, 8, 1, 8, 8, null) == -1
+    # the MR-row ordered instance: W^T form only (form 4 of kind 2), rows 0, 2, 4 or 8, 16-byte operands
+    assert lib.ggo_test_gemv_instance(1, 0, 4, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(2, 3, 4, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(2, 16, 4, 16, 8, 16, 8, 16, 8, 4, 8, 8, null) == -1
+    assert lib.ggo_test_gemv_instance(2, 4, 4, 8, 8, 16, 8, 16, 8, 4, 8, 8, null) == -2   # x 8-byte aligned only
+    assert lib.ggo_test_gemv_instance(2, 4, 4, 16, 12, 16, 12, 16, 8, 4, 8, 12, null) == -2   # K = 12
     # empty problems launch nothing
     assert lib.ggo_test_gemv_instance(0, 1, 2, null, 8, null, 8, null, 8, 0, 8, 8, null) == 0
 

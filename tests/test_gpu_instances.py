@@ -53,14 +53,20 @@ def test_tree_instances_at_the_decode_shape(g, decode, M):
         assert np.array_equal(got, entry), (M, rows, form)
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 16])
 def test_ordered_instances_at_the_decode_shape(g, decode, M):
     ref = decode["ordered"][:M]
+    entry = host_bits(g.gemv_ordered_wt(decode["dx"][:M], decode["dWT"]))
+    assert np.array_equal(entry, ref), M
     for kind, W in (("ordered", decode["dW"]), ("ordered_wt", decode["dWT"])):
         for form in (1, 2, 3) if kind == "ordered_wt" and M == 1 else (1, 2):
             say(f"gemv {kind} instance form={form} M={M}")
             got = host_bits(g.test_gemv_instance(kind, 0, form, decode["dx"][:M], W))
             assert np.array_equal(got, ref), (kind, M, form)
+    for rows in (0, 2, 4, 8):   # the MR-row instance (W^T): any rows per workgroup at any M
+        say(f"gemv ordered_wt instance form=4 rows={rows} M={M}")
+        got = host_bits(g.test_gemv_instance("ordered_wt", rows, 4, decode["dx"][:M], decode["dWT"]))
+        assert np.array_equal(got, ref), ("mr", M, rows)
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 7, 16])
@@ -95,6 +101,9 @@ def test_instances_on_ragged_shapes(g, M, N, K):
             assert np.array_equal(host_bits(g.test_gemv_instance("ordered_wt", 0, form, dx, dWT)), ref_o), form
     if M == 1 and K % 8 == 0:   # the 512-k stages of the W^T form
         assert np.array_equal(host_bits(g.test_gemv_instance("ordered_wt", 0, 3, dx, dWT)), ref_o)
+    if K % 8 == 0:   # the MR-row instance of the W^T form
+        for rows in (2, 4, 8):
+            assert np.array_equal(host_bits(g.test_gemv_instance("ordered_wt", rows, 4, dx, dWT)), ref_o), rows
     if K % 8 == 0:
         ref_m = f32_bits(oracle.gemm_mfma(x, W))
         for rows in TIERS:
