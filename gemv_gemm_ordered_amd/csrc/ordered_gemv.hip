@@ -832,9 +832,11 @@ bool gemv_ordered_k128_ok(const GemvArgs& a) {
 
 hipError_t launch_gemv_ordered(const GemvArgs& a, hipStream_t stream) {
     const dim3 grid((a.N + NS - 1) / NS, (a.M + RG - 1) / RG);
-    // M > 4 with operands it can take: the 128-k form (same bits; see k_gemv_ordered_k128); form 1 or 2
-    // forces the 64-k or the 128-k form (the caller has checked that the latter can serve)
-    const bool k128 = a.form == 2 || (a.form == 0 && a.M > 4 && gemv_ordered_k128_ok(a));
+    // With operands it can take, the 128-k form (same bits; see k_gemv_ordered_k128) from M = 2 on W [K, N]
+    // (4096 x 4096: 20.5 / 22.5 us at M = 2 / 4 against 21.5 / 28.3 with 64-k stages; level at M = 1) and
+    // above M = 4 on W^T where the MR-row instance cannot serve; form 1 or 2 forces the 64-k or the 128-k
+    // form (the caller has checked that the latter can serve)
+    const bool k128 = a.form == 2 || (a.form == 0 && a.M > (a.wt ? 4 : 1) && gemv_ordered_k128_ok(a));
     if (a.form == 3 || (a.form == 0 && a.M == 1 && gemv_ordered_m1_ok(a))) {
         hipLaunchKernelGGL(k_gemv_ordered_m1, dim3((a.N + NS1 - 1) / NS1), dim3(THREADS1), 0, stream, a);
     } else if (a.form == 4 || (a.form == 0 && a.M >= 2 && gemv_ordered_mr_ok(a))) {

@@ -63,6 +63,7 @@ def test_ordered_instances_at_the_decode_shape(g, decode, M):
             say(f"gemv {kind} instance form={form} M={M}")
             got = host_bits(g.test_gemv_instance(kind, 0, form, decode["dx"][:M], W))
             assert np.array_equal(got, ref), (kind, M, form)
+    assert np.array_equal(host_bits(g.gemv_ordered(decode["dx"][:M], decode["dW"])), ref), M
     for rows in (0, 2, 4, 8):   # the MR-row instance (W^T): any rows per workgroup at any M
         say(f"gemv ordered_wt instance form=4 rows={rows} M={M}")
         got = host_bits(g.test_gemv_instance("ordered_wt", rows, 4, decode["dx"][:M], decode["dWT"]))
@@ -83,7 +84,8 @@ def test_mfma_gemv_instances_at_the_decode_shape(g, decode, M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 37, 200), (3, 100, 2056), (5, 33, 4096), (2, 300, 1000), (6, 17, 4104),
-                                   (8, 129, 776), (1, 100, 4104), (1, 1000, 1536), (1, 17, 8)])
+                                   (8, 129, 776), (1, 100, 4104), (1, 1000, 1536), (1, 17, 8), (3, 104, 1001),
+                                   (7, 520, 777), (1, 8, 3), (16, 136, 600)])
 def test_instances_on_ragged_shapes(g, M, N, K):
     x = synth.normal_bf16(M + N + K, "inst.x", (M, K))
     W = synth.normal_bf16(M + N + K, "inst.W", (K, N), 0.02)
