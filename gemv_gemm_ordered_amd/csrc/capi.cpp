@@ -213,6 +213,22 @@ enum {
 constexpr int64_t MFMA_SMALL_WEIGHT = int64_t(1) << 20, MFMA_LARGE_WEIGHT = int64_t(1) << 24;
 constexpr int64_t MFMA_SHORT_K = 1024;
 
+// The direct-to-LDS tile of a weight N x K (operands that allow its loads), by the rule above
+static int mfma_wide_tile(int64_t N, int64_t K) {
+    return N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x128_LDS
+         : N * K >= MFMA_LARGE_WEIGHT ? MFMA_TILE_256x256
+         : K <= MFMA_SHORT_K          ? MFMA_TILE_128x128_LDS
+                                      : MFMA_TILE_256x128;
+}
+
+// Its shape
+static void mfma_wide_shape(int tile, int* bm, int* bn) {
+    if (tile == MFMA_TILE_256x256) mfma_tile_shape_t256x256(bm, bn);
+    else if (tile == MFMA_TILE_128x128_LDS) mfma_tile_shape_lds128(bm, bn);
+    else if (tile == MFMA_TILE_64x128_LDS) mfma_tile_shape_lds64x128(bm, bn);
+    else mfma_tile_shape(bm, bn);
+}
+
 int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, void* C, int64_t ldc,
              int64_t M, int64_t N, int64_t K, hipStream_t s, int force, const Epi& ep) {
     int rc = check_mnk(fn, M, N, K);
@@ -226,9 +242,7 @@ int run_mfma(const char* fn, const uint16_t* A, int64_t lda, const uint16_t* W, 
     // the tile follows the weight (and what the operands allow), never M
     const int tile = force >= 0 ? force
                    : !wide_ok ? (N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x64 : MFMA_TILE_128x128)
-                   : N * K <= MFMA_SMALL_WEIGHT ? MFMA_TILE_64x128_LDS
-                   : N * K >= MFMA_LARGE_WEIGHT ? MFMA_TILE_256x256
-                   : K <= MFMA_SHORT_K ? MFMA_TILE_128x128_LDS : MFMA_TILE_256x128;
+                   : mfma_wide_tile(N, K);
     static const char* const names[] = {"256x128", "128x128", "64x64", "256x256", "128x128 direct-to-LDS",
                                         "64x128 direct-to-LDS"};
     const bool needs_wide = tile == MFMA_TILE_256x128 || tile == MFMA_TILE_256x256 || tile == MFMA_TILE_128x128_LDS ||
@@ -477,7 +491,7 @@ int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, i
                     "%s: A and W^T must be 16-byte aligned with row strides that are multiples of 8 and below 2^22, "
                     "and K a multiple of 8 (gemm_mfma_invariant takes any W [K, N] and gives the same bits)", fn);
     int bm, bn;
-    mfma_tile_shape(&bm, &bn);
+    mfma_wide_shape(mfma_wide_tile(N, K), &bm, &bn);   // the weight's tile, as for gemm_mfma_invariant
     MfmaArgs a;
     a.A = A;
     a.W = WT;
@@ -495,7 +509,7 @@ int gemm_mfma_invariant_wt(const uint16_t* A, int64_t lda, const uint16_t* WT, i
     a.vec = VEC_A | VEC_W;
     if (aligned(C, 16) && ldc % 4 == 0) a.vec |= VEC_C;
     a.ep = no_epi();
-    return launched(fn, launch_gemm_mfma_invariant_wt(a, s));
+    return launched(fn, launch_gemm_mfma_invariant_wt(a, bm, bn, s));
 }
 
 }  // extern "C"

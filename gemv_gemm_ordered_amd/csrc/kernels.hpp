@@ -102,7 +102,8 @@ hipError_t launch_gemm_mfma_lds128(const MfmaArgs& a, hipStream_t stream);      
 hipError_t launch_gemm_mfma_lds64x128(const MfmaArgs& a, hipStream_t stream);        // 64x128, direct to LDS
 hipError_t launch_gemm_mfma_t128(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mfma_t64(const MfmaArgs& a, hipStream_t stream);
-hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream);   // W given as W^T [N, K]
+// W given as W^T [N, K]: the direct-to-LDS instance of tile bm x bn (one of the four shapes above)
+hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, int bm, int bn, hipStream_t stream);
 
 struct GemvMfmaArgs {
     const uint16_t* x;

@@ -911,9 +911,19 @@ hipError_t launch_gemm_mfma_lds64x128(const MfmaArgs& a, hipStream_t stream) {
     return launch_t256<t256::BM_SMALL, t256::BN_NARROW, t256::BK_NARROW, t256::NST_NARROW>(a, stream);
 }
 
-hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, hipStream_t stream) {   // no epilogue on this entry
-    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<t256::BM_MAIN, t256::BN_MAIN, t256::BK_MAIN, t256::NST_MAIN, true, false>),
-                       dim3(a.tiles_m * a.tiles_n), dim3(t256::THREADS), 0, stream, a);
+// W^T entry (no epilogue): the direct-to-LDS instance of tile bm x bn
+template <int BM, int BN, int BK, int NST>
+static void launch_wt(const MfmaArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((t256::k_gemm_mfma_invariant<BM, BN, BK, NST, true, false>), dim3(a.tiles_m * a.tiles_n),
+                       dim3(t256::THREADS), 0, stream, a);
+}
+
+hipError_t launch_gemm_mfma_invariant_wt(const MfmaArgs& a, int bm, int bn, hipStream_t stream) {
+    using namespace t256;
+    if (bm == BM_MAIN && bn == BN_LARGE) launch_wt<BM_MAIN, BN_LARGE, BK_LARGE, NST_LARGE>(a, stream);
+    else if (bm == BM_MID) launch_wt<BM_MID, BN_NARROW, BK_NARROW, NST_NARROW>(a, stream);
+    else if (bm == BM_SMALL) launch_wt<BM_SMALL, BN_NARROW, BK_NARROW, NST_NARROW>(a, stream);
+    else launch_wt<BM_MAIN, BN_MAIN, BK_MAIN, NST_MAIN>(a, stream);
     return hipGetLastError();
 }
 

@@ -271,6 +271,8 @@ int gemm_mfma_invariant(const uint16_t *A, int64_t lda,
  * fragment, which costs 2.5x as much LDS time). The descriptor is
  * gemm_mfma_invariant's and every output has exactly its bits:
  * gemm_mfma_invariant_wt(A, W^T) == gemm_mfma_invariant(A, W) bit for bit.
+ * It runs the direct-to-LDS tile that gemm_mfma_invariant's rule gives the
+ * weight (256x256, 256x128, 128x128 or 64x128).
  *   A   device, [M, K] bfloat16 bits; 16-byte aligned, lda % 8 == 0, lda < 2^22
  *   WT  device, [N, K] bfloat16 bits; 16-byte aligned, ldwt % 8 == 0, ldwt < 2^22
  *   C   device, [M, N] binary32
