@@ -137,3 +137,30 @@ def test_bad_epilogue_rejected(g):
     assert g.lib.gemm_mfma_invariant_ep(1, 8, 1, 8, ct.byref(e), 1, 8, 1, 8, 8, None) == -1
     e = g.Epilogue(None, 1, 4, 0, g.GGO_F32)     # residual row stride below N
     assert g.lib.gemv_tree_ep(1, 8, 1, 8, ct.byref(e), 1, 8, 1, 8, 8, None) == -1
+
+
+_FOLDS = {}
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,tile", [((96, 2048, 1024), "128x128"), ((200, 1032, 2048), "256x128"),
+                                        ((70, 4096, 4096), "256x256")])
+def test_gemm_mfma_ep_on_the_wide_tiles(g, act, out, shape, tile):
+    """The fused epilogue of each direct-to-LDS tile the weight rule picks (ragged M, and a ragged N for
+    256x128): its passes stage a wave's rows through LDS, one to four per tile height."""
+    M, N, K = shape
+    if shape not in _FOLDS:
+        A = synth.normal_bf16(M + K, "epiw.A", (M, K))
+        W = synth.normal_bf16(N + K, "epiw.W", (K, N), 0.02)
+        say(f"epilogue {tile}: oracle fold {M}x{N}x{K}")
+        _FOLDS[shape] = (A, W, oracle.gemm_mfma(A, W, threads=16), synth.normal_f32(M + N, "epiw.b", (N,), 0.5),
+                         synth.normal_f32(M + N, "epiw.r", (M, N), 0.5))
+    A, W, Y, bias, res = _FOLDS[shape]
+    ref = ref_bits(Y, bias, act, res, out)
+    dA, dW = dev_bf16(A), dev_bf16(W)
+    got = host(g.gemm_mfma_invariant_ep(dA, dW, bias=dev_f32(bias), act=act, residual=dev_f32(res), out=out))
+    assert same(got, ref, out), (tile, act, out)
+    # and the tile's plain fold (no epilogue), forced through the hook, is the oracle's fold
+    assert np.array_equal(host(g.test_gemm_mfma_tile(tile if tile != "128x128" else "128x128_lds", dA, dW)),
+                          f32_bits(Y)), tile
