@@ -483,8 +483,8 @@ COUNTED = {
              "md": "gemv_tree_decode_4096x4096_traffic.md"},
     "mfma": {"kernel": "k_gemv_mfma", "source": "mfma_gemv.hip", "json": "gemv_mfma_traffic.json",
              "md": "gemv_mfma_decode_4096x4096_traffic.md"},
-    # gemv_ordered on W [K, N]: k_gemv_ordered at M <= 4, k_gemv_ordered_k128 at M = 8
-    "ordered": {"kernel": "k_gemv_ordered", "source": "ordered_gemv.hip", "json": "gemv_ordered_traffic.json",
+    # gemv_ordered on W [K, N]: k_gemv_ordered at M = 1, k_gemv_ordered_k128 at M = 4 and 8
+    "ordered": {"kernel": "k_gemv_ordered, k_gemv_ordered_k128", "source": "ordered_gemv.hip", "json": "gemv_ordered_traffic.json",
                 "md": "gemv_ordered_decode_4096x4096_traffic.md"},
 }
 
