@@ -219,20 +219,22 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree(TreeArgs a) {
 // The same arithmetic in persistent form, for 16-byte operands with K <= S * 2048 (S steps per
 // chain) and M <= 8. A lane's x tiles are the same for every output n (chain p always takes the
 // tiles p, p + 256, ...), so they are loaded once, widened to binary32 and kept in registers. The
-// workgroup then walks groups of R outputs, g = blockIdx.x, blockIdx.x + gridDim.x, ..., with the
-// weight rows of the next NB - 1 groups in flight while a group is folded: the weight stream and the
+// workgroup then walks groups of R outputs (consecutive groups, or with CONTIG false the groups
+// blockIdx.x, blockIdx.x + gridDim.x, ...), with the weight rows of the next NB - 1 groups in flight while a
+// group is folded: the weight stream and the
 // FMAs overlap, and the x tiles are not fetched again for every R rows. (In the form above a
 // workgroup owns one group: all of its loads, then all of its FMAs, in step with the other
 // workgroups on its CU.) Every output's chains, their order and the tree are those of k_gemv_tree,
 // so the bits are too.
 template <int MT, int R, int S>
-GGO_DEV void load_group(const TreeArgs& a, int g, int off, uint32_t (&w)[S][R][4]) {
+GGO_DEV void load_group(const TreeArgs& a, int g, int gend, int off, uint32_t (&w)[S][R][4]) {
     const int kbytes = a.K * 2;
     rsrc_t wr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t n = static_cast<int64_t>(g) * R + r;
-        wr[r] = row_rsrc(a.WT + n * a.ldwt, n < a.N ? kbytes : 0);   // past N (or past the last group): empty
+        // past the workgroup's last group (or past N): empty
+        wr[r] = row_rsrc(a.WT + n * a.ldwt, g < gend && n < a.N ? kbytes : 0);
     }
 #pragma unroll
     for (int j = 0; j < S; ++j)
@@ -256,14 +258,15 @@ GGO_DEV void wave_partials(float (&acc)[R][MT], float (&red)[WAVES][R * MT], int
 }
 
 // Levels 7-8 of the tree, (w0 + w1) + (w2 + w3), for the cnt groups whose wave totals sit in red[0 .. cnt),
-// the groups of ordinals j0 .. j0 + cnt - 1 of this workgroup (group g = blockIdx.x + ordinal * gridDim.x),
-// and the store. Called by every thread after a barrier.
+// the groups of ordinals j0 .. j0 + cnt - 1 of this workgroup (group g = first + ordinal * step), and the
+// store. Called by every thread after a barrier.
 template <int MT, int R, int RB, bool EPI>
-GGO_DEV void finish_groups(const TreeArgs& a, const float (&red)[RB][WAVES][R * MT], int j0, int cnt) {
+GGO_DEV void finish_groups(const TreeArgs& a, const float (&red)[RB][WAVES][R * MT], int first, int step, int j0,
+                           int cnt) {
     constexpr int V = R * MT;
     for (int i = threadIdx.x; i < cnt * V; i += THREADS) {
         const int q = i / V, iv = i - q * V, r = iv / MT, m = iv % MT;
-        const int64_t n = (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j0 + q) * gridDim.x) * R + r;
+        const int64_t n = (static_cast<int64_t>(first) + static_cast<int64_t>(j0 + q) * step) * R + r;
         if (m < a.M && n < a.N) {
             const float y = (red[q][0][iv] + red[q][1][iv]) + (red[q][2][iv] + red[q][3][iv]);
             if constexpr (EPI) epi_store(a.ep, a.y, a.ldy, m, n, y);
@@ -293,8 +296,9 @@ GGO_DEV void fold_group(float (&acc)[R][MT], const uint32_t (&w)[S][R][4], const
         }
 }
 
-template <int MT, int R, int S, int NB, bool EPI, int RB>
-__global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a) {
+// CONTIG: workgroup b walks the gpw consecutive groups from b gpw, else the groups b, b + gridDim.x, ...
+template <int MT, int R, int S, int NB, bool EPI, int RB, bool CONTIG>
+__global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a, int gpw) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p = wave * 64 + lane;
     const int off = p * TILE * 2;
@@ -322,24 +326,26 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a) {
     __shared__ float red[2][RB][WAVES][R * MT];
     uint32_t w[NB][S][R][4];
     float acc[R][MT];
-    const int stride = gridDim.x;
-    int g = blockIdx.x;                       // < groups: the grid is never larger
+    const int first = CONTIG ? static_cast<int>(blockIdx.x) * gpw : static_cast<int>(blockIdx.x);   // < groups
+    const int stride = CONTIG ? 1 : static_cast<int>(gridDim.x);
+    const int gend = CONTIG ? min(groups, first + gpw) : groups;
+    int g = first;
     int j = 0;                                // ordinal of the current group in this workgroup
 #pragma unroll
-    for (int b = 0; b + 1 < NB; ++b) load_group<MT, R, S>(a, g + b * stride, off, w[b]);
+    for (int b = 0; b + 1 < NB; ++b) load_group<MT, R, S>(a, g + b * stride, gend, off, w[b]);
     for (;;) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int gb = g + b * stride;
-            load_group<MT, R, S>(a, gb + (NB - 1) * stride, off, w[(b + NB - 1) % NB]);
+            load_group<MT, R, S>(a, gb + (NB - 1) * stride, gend, off, w[(b + NB - 1) % NB]);
             __builtin_amdgcn_sched_barrier(0);    // the requests stay ahead of this fold
             fold_group<MT, R, S>(acc, w[b], x);
             const int h = (j / RB) & 1, q = j % RB;
             wave_partials<MT, R>(acc, red[h][q], lane, wave);
-            const bool last = gb + stride >= groups;   // uniform across the workgroup
+            const bool last = gb + stride >= gend;   // uniform across the workgroup
             if (last || q == RB - 1) {
                 __syncthreads();
-                finish_groups<MT, R, RB, EPI>(a, red[h], j - q, q + 1);
+                finish_groups<MT, R, RB, EPI>(a, red[h], first, stride, j - q, q + 1);
             }
             ++j;
             if (last) goto done;
@@ -380,13 +386,22 @@ hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
     // from overlapping the stream (R = 2: 9.6 us; batches of 4: 9.2 us; one output per group in batches
     // of 8: 8.9 us); at M <= 4, with two to four groups per workgroup, deferring the last levels only
     // lengthens the tail (7.7 -> 7.9 us at M = 4).
+    // CONTIG: each workgroup walks consecutive groups, so the rows it has in flight are neighbours (one
+    // advancing window per wave instead of rows gridDim.x groups apart): M = 4 / 8 7.42 / 8.93 us against
+    // 7.74 / 9.18 strided, M = 1 level (alternated three times; the same bits). With contiguous groups a
+    // third group in flight gained nothing at M = 8 and a fourth lost 0.7 us.
     constexpr int R = MT >= 8 ? 1 : 2, NB = 2, PER_CU = 2, RB = MT >= 8 ? 8 : 1;
+    constexpr bool CONTIG = true;
     const int64_t groups = (a.N + R - 1) / R;
-    const int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
+    int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
+    const int gpw = static_cast<int>((groups + blocks - 1) / blocks);
+    if (CONTIG) blocks = (groups + gpw - 1) / gpw;   // every workgroup has at least one group
     if (epi_identity(a.ep))
-        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, false, RB>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, false, RB, CONTIG>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0,
+                           stream, a, gpw);
     else
-        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, true, RB>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, true, RB, CONTIG>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0,
+                           stream, a, gpw);
     return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ def test_ordered_kernels_have_no_contraction(code):
 
 def test_tree_kernels_use_single_fma_and_add(code):
     """The instances without an epilogue (template flag EPI = false, mangled ...Lb0EEEv8TreeArgs, or
-    ...Lb0ELi<batch>EEEv8TreeArgs for the persistent form) hold
+    ...Lb0ELi<batch>ELb<contiguous>EEEv8TreeArgsi for the persistent form) hold
     the fold and the tree alone: their binary32 arithmetic is v_fma_f32 / v_fmac_f32 and v_add_f32 only.
     The epilogue instances add the epilogue's own operations after the fold; they are checked for no
     packed, dot or matrix instruction."""
@@ -78,8 +78,9 @@ def test_tree_kernels_use_single_fma_and_add(code):
     # persistent form: M tiers 1, 2, 4, 8 x 1 or 2 steps per chain x with / without epilogue
     assert len([k for k in ks if "k_gemv_treeI" in k]) == 20, ks
     assert len([k for k in ks if "k_gemv_tree_pI" in k]) == 16, ks
-    # the epilogue flag is the last bool template argument (the persistent form adds its batch size after it)
-    plain = [k for k in ks if k.endswith("Lb0EEEv8TreeArgs") or re.search(r"Lb0ELi\d+EEEv8TreeArgs$", k)]
+    # the epilogue flag is the last bool template argument (the persistent form adds its batch size and its
+    # group-mapping flag after it, and takes an int argument after TreeArgs)
+    plain = [k for k in ks if k.endswith("Lb0EEEv8TreeArgs") or re.search(r"Lb0ELi\d+ELb[01]EEEv8TreeArgsi$", k)]
     assert len(plain) == 18, plain
     for k in ks:
         text = "\n".join(code["tree_gemv.hip"][k])
