@@ -384,13 +384,14 @@ template <int MT, int S>
 hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
     // RB: groups per cross-wave batch. At M = 8 a barrier per group kept the waves in step and the folds
     // from overlapping the stream (R = 2: 9.6 us; batches of 4: 9.2 us; one output per group in batches
-    // of 8: 8.9 us); at M <= 4, with two to four groups per workgroup, deferring the last levels only
-    // lengthens the tail (7.7 -> 7.9 us at M = 4).
+    // of 8: 8.9 us). At M <= 2 (four groups per workgroup) one batch, so one barrier, per workgroup: M = 1
+    // 6.70 against 6.92 - 7.09 us with a barrier per group, M = 2 level; at M = 4 the batch was level to
+    // 0.1 us slower, and it keeps a barrier per group.
     // CONTIG: each workgroup walks consecutive groups, so the rows it has in flight are neighbours (one
     // advancing window per wave instead of rows gridDim.x groups apart): M = 4 / 8 7.42 / 8.93 us against
     // 7.74 / 9.18 strided, M = 1 level (alternated three times; the same bits). With contiguous groups a
     // third group in flight gained nothing at M = 8 and a fourth lost 0.7 us.
-    constexpr int R = MT >= 8 ? 1 : 2, NB = 2, PER_CU = 2, RB = MT >= 8 ? 8 : 1;
+    constexpr int R = MT >= 8 ? 1 : 2, NB = 2, PER_CU = 2, RB = MT >= 8 ? 8 : MT <= 2 ? 4 : 1;
     constexpr bool CONTIG = true;
     const int64_t groups = (a.N + R - 1) / R;
     int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
