@@ -374,8 +374,10 @@ int device_cus() {
 // Persistent launch: R outputs per group, NB groups in rotation, two workgroups per CU (8 waves).
 // Measured on the decode shape (N = K = 4096): two outputs per group at M <= 4 (M = 1: 6.8 us against
 // 7.0 with four), one at M = 8, where the fold per group is largest. Slower, each measured at M = 8 in
-// the same process: deeper rotation (NB = 3, 4: 9.5, 9.9 against 9.0 us); three workgroups per CU or one
-// (9.6, 11.3); issuing the first groups' weight loads before the x tiles are widened (no change);
+// the same process: deeper rotation (NB = 3, 4: 9.5, 9.9 against 9.0 us; again with the prologue's loads
+// kept in order, so that the loop waits for the oldest group only, and the groups in whole rounds with
+// one batch: 10.0 - 10.4, 9.6 - 10.1 against 8.8 - 9.0, and with NB = 2 level); three workgroups per CU
+// or one (9.6, 11.3); issuing the first groups' weight loads before the x tiles are widened (no change);
 // raising the wave priority around the weight loads (no change); splitting the rows of x over twice or
 // four times the waves, each set fetching the same weight tiles (10.8-17.7); producer waves streaming
 // the weight into an LDS ring with direct-to-LDS loads and four folding waves (12.3-15.2: a barrier per
