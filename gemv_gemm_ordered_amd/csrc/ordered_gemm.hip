@@ -14,7 +14,8 @@
 // while each chain stays sequential). Small weights take a 16x16 tile with one
 // output per lane instead (see Tile below). A and W tiles are read from HBM with
 // 16-byte loads, widened to binary32 once, and staged in LDS (A transposed so a
-// lane's four rows sit in one 16-byte LDS read). Tiles move through registers
+// lane's four rows sit in one 16-byte LDS read; on the one-output tile A by rows
+// and W by columns, so a lane's four k do). Tiles move through registers
 // one step ahead of the arithmetic (prefetch), which moves loads but no adds.
 // Built with -ffp-contract=off and the pragma below, so no mul/add pair is ever
 // fused; packed binary32 ops are disabled at build time.
@@ -164,6 +165,21 @@ GGO_DEV void store_tiles(float (*As)[T::BM + APAD], float (*Ws)[T::BN], int t, c
     *reinterpret_cast<float4*>(&Ws[kr][nc + 4]) = make_float4(elem<0>(w, 4), elem<0>(w, 5), elem<0>(w, 6), elem<0>(w, 7));
 }
 
+// One-output tile: LDS holds the rows of A and the columns of W with k contiguous (each row padded by 4
+// floats, so the 4 rows of A and the 16 columns of W a wave reads fall on distinct banks), and a lane takes
+// 4 k of its row and of its column with one 16-byte read each. The thread's chunk of A (one row, 8 k)
+// goes into its row with two 16-byte writes; its chunk of W (one k-row, 8 columns) into 8 columns.
+template <class T, int AF32>
+GGO_DEV void store_rows(float (*A1)[T::BK + 4], float (*W1)[T::BK + 4], int t, const Chunk& a, const Chunk& w) {
+    const int r = t / T::CA, kc = (t % T::CA) * 8;
+    *reinterpret_cast<float4*>(&A1[r][kc]) = make_float4(elem<AF32>(a, 0), elem<AF32>(a, 1), elem<AF32>(a, 2), elem<AF32>(a, 3));
+    *reinterpret_cast<float4*>(&A1[r][kc + 4]) = make_float4(elem<AF32>(a, 4), elem<AF32>(a, 5), elem<AF32>(a, 6), elem<AF32>(a, 7));
+    if (T::WCH < THREADS && t >= T::WCH) return;   // uniform per wave
+    const int kr = t / T::CW, nc = (t % T::CW) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) W1[nc + i][kr] = elem<0>(w, i);
+}
+
 // One step of every chain the lane owns: acc[i][j] = acc[i][j] + (a[i] * w[j]).
 template <class T>
 GGO_DEV void fold_step(float (&acc)[T::TM][T::TN], const float (*As)[T::BM + APAD], const float (*Ws)[T::BN],
@@ -205,6 +221,11 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
     constexpr int NSTG = T::TM * T::TN == 1 ? 1 : 2;
     __shared__ __attribute__((aligned(16))) float AsB[NSTG][BK][BM + APAD];
     __shared__ __attribute__((aligned(16))) float WsB[NSTG][BK][BN];
+    // the one-output tile's rows of A and columns of W (store_rows); the arrays an instance never touches
+    // take no LDS
+    constexpr bool ONE = T::TM * T::TN == 1;
+    __shared__ __attribute__((aligned(16))) float A1[ONE ? BM : 1][BK + 4];
+    __shared__ __attribute__((aligned(16))) float W1[ONE ? BN : 1][BK + 4];
 
     // which problem, which batch entry, which tile
     const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -245,7 +266,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
                 load_w<T>(P, Wb, n0, d * BK, t, rw[d]);
             }
         }
-    if (nkt > 0) store_tiles<T, AF32>(AsB[0], WsB[0], t, ra[0], rw[0]);
+    if (nkt > 0) {
+        if constexpr (ONE) store_rows<T, AF32>(A1, W1, t, ra[0], rw[0]);
+        else store_tiles<T, AF32>(AsB[0], WsB[0], t, ra[0], rw[0]);
+    }
     __syncthreads();
     for (int kt0 = 0; kt0 < nkt; kt0 += D) {
 #pragma unroll
@@ -268,27 +292,36 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             if (kb == BK) {
                 if constexpr (T::TM * T::TN == 1) {
                     // One output per lane and one wave per SIMD: nothing else hides the LDS latency, so
-                    // the reads of the next 8 k are issued before the adds of the current 8 (the
-                    // compiler's own schedule kept two steps ahead).
+                    // the reads of the next 8 k (two 16-byte reads of the lane's row of A, two of its
+                    // column of W) are issued before the adds of the current 8. With a 4-byte read per
+                    // operand and k the GPT-2 projection took 13.0 - 13.3 us at M = 1 - 64 and 55 us at
+                    // M = 512, against 9.1 - 9.8 and 27 (same bits).
                     constexpr int CH = 8, NCH = BK / CH;
-                    float av[2][CH], wv[2][CH];
+                    float4 av[2][2], wv[2][2];
 #pragma unroll
-                    for (int j = 0; j < CH; ++j) {
-                        av[0][j] = As[j][ty];
-                        wv[0][j] = Ws[j][tx];
+                    for (int h = 0; h < 2; ++h) {
+                        av[0][h] = *reinterpret_cast<const float4*>(&A1[ty][4 * h]);
+                        wv[0][h] = *reinterpret_cast<const float4*>(&W1[tx][4 * h]);
                     }
 #pragma unroll
                     for (int c = 0; c < NCH; ++c) {
                         if (c + 1 < NCH) {
 #pragma unroll
-                            for (int j = 0; j < CH; ++j) {
-                                av[(c + 1) & 1][j] = As[(c + 1) * CH + j][ty];
-                                wv[(c + 1) & 1][j] = Ws[(c + 1) * CH + j][tx];
+                            for (int h = 0; h < 2; ++h) {
+                                av[(c + 1) & 1][h] = *reinterpret_cast<const float4*>(&A1[ty][(c + 1) * CH + 4 * h]);
+                                wv[(c + 1) & 1][h] = *reinterpret_cast<const float4*>(&W1[tx][(c + 1) * CH + 4 * h]);
                             }
                         }
 #pragma unroll
-                        for (int j = 0; j < CH; ++j) {   // ascending k
-                            const float p = av[c & 1][j] * wv[c & 1][j];
+                        for (int h = 0; h < 2; ++h) {   // ascending k
+                            const float4 a = av[c & 1][h], w = wv[c & 1][h];
+                            float p = a.x * w.x;
+                            acc[0][0] = acc[0][0] + p;
+                            p = a.y * w.y;
+                            acc[0][0] = acc[0][0] + p;
+                            p = a.z * w.z;
+                            acc[0][0] = acc[0][0] + p;
+                            p = a.w * w.w;
                             acc[0][0] = acc[0][0] + p;
                         }
                     }
@@ -342,6 +375,11 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
                             }
                     }
                 }
+            } else if constexpr (ONE) {
+                for (int kk = 0; kk < kb; ++kk) {   // the partial last step, ascending k
+                    const float p = A1[ty][kk] * W1[tx][kk];
+                    acc[0][0] = acc[0][0] + p;
+                }
             } else {
                 for (int kk = 0; kk < kb; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
             }
@@ -352,7 +390,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             } else {
                 __syncthreads();
                 if (kt + 1 < nkt) {
-                    store_tiles<T, AF32>(AsB[0], WsB[0], t, ra[(d + 1) % D], rw[(d + 1) % D]);
+                    if constexpr (ONE) store_rows<T, AF32>(A1, W1, t, ra[(d + 1) % D], rw[(d + 1) % D]);
+                    else store_tiles<T, AF32>(AsB[0], WsB[0], t, ra[(d + 1) % D], rw[(d + 1) % D]);
                     __syncthreads();
                 }
             }

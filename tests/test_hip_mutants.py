@@ -35,8 +35,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 HIP_MUTANTS = {
     "ordered_k_reversed_in_8": ("ordered_gemm.hip", [
-        ("const float p = av[c & 1][j] * wv[c & 1][j];",
-         "const float p = av[c & 1][CH - 1 - j] * wv[c & 1][CH - 1 - j];"),
+        # each run of 8 k is read as two 16-byte halves of 4 k: take the halves in reverse and each half's
+        # 4 k in reverse, so k runs 7, 6, ..., 0 within every run of 8
+        ("const float4 a = av[c & 1][h], w = wv[c & 1][h];",
+         "const float4 a0 = av[c & 1][1 - h], w0 = wv[c & 1][1 - h];\n"
+         "                            const float4 a = make_float4(a0.w, a0.z, a0.y, a0.x), "
+         "w = make_float4(w0.w, w0.z, w0.y, w0.x);"),
     ]),
     "mfma_group_swap": ("mfma_invariant.hip", [
         ("f.a[i] = *reinterpret_cast<const bf16x8*>(base + c.ra[g] + i * ROW16);",
