@@ -214,18 +214,18 @@ GGO_DEV void fold_step(float (&acc)[T::TM][T::TN], const float (*As)[T::BM + APA
 template <class T, int AF32, bool WIDE>
 __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK, TM = T::TM, TN = T::TN;
-    // Two LDS stages on the micro-tile instances: step kt + 1 is stored into the other stage while the
-    // slower lanes may still be folding step kt, so a k-step needs one barrier instead of two (MLP weight
-    // M = 256 / 512: 32.3 -> 34.2 / 39.1 -> 41.2 TFLOP/s; 4096 x 4096 at M = 2048 52.2 -> 54.6). The
-    // one-output tile keeps one stage and two barriers (two stages were 2% slower there).
-    constexpr int NSTG = T::TM * T::TN == 1 ? 1 : 2;
+    // Two LDS stages: step kt + 1 is stored into the other stage while the slower lanes may still be
+    // folding step kt, so a k-step needs one barrier instead of two (MLP weight M = 256 / 512: 32.3 -> 34.2
+    // / 39.1 -> 41.2 TFLOP/s; 4096 x 4096 at M = 2048 52.2 -> 54.6; the one-output tile's GPT-2 projection
+    // 9.0 - 9.8 -> 8.8 - 9.4 us at M <= 64, 27.0 -> 26.6 at M = 512).
+    constexpr int NSTG = 2;
     __shared__ __attribute__((aligned(16))) float AsB[NSTG][BK][BM + APAD];
     __shared__ __attribute__((aligned(16))) float WsB[NSTG][BK][BN];
     // the one-output tile's rows of A and columns of W (store_rows); the arrays an instance never touches
     // take no LDS
     constexpr bool ONE = T::TM * T::TN == 1;
-    __shared__ __attribute__((aligned(16))) float A1[ONE ? BM : 1][BK + 4];
-    __shared__ __attribute__((aligned(16))) float W1[ONE ? BN : 1][BK + 4];
+    __shared__ __attribute__((aligned(16))) float A1S[ONE ? NSTG : 1][ONE ? BM : 1][BK + 4];
+    __shared__ __attribute__((aligned(16))) float W1S[ONE ? NSTG : 1][ONE ? BN : 1][BK + 4];
 
     // which problem, which batch entry, which tile
     const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             }
         }
     if (nkt > 0) {
-        if constexpr (ONE) store_rows<T, AF32>(A1, W1, t, ra[0], rw[0]);
+        if constexpr (ONE) store_rows<T, AF32>(A1S[0], W1S[0], t, ra[0], rw[0]);
         else store_tiles<T, AF32>(AsB[0], WsB[0], t, ra[0], rw[0]);
     }
     __syncthreads();
@@ -289,6 +289,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             const int kb = P.K - k0 < BK ? P.K - k0 : BK;
             const auto& As = AsB[kt & (NSTG - 1)];
             const auto& Ws = WsB[kt & (NSTG - 1)];
+            const auto& A1 = A1S[ONE ? (kt & (NSTG - 1)) : 0];
+            const auto& W1 = W1S[ONE ? (kt & (NSTG - 1)) : 0];
             if (kb == BK) {
                 if constexpr (T::TM * T::TN == 1) {
                     // One output per lane and one wave per SIMD: nothing else hides the LDS latency, so
@@ -383,18 +385,12 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             } else {
                 for (int kk = 0; kk < kb; ++kk) fold_step<T>(acc, As, Ws, kk, ty, tx);
             }
-            if constexpr (NSTG == 2) {
-                // the other stage was last read in step kt - 1, before the barrier that ended it
-                if (kt + 1 < nkt) store_tiles<T, AF32>(AsB[(kt + 1) & 1], WsB[(kt + 1) & 1], t, ra[(d + 1) % D], rw[(d + 1) % D]);
-                __syncthreads();
-            } else {
-                __syncthreads();
-                if (kt + 1 < nkt) {
-                    if constexpr (ONE) store_rows<T, AF32>(A1, W1, t, ra[(d + 1) % D], rw[(d + 1) % D]);
-                    else store_tiles<T, AF32>(AsB[0], WsB[0], t, ra[(d + 1) % D], rw[(d + 1) % D]);
-                    __syncthreads();
-                }
+            // the other stage was last read in step kt - 1, before the barrier that ended it
+            if (kt + 1 < nkt) {
+                if constexpr (ONE) store_rows<T, AF32>(A1S[(kt + 1) & 1], W1S[(kt + 1) & 1], t, ra[(d + 1) % D], rw[(d + 1) % D]);
+                else store_tiles<T, AF32>(AsB[(kt + 1) & 1], WsB[(kt + 1) & 1], t, ra[(d + 1) % D], rw[(d + 1) % D]);
             }
+            __syncthreads();
         }
     }
 
