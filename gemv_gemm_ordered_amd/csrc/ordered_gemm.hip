@@ -180,6 +180,24 @@ GGO_DEV void store_rows(float (*A1)[T::BK + 4], float (*W1)[T::BK + 4], int t, c
     for (int i = 0; i < 8; ++i) W1[nc + i][kr] = elem<0>(w, i);
 }
 
+// 4 x 2 tile: LDS holds the rows of A and the columns of W with k contiguous, so a lane reads 4 k of
+// each of its 4 rows and 2 columns with 6 16-byte reads (8 with one k per read). Column n of W sits in row
+// (n & 1) BN/2 + n/2 (rows padded by 4 floats): the 16 columns a wave reads together, and the 4 rows of A,
+// then fall on distinct banks.
+template <class T, int AF32>
+GGO_DEV void store_rows2(float (*A2)[T::BK + 4], float (*W2)[T::BK + 4], int t, const Chunk& a, const Chunk& w) {
+    const int r = t / T::CA, kc = (t % T::CA) * 8;
+    *reinterpret_cast<float4*>(&A2[r][kc]) = make_float4(elem<AF32>(a, 0), elem<AF32>(a, 1), elem<AF32>(a, 2), elem<AF32>(a, 3));
+    *reinterpret_cast<float4*>(&A2[r][kc + 4]) = make_float4(elem<AF32>(a, 4), elem<AF32>(a, 5), elem<AF32>(a, 6), elem<AF32>(a, 7));
+    if (T::WCH < THREADS && t >= T::WCH) return;   // uniform per wave
+    const int kr = t / T::CW, nc = (t % T::CW) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int n = nc + i;
+        W2[(n & 1) * (T::BN / 2) + (n >> 1)][kr] = elem<0>(w, i);
+    }
+}
+
 // One step of every chain the lane owns: acc[i][j] = acc[i][j] + (a[i] * w[j]).
 template <class T>
 GGO_DEV void fold_step(float (&acc)[T::TM][T::TN], const float (*As)[T::BM + APAD], const float (*Ws)[T::BN],
@@ -226,6 +244,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
     constexpr bool ONE = T::TM * T::TN == 1;
     __shared__ __attribute__((aligned(16))) float A1S[ONE ? NSTG : 1][ONE ? BM : 1][BK + 4];
     __shared__ __attribute__((aligned(16))) float W1S[ONE ? NSTG : 1][ONE ? BN : 1][BK + 4];
+    // the 4 x 2 tile's rows of A and columns of W (store_rows2)
+    constexpr bool ROWS2 = T::TM == 4 && T::TN == 2;
+    __shared__ __attribute__((aligned(16))) float A2S[ROWS2 ? NSTG : 1][ROWS2 ? BM : 1][BK + 4];
+    __shared__ __attribute__((aligned(16))) float W2S[ROWS2 ? NSTG : 1][ROWS2 ? BN : 1][BK + 4];
 
     // which problem, which batch entry, which tile
     const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -268,6 +290,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
         }
     if (nkt > 0) {
         if constexpr (ONE) store_rows<T, AF32>(A1S[0], W1S[0], t, ra[0], rw[0]);
+        else if constexpr (ROWS2) store_rows2<T, AF32>(A2S[0], W2S[0], t, ra[0], rw[0]);
         else store_tiles<T, AF32>(AsB[0], WsB[0], t, ra[0], rw[0]);
     }
     __syncthreads();
@@ -291,6 +314,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             const auto& Ws = WsB[kt & (NSTG - 1)];
             const auto& A1 = A1S[ONE ? (kt & (NSTG - 1)) : 0];
             const auto& W1 = W1S[ONE ? (kt & (NSTG - 1)) : 0];
+            const auto& A2 = A2S[ROWS2 ? (kt & (NSTG - 1)) : 0];
+            const auto& W2 = W2S[ROWS2 ? (kt & (NSTG - 1)) : 0];
             if (kb == BK) {
                 if constexpr (T::TM * T::TN == 1) {
                     // One output per lane and one wave per SIMD: nothing else hides the LDS latency, so
@@ -354,29 +379,52 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
                             }
                     }
                 } else {
-                    // 4 x 2 micro-tile: the same schedule with an 8-byte read of W
+                    // 4 x 2 micro-tile, rows of A and columns of W: the next 4 k's six 16-byte reads are
+                    // issued before this 4 k's 32 operations. With one k per read (a 16-byte read of A, an
+                    // 8-byte read of W) the MLP weight took 50.3 / 61.7 / 102 / 343 us at M = 64 / 256 /
+                    // 512 / 2048, against 48.0 / 54.2 / 94.9 / 325 (same bits).
                     static_assert(T::TM == 4 && T::TN == 2, "");
-                    float4 a4[2];
-                    float2 w2[2];
-                    a4[0] = *reinterpret_cast<const float4*>(&As[0][ty * 4]);
-                    w2[0] = *reinterpret_cast<const float2*>(&Ws[0][tx * 2]);
+                    float4 a4[2][4], w4[2][2];
 #pragma unroll
-                    for (int kk = 0; kk < BK; ++kk) {
-                        if (kk + 1 < BK) {
-                            a4[(kk + 1) & 1] = *reinterpret_cast<const float4*>(&As[kk + 1][ty * 4]);
-                            w2[(kk + 1) & 1] = *reinterpret_cast<const float2*>(&Ws[kk + 1][tx * 2]);
+                    for (int i = 0; i < 4; ++i) a4[0][i] = *reinterpret_cast<const float4*>(&A2[ty * 4 + i][0]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) w4[0][j] = *reinterpret_cast<const float4*>(&W2[j * (BN / 2) + tx][0]);
+#pragma unroll
+                    for (int k4 = 0; k4 < BK / 4; ++k4) {
+                        if (k4 + 1 < BK / 4) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                a4[(k4 + 1) & 1][i] = *reinterpret_cast<const float4*>(&A2[ty * 4 + i][4 * (k4 + 1)]);
+#pragma unroll
+                            for (int j = 0; j < 2; ++j)
+                                w4[(k4 + 1) & 1][j] = *reinterpret_cast<const float4*>(&W2[j * (BN / 2) + tx][4 * (k4 + 1)]);
                         }
-                        const float a[4] = {a4[kk & 1].x, a4[kk & 1].y, a4[kk & 1].z, a4[kk & 1].w};
-                        const float w[2] = {w2[kk & 1].x, w2[kk & 1].y};
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
+                        for (int e = 0; e < 4; ++e) {   // ascending k
+                            float a[4], w[2];
 #pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                const float p = a[i] * w[j];   // first rounding
-                                acc[i][j] = acc[i][j] + p;     // second rounding
-                            }
+                            for (int i = 0; i < 4; ++i) a[i] = (&a4[k4 & 1][i].x)[e];
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) w[j] = (&w4[k4 & 1][j].x)[e];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                for (int j = 0; j < 2; ++j) {
+                                    const float p = a[i] * w[j];   // first rounding
+                                    acc[i][j] = acc[i][j] + p;     // second rounding
+                                }
+                        }
                     }
                 }
+            } else if constexpr (ROWS2) {
+                for (int kk = 0; kk < kb; ++kk)   // the partial last step, ascending k
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const float p = A2[ty * 4 + i][kk] * W2[j * (BN / 2) + tx][kk];
+                            acc[i][j] = acc[i][j] + p;
+                        }
             } else if constexpr (ONE) {
                 for (int kk = 0; kk < kb; ++kk) {   // the partial last step, ascending k
                     const float p = A1[ty][kk] * W1[tx][kk];
@@ -388,6 +436,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_ordered(const OrdGroup g) {
             // the other stage was last read in step kt - 1, before the barrier that ended it
             if (kt + 1 < nkt) {
                 if constexpr (ONE) store_rows<T, AF32>(A1S[(kt + 1) & 1], W1S[(kt + 1) & 1], t, ra[(d + 1) % D], rw[(d + 1) % D]);
+                else if constexpr (ROWS2) store_rows2<T, AF32>(A2S[(kt + 1) & 1], W2S[(kt + 1) & 1], t, ra[(d + 1) % D], rw[(d + 1) % D]);
                 else store_tiles<T, AF32>(AsB[(kt + 1) & 1], WsB[(kt + 1) & 1], t, ra[(d + 1) % D], rw[(d + 1) % D]);
             }
             __syncthreads();
