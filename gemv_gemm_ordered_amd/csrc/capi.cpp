@@ -142,9 +142,26 @@ int fill_problem(const char* fn, const ggo_problem& q, int a_dtype, int kind, Or
 // Tile of the ordered kernel, for gemm_ordered: 16 x 16 (one output per lane) on a weight of at most
 // 2^20 elements, 64 x 32 (4 x 2 per lane) on one of at most 2^22, else 64 x 64 (4 x 4 per lane): the
 // smaller the weight, the more outputs a tile gives up so that the weight still fills the chip at small
-// M. The choice depends on the entry point and the weight's shape, never on M; every output's chain,
-// and so its bits, is the same under every tile. Grouped launches (the value product) keep 64 x 64.
+// M. A grouped launch (the value product) counts the weight elements of all its problems and batch
+// entries: 64 x 32 up to 2^22, else 64 x 64 (32 heads of d = 128: 64 x 32 at L = 256 took 17 - 19 us
+// against 24 - 26 on 64 x 64, level at L = 1024, 6% slower at L = 5000; the 16 x 16 tile was no faster
+// than 64 x 64 at L = 256). The choice depends on the entry point and the weights' shapes, never on M;
+// every output's chain, and so its bits, is the same under every tile.
 constexpr int64_t ORDERED_SMALL_WEIGHT = int64_t(1) << 20, ORDERED_MID_WEIGHT = int64_t(1) << 22;
+
+// Weight elements of a launch, counted up to just past ORDERED_MID_WEIGHT (problems that validation will
+// reject count as nothing, and nothing here can overflow)
+int64_t launch_weight(const ggo_problem* qs, int64_t count) {
+    const int64_t cap = ORDERED_MID_WEIGHT + 1;
+    int64_t w = 0;
+    for (int64_t i = 0; i < count && w < cap; ++i) {
+        const ggo_problem& q = qs[i];
+        if (q.batch <= 0 || q.N <= 0 || q.K <= 0) continue;
+        if (q.batch >= cap || q.N >= cap || q.K >= cap || q.N * q.K >= cap) return cap;
+        w += q.batch * (q.N * q.K);   // each factor below 2^23: no overflow
+    }
+    return w < cap ? w : cap;
+}
 
 int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype, int small_ok, hipStream_t s,
               int force_kind = -1) {
@@ -156,10 +173,11 @@ int run_group(const char* fn, const ggo_problem* qs, int64_t count, int a_dtype,
     int64_t total = 0;
     int n = 0;
     const bool single = small_ok && count == 1 && qs[0].batch == 1;
-    const int kind = force_kind >= 0                                            ? force_kind
-                   : single && qs[0].N * qs[0].K <= ORDERED_SMALL_WEIGHT ? ORD_TILE_SMALL
-                   : single && qs[0].N * qs[0].K <= ORDERED_MID_WEIGHT   ? ORD_TILE_MID
-                                                                         : ORD_TILE_BIG;
+    const int64_t wsum = launch_weight(qs, count);
+    const int kind = force_kind >= 0                            ? force_kind
+                   : single && wsum <= ORDERED_SMALL_WEIGHT ? ORD_TILE_SMALL
+                   : wsum <= ORDERED_MID_WEIGHT             ? ORD_TILE_MID
+                                                            : ORD_TILE_BIG;
     int wide = 1;   // the launch takes the wide loads only if every problem allows them
     for (int64_t i = 0; i < count; ++i) {
         int64_t tiles = 0;
