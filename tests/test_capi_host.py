@@ -81,6 +81,14 @@ def test_bad_arguments_are_rejected_without_touching_the_gpu(g):
     assert lib.gemm_ordered_grouped(null, 1, 0, null) == -1
     arr = (g.Problem * 1)()
     assert lib.gemm_ordered_grouped(arr, 17, 0, null) == -1
+    # the grouped launch sizes its tile from the problems before it validates them: sizes that would overflow
+    # that count, or negative ones, still end in an error code, with nothing launched
+    big = (g.Problem * 2)()
+    big[0].M, big[0].N, big[0].K, big[0].batch = 8, 1 << 40, 1 << 40, 1 << 40
+    big[1].M, big[1].N, big[1].K, big[1].batch = 8, -5, 1 << 62, 3
+    assert lib.gemm_ordered_grouped(big, 2, 0, null) < 0
+    big[0].N, big[0].K, big[0].batch = -1, -1, -1
+    assert lib.gemm_ordered_grouped(big, 1, 0, null) < 0
     # empty problems are valid and launch nothing
     assert lib.gemm_ordered(null, 0, 8, null, 8, null, 8, 0, 8, 8, null) == 0
     assert lib.gemv_ordered(null, 8, null, 8, null, 8, 0, 8, 8, null) == 0
