@@ -22,7 +22,8 @@
  *    anything else takes element loads, with the same arithmetic and bits.
  *  - Dispatch. M never chooses anything that decides an output's order: no
  *    split of K, no tile of the matrix-core or ordered GEMM (those follow the
- *    weight's shape and the operands' alignment). The decode GEMVs
+ *    weight's shape -- for a grouped launch, the weight elements of all its
+ *    problems together -- and the operands' alignment). The decode GEMVs
  *    (gemv_ordered, gemv_ordered_wt, gemv_tree, gemv_mfma_invariant) do
  *    choose, from M, an instance of their kernel: how many rows of x a
  *    workgroup stages (M rounded up to 1, 2, 4, 8 or 16), and for the ordered
