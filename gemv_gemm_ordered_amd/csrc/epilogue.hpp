@@ -76,12 +76,21 @@ GGO_DEV float epi_act(float v, int act) {
     }
 }
 
-GGO_DEV float epi_apply(const Epi& e, float y, int64_t m, int64_t n) {
+// y + bias, the activation, + residual, with the bias b and the residual r of the output already loaded
+// (each ignored when the epilogue has none)
+GGO_DEV float epi_apply_loaded(const Epi& e, float y, float b, float r) {
     float v = y;
-    if (e.bias) v = v + e.bias[n];
+    if (e.bias) v = v + b;
     v = epi_act(v, e.act);
-    if (e.res) v = v + e.res[m * e.ldr + n];
+    if (e.res) v = v + r;
     return v;
+}
+
+GGO_DEV float epi_bias1(const Epi& e, int64_t n) { return e.bias ? e.bias[n] : 0.0f; }
+GGO_DEV float epi_res1(const Epi& e, int64_t m, int64_t n) { return e.res ? e.res[m * e.ldr + n] : 0.0f; }
+
+GGO_DEV float epi_apply(const Epi& e, float y, int64_t m, int64_t n) {
+    return epi_apply_loaded(e, y, epi_bias1(e, n), epi_res1(e, m, n));
 }
 
 GGO_DEV uint16_t epi_bf16(float v) {
@@ -90,11 +99,17 @@ GGO_DEV uint16_t epi_bf16(float v) {
     return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Store one result of row m, column n into C (binary32 or bfloat16, row stride ldc elements).
-GGO_DEV void epi_store(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n, float y) {
-    const float v = epi_apply(e, y, m, n);
+// Store one result of row m, column n into C (binary32 or bfloat16, row stride ldc elements), with its
+// bias b and residual r already loaded.
+GGO_DEV void epi_store_loaded(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n, float y, float b, float r) {
+    const float v = epi_apply_loaded(e, y, b, r);
     if (e.out_bf16) static_cast<uint16_t*>(C)[m * ldc + n] = epi_bf16(v);
     else static_cast<float*>(C)[m * ldc + n] = v;
+}
+
+// Store one result of row m, column n into C (binary32 or bfloat16, row stride ldc elements).
+GGO_DEV void epi_store(const Epi& e, void* C, int64_t ldc, int64_t m, int64_t n, float y) {
+    epi_store_loaded(e, C, ldc, m, n, y, epi_bias1(e, n), epi_res1(e, m, n));
 }
 
 // Four consecutive results of row m, columns n .. n+3, given the bias b[n .. n+3] and the residual
