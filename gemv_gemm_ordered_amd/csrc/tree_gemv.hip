@@ -260,37 +260,17 @@ GGO_DEV void wave_partials(float (&acc)[R][MT], float (&red)[WAVES][R * MT], int
 // Levels 7-8 of the tree, (w0 + w1) + (w2 + w3), for the cnt groups whose wave totals sit in red[0 .. cnt),
 // the groups of ordinals j0 .. j0 + cnt - 1 of this workgroup (group g = first + ordinal * step), and the
 // store. Called by every thread after a barrier.
-// PRE: the fused epilogue's bias and residual of the thread's output were loaded ahead (pb, pr; a batch then
-// holds at most one output per thread).
-template <int MT, int R, int RB, bool EPI, bool PRE = false>
+template <int MT, int R, int RB, bool EPI>
 GGO_DEV void finish_groups(const TreeArgs& a, const float (&red)[RB][WAVES][R * MT], int first, int step, int j0,
-                           int cnt, float pb = 0.0f, float pr = 0.0f) {
+                           int cnt) {
     constexpr int V = R * MT;
-    static_assert(!PRE || RB * V <= THREADS, "one output of a batch per thread at most");
     for (int i = threadIdx.x; i < cnt * V; i += THREADS) {
         const int q = i / V, iv = i - q * V, r = iv / MT, m = iv % MT;
         const int64_t n = (static_cast<int64_t>(first) + static_cast<int64_t>(j0 + q) * step) * R + r;
         if (m < a.M && n < a.N) {
             const float y = (red[q][0][iv] + red[q][1][iv]) + (red[q][2][iv] + red[q][3][iv]);
-            if constexpr (EPI && PRE) epi_store_loaded(a.ep, a.y, a.ldy, m, n, y, pb, pr);
-            else if constexpr (EPI) epi_store(a.ep, a.y, a.ldy, m, n, y);
+            if constexpr (EPI) epi_store(a.ep, a.y, a.ldy, m, n, y);
             else static_cast<float*>(a.y)[m * a.ldy + n] = y;
-        }
-    }
-}
-
-// The bias and residual of the output this thread finishes in the batch of groups j0 .. j0 + cnt - 1 (as
-// in finish_groups), loaded ahead of the batch's end.
-template <int MT, int R>
-GGO_DEV void epi_load_batch(const TreeArgs& a, int first, int step, int j0, int cnt, float& pb, float& pr) {
-    constexpr int V = R * MT;
-    const int i = threadIdx.x;
-    if (i < cnt * V) {
-        const int q = i / V, iv = i - q * V, r = iv / MT, m = iv % MT;
-        const int64_t n = (static_cast<int64_t>(first) + static_cast<int64_t>(j0 + q) * step) * R + r;
-        if (m < a.M && n < a.N) {
-            pb = epi_bias1(a.ep, n);
-            pr = epi_res1(a.ep, m, n);
         }
     }
 }
@@ -353,14 +333,6 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a, int gpw) {
     int j = 0;                                // ordinal of the current group in this workgroup
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) load_group<MT, R, S>(a, g + b * stride, gend, off, w[b]);
-    // With a barrier per group (RB = 1) the fused epilogue's bias and residual of the thread's output are
-    // loaded a group ahead: the first group's here, each next group's after a group's store (M = 4: 9.8 -
-    // 10.2 -> 8.8 - 9.1 us, same bits). With batches of groups loading them at the batch's end measured
-    // faster (M = 1 / 8: 7.1 / 9.3 us against 7.1 - 7.4 / 9.5 - 9.7 when loaded ahead).
-    constexpr bool PRE = EPI && RB == 1;
-    const int gcount = CONTIG ? gend - first : (groups - first + stride - 1) / stride;
-    float pb = 0.0f, pr = 0.0f;
-    if constexpr (PRE) epi_load_batch<MT, R>(a, first, stride, 0, 1, pb, pr);
     for (;;) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -373,10 +345,7 @@ __global__ __launch_bounds__(THREADS) void k_gemv_tree_p(TreeArgs a, int gpw) {
             const bool last = gb + stride >= gend;   // uniform across the workgroup
             if (last || q == RB - 1) {
                 __syncthreads();
-                finish_groups<MT, R, RB, EPI, PRE>(a, red[h], first, stride, j - q, q + 1, pb, pr);
-                if constexpr (PRE) {
-                    if (j + 1 < gcount) epi_load_batch<MT, R>(a, first, stride, j + 1, 1, pb, pr);
-                }
+                finish_groups<MT, R, RB, EPI>(a, red[h], first, stride, j - q, q + 1);
             }
             ++j;
             if (last) goto done;
@@ -424,7 +393,12 @@ hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
     // advancing window per wave instead of rows gridDim.x groups apart): M = 4 / 8 7.42 / 8.93 us against
     // 7.74 / 9.18 strided, M = 1 level (alternated three times; the same bits). With contiguous groups a
     // third group in flight gained nothing at M = 8 and a fourth lost 0.7 us.
+    // RB_EP: the fused epilogue's instances take one batch at M = 4 too. Its code then runs once per
+    // workgroup instead of once per group, each time on the critical path of the next barrier: M = 4 7.8 -
+    // 8.0 us against 9.0 - 9.2 with a barrier per group (and 9.8 - 10.2 before that form loaded each group's
+    // bias and residual a group ahead; same bits throughout).
     constexpr int R = MT >= 8 ? 1 : 2, NB = 2, PER_CU = 2, RB = MT >= 8 ? 8 : MT <= 2 ? 4 : 1;
+    constexpr int RB_EP = MT >= 8 ? 8 : 4;
     constexpr bool CONTIG = true;
     const int64_t groups = (a.N + R - 1) / R;
     int64_t blocks = std::min<int64_t>(groups, static_cast<int64_t>(device_cus()) * PER_CU);
@@ -434,7 +408,7 @@ hipError_t launch_persistent(const TreeArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, false, RB, CONTIG>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0,
                            stream, a, gpw);
     else
-        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, true, RB, CONTIG>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0,
+        hipLaunchKernelGGL((k_gemv_tree_p<MT, R, S, NB, true, RB_EP, CONTIG>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0,
                            stream, a, gpw);
     return hipGetLastError();
 }
