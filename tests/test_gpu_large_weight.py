@@ -1,11 +1,12 @@
-"""Weights past 2^32 bytes: each GEMV and GEMM entry point on a 4.3 GB bfloat16 weight, sampled outputs
-bit for bit against the oracle.
+"""Operands past 2^32 bytes: each GEMV and GEMM entry point on a 4.3 GB bfloat16 weight, and both GEMMs
+on 4.3 GB of activation rows, sampled outputs bit for bit against the oracle.
 
 At K = 4096 a row of W^T is 8 KiB, so rows 262144 and 524288 start at 2^31 and 2^32 bytes. The weight
-repeats a seeded block of B = 4099 rows of W^T (or columns of W [K, N]) 128 times, N = 524672. B is odd,
-so it divides neither 2^18 nor 2^19: an address that wrapped at 2^31 or 2^32 bytes would read another
-row of the block, and the sampled outputs around those rows and at the end would move. Each sampled
-output needs only its own row of W^T (column of W) and x, so the oracle computes it on that row alone.
+repeats a seeded block of B = 4099 rows of W^T (or columns of W [K, N]) 128 times, N = 524672, and the
+activations repeat a block of B rows of A the same way. B is odd, so it divides neither 2^18 nor 2^19:
+an address that wrapped at 2^31 or 2^32 bytes would read another row of the block, and the sampled
+outputs around those rows and at the end would move. Each sampled output needs only its own row of W^T
+(column of W, row of A) and the other operand, so the oracle computes it on that row alone.
 The kernels' row and stage bases are 64-bit and their in-range offsets 32-bit; these cases are the
 largest operands the decode and prefill entry points are sized for here.
 """
@@ -123,3 +124,28 @@ def test_matrix_core_gemm(g, block, big_w):
     say(f"gemm_mfma_invariant M=3 N={N} K={K}")
     ref = oracle.gemm_mfma(x[:3], np.ascontiguousarray(rows.T)).view(np.uint32)
     check(sampled(g.gemm_mfma_invariant(dx[:3], dW)), ref, "gemm_mfma_invariant M=3")
+
+
+@pytest.fixture(scope="module")
+def big_a():
+    """A [N, K] (the same 4.3 GB size, as rows of activations) repeating a seeded block of B rows, and a
+    small weight W [K, 64]."""
+    import torch
+    A0 = synth.normal_bf16(22, "large.A", (B, K), 1.0)
+    W = synth.normal_bf16(22, "large.W", (K, 64), 0.02)
+    say(f"large activations: A [{N}, {K}] bf16, {N * ROW_BYTES / 1e9:.2f} GB")
+    dA = dev_bf16(A0).repeat(REPS, 1)
+    assert dA.shape == (N, K) and dA.is_contiguous()
+    yield A0, W, dA, dev_bf16(W)
+    del dA
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("entry", ["gemm_ordered", "gemm_mfma_invariant"])
+def test_gemm_rows_past_2_32_bytes(g, big_a, entry):
+    A0, W, dA, dW = big_a
+    say(f"{entry} M={N} N=64 K={K}")
+    got = host_bits(getattr(g, entry)(dA, dW)[SAMPLE.tolist()].contiguous())
+    rows = np.ascontiguousarray(A0[SAMPLE % B])
+    ref = f32_bits(oracle.gemm_ordered(rows, W)) if entry == "gemm_ordered" else oracle.gemm_mfma(rows, W).view(np.uint32)
+    check(got, ref, entry)
