@@ -149,3 +149,29 @@ def test_gemm_rows_past_2_32_bytes(g, big_a, entry):
     rows = np.ascontiguousarray(A0[SAMPLE % B])
     ref = f32_bits(oracle.gemm_ordered(rows, W)) if entry == "gemm_ordered" else oracle.gemm_mfma(rows, W).view(np.uint32)
     check(got, ref, entry)
+
+
+def bf16_sampled(y):
+    import torch
+    torch.cuda.synchronize()
+    return y[:, SAMPLE.tolist()].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("entry", ["gemv_tree_ep", "gemm_mfma_invariant_ep"])
+def test_fused_epilogue(g, block, big_wt, big_w, entry):
+    """Bias, activation and residual indexed past 2^21 outputs, bfloat16 out, on the 4.3 GB weight."""
+    _, x, rows = block
+    M, act = (4, "silu") if entry == "gemv_tree_ep" else (3, "gelu_tanh")
+    bias = synth.normal_f32(23, "large.bias", (N,), 0.1)
+    res = synth.normal_f32(23, "large.res", (M, N), 1.0)
+    from tests.gpu_util import dev_f32
+    dbias, dres = dev_f32(bias), dev_f32(res)
+    say(f"{entry} M={M} N={N} K={K} {act}, bias, residual, bf16 out")
+    if entry == "gemv_tree_ep":
+        y = g.gemv_tree_ep(big_wt[1][:M], big_wt[0], bias=dbias, act=act, residual=dres, out="bf16")
+        Y = oracle.gemv_tree(x[:M], rows)
+    else:
+        y = g.gemm_mfma_invariant_ep(big_w[1][:M], big_w[0], bias=dbias, act=act, residual=dres, out="bf16")
+        Y = oracle.gemm_mfma(x[:M], np.ascontiguousarray(rows.T))
+    ref = oracle.epilogue(Y, bias=bias[SAMPLE], act=act, residual=np.ascontiguousarray(res[:, SAMPLE]), out="bf16")
+    check(bf16_sampled(y), ref, entry)
