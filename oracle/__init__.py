@@ -133,7 +133,10 @@ def ep_exp(x: float, lib=None) -> float:
 
 
 def gemm_mfma(A: np.ndarray, W: np.ndarray, threads: int = 1, lib=None) -> np.ndarray:
-    """Bit model of the matrix-core product (A [M, K], W [K, N] bf16 bits) -> float32 [M, N]."""
+    """Bit model of the matrix-core product (A [M, K], W [K, N] bf16 bits) -> float32 [M, N].
+
+    Finite operands only: an exponent field of all ones is read as a number, so outputs that meet an Inf or
+    NaN operand are not modelled (IEEE arithmetic fixes their class, NaN or an infinity, in any order)."""
     A = np.ascontiguousarray(A, dtype=np.uint16)
     W = np.ascontiguousarray(W, dtype=np.uint16)
     assert A.ndim == 2 and W.ndim == 2 and A.shape[1] == W.shape[0], (A.shape, W.shape)
