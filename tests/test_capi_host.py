@@ -78,6 +78,17 @@ def test_bad_arguments_are_rejected_without_touching_the_gpu(g):
     assert lib.gemv_mfma_invariant(16, 12, 16, 12, 16, 8, 4, 8, 12, null) == -2   # K % 8 != 0
     assert lib.gemv_mfma_invariant(16, 1 << 29, 16, 1 << 29, 16, 8, 1, 8, 1 << 29, null) == -2   # K too large
     assert b"too large" in lib.ggo_last_error()
+    # size limits of the ordered GEMVs (32-bit offsets inside a stage or slab) and of every size argument
+    assert lib.gemv_ordered(16, 8, 16, 1 << 25, 16, 8, 1, 8, 8, null) == -2             # ldw past the stage range
+    assert b"too large" in lib.ggo_last_error()
+    assert lib.gemv_ordered(16, 1 << 30, 16, 8, 16, 8, 1, 8, 1 << 30, null) == -2       # K >= 2^30
+    assert b"too large" in lib.ggo_last_error()
+    assert lib.gemv_ordered_wt(16, 8, 16, 1 << 27, 16, 8, 1, 8, 8, null) == -2          # ldwt past the slab range
+    assert b"too large" in lib.ggo_last_error()
+    assert lib.gemm_ordered(16, 0, 8, 16, 8, 16, 8, 1 << 31, 8, 8, null) == -2          # M > 2^31 - 1
+    assert b"2^31-1" in lib.ggo_last_error()
+    assert lib.gemm_mfma_invariant(16, 1 << 31, 16, 8, 16, 8, 4, 8, 1 << 31, null) == -2   # K > 2^31 - 1
+    assert b"2^31-1" in lib.ggo_last_error()
     assert lib.gemm_ordered_grouped(null, 1, 0, null) == -1
     arr = (g.Problem * 1)()
     assert lib.gemm_ordered_grouped(arr, 17, 0, null) == -1
